@@ -1,0 +1,102 @@
+"""Planted mistakes in the oracle (on the CPU) must each be caught by a pin.
+
+Each mutant replaces one oracle function with a plausible wrong version; the
+listed pin tests must then fail.  This shows the pins constrain the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.mk_oracle as M
+from tests import test_oracle_pins as P
+
+
+def _truncating_bf16(x):
+    x32 = np.asarray(x, np.float64).astype(np.float32)
+    return (x32.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _gemm_transposed_b(a_bits, b_bits):
+    a = M.bf16_to_f64(a_bits)
+    b = M.bf16_to_f64(b_bits)
+    if a.shape[1] != b.shape[0]:
+        raise ValueError("shape")
+    if b.shape[0] == b.shape[1]:
+        return a @ b.T
+    return a @ b
+
+
+def _gemm_drops_last_k(a_bits, b_bits):
+    a = M.bf16_to_f64(a_bits)
+    b = M.bf16_to_f64(b_bits)
+    if a.shape[1] != b.shape[0]:
+        raise ValueError("shape")
+    return a[:, :-1] @ b[:-1] if a.shape[1] > 1 else a @ b
+
+
+def _sum_skips_last_peer(own, peers, rank):
+    acc = np.array(own, dtype=np.float64, copy=True)
+    last = max(q for q in range(len(peers)) if q != rank)
+    for q, p in enumerate(peers):
+        if q == rank or q == last:
+            continue
+        acc = acc + np.asarray(p, dtype=np.float64)
+    return acc
+
+
+def _sum_subtracts(own, peers, rank):
+    acc = np.array(own, dtype=np.float64, copy=True)
+    for q, p in enumerate(peers):
+        if q != rank:
+            acc = acc - np.asarray(p, dtype=np.float64)
+    return acc
+
+
+_orig_route = M.moe_route
+
+
+def _route_ties_to_higher_id(logits, top_k):
+    lg = np.asarray(logits, np.float32)
+    E = lg.shape[1]
+    r = _orig_route(lg[:, ::-1], top_k)
+    idx = (E - 1 - r["idx"]).astype(np.int32)
+    prob = r["prob"][:, ::-1]
+    return dict(idx=idx, gate=np.take_along_axis(prob, idx.astype(np.int64), 1), prob=prob)
+
+
+def _route_renormalised(logits, top_k):
+    r = _orig_route(logits, top_k)
+    g = r["gate"] / r["gate"].sum(axis=1, keepdims=True)
+    return dict(r, gate=g)
+
+
+_orig_dispatch = M.moe_dispatch
+
+
+def _dispatch_token_major(idx, gate, S, T, E_loc, rank=0):
+    d = _orig_dispatch(idx, gate, S, T, E_loc, rank)
+    o = np.argsort(d["slot_token"], kind="stable")
+    return dict(d, slot_token=d["slot_token"][o], slot_gate=d["slot_gate"][o])
+
+
+MUTANTS = [
+    ("f64_to_bf16", _truncating_bf16, [P.test_bf16_hand_patterns]),
+    ("gemm", _gemm_transposed_b, [lambda: P.test_gemm_exact_bruteforce((5, 6, 6))]),
+    ("gemm", _gemm_drops_last_k, [lambda: P.test_gemm_exact_bruteforce((3, 5, 7))]),
+    ("_sum_partials", _sum_skips_last_peer, [P.test_gemm_rs_w_rank_emulation_tiles_full_sum]),
+    ("_sum_partials", _sum_subtracts, [P.test_gemm_ar_golden_hand_example]),
+    ("moe_route", _route_ties_to_higher_id, [P.test_moe_golden_hand_example]),
+    ("moe_route", _route_renormalised, [P.test_moe_gates_are_softmax]),
+    ("moe_dispatch", _dispatch_token_major, [P.test_moe_golden_hand_example]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pins", MUTANTS,
+                         ids=[f"{m[0]}-{m[1].__name__}" for m in MUTANTS])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant, pins):
+    monkeypatch.setattr(M, name, mutant)
+    if hasattr(O, name):
+        monkeypatch.setattr(O, name, mutant)
+    for pin in pins:
+        with pytest.raises((AssertionError, ValueError)):
+            pin()
