@@ -1,0 +1,604 @@
+// Host side of libmk: the C ABI declared in include/mk.h.
+//
+// A handle owns a control block (tickets, counters, error record), per-chunk
+// ready flags with self-resetting arrival counters, and an on-demand
+// workspace.  Each operation validates its arguments, classifies every peer
+// pointer (device memory or pinned host memory read/written over PCIe),
+// chooses the tile shape and role counts, advances the handle's epoch and
+// makes exactly one persistent kernel launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "mk_params.h"
+
+namespace mk {
+hipError_t launch_ag(const AgParams &p, int bm, int grid, hipStream_t s);
+hipError_t launch_rs(const RsParams &p, int bm, int grid, hipStream_t s);
+hipError_t launch_ar(const ArParams &p, int bm, int grid, hipStream_t s);
+hipError_t launch_moe(const MoeParams &p, int bm, int grid, hipStream_t s);
+hipError_t occupancy(int op, int bm, int *blocks_per_cu);
+hipError_t occupancy_moe(int bm, int *blocks_per_cu);
+}  // namespace mk
+
+struct mk_ctx {
+  int device = 0;
+  int cu_count = 0;
+  int timeout_ms = 2000;
+  uint64_t timeout_ticks = 0;
+  int force_tile = 0;  // MK_TILE env: 128 or 256 forces the tile edge
+  mk::Ctrl *ctrl = nullptr;
+  uint32_t *flags = nullptr;
+  uint32_t *cnt = nullptr;
+  uint32_t epoch = 0;
+  mk_roles roles[MK_OP_COUNT];
+  mk_roles last[MK_OP_COUNT];
+  int last_grid[MK_OP_COUNT] = {0, 0, 0, 0};
+  bool launched[MK_OP_COUNT] = {false, false, false, false};
+  int occ[MK_OP_COUNT][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};  // blocks per CU: [bm=256, bm=128]
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  std::string err;
+};
+
+namespace {
+
+struct DeviceGuard {
+  int old = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&old) != hipSuccess) old = -1;
+    if (old != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (old >= 0) (void)hipSetDevice(old);
+  }
+};
+
+mk_status fail(mk_ctx *h, mk_status st, const std::string &msg) {
+  if (h) h->err = msg;
+  return st;
+}
+
+mk_status hip_fail(mk_ctx *h, hipError_t e, const char *what) {
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  (void)hipGetLastError();
+  return fail(h, MK_ERR_HIP, m);
+}
+
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Resolve a pointer the kernel will dereference.  Device memory must belong
+// to the handle's device; pinned host memory is accepted when allow_host
+// and replaced by its device-side address.
+mk_status resolve(mk_ctx *h, const void *p, bool allow_host, const void **out, const char *what) {
+  if (p == nullptr) return fail(h, MK_ERR_INVALID, std::string(what) + " is NULL");
+  if (reinterpret_cast<uintptr_t>(p) & 15u)
+    return fail(h, MK_ERR_INVALID, std::string(what) + " is not 16-byte aligned");
+  hipPointerAttribute_t a;
+  std::memset(&a, 0, sizeof(a));
+  hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(h, MK_ERR_INVALID, std::string(what) + " is not HIP-allocated memory (pageable host memory?)");
+  }
+  switch (a.type) {
+    case hipMemoryTypeDevice:
+      if (a.device != h->device)
+        return fail(h, MK_ERR_INVALID, std::string(what) + " lives on another device");
+      *out = p;
+      return MK_OK;
+    case hipMemoryTypeHost:
+      if (!allow_host) return fail(h, MK_ERR_INVALID, std::string(what) + " must be device memory");
+      *out = a.devicePointer ? a.devicePointer : p;
+      return MK_OK;
+    case hipMemoryTypeManaged:
+    case hipMemoryTypeUnified:
+      *out = p;
+      return MK_OK;
+    default:
+      return fail(h, MK_ERR_INVALID, std::string(what) + " is not device or pinned host memory");
+  }
+}
+
+mk::Sync make_sync(mk_ctx *h, uint32_t n_flags) {
+  if (++h->epoch == 0) h->epoch = 1;
+  mk::Sync s;
+  s.ctrl = h->ctrl;
+  s.flags = h->flags;
+  s.cnt = h->cnt;
+  s.epoch = h->epoch;
+  s.n_flags = n_flags;
+  s.timeout_ticks = h->timeout_ticks;
+  return s;
+}
+
+// Workgroups resident at once for a kernel instantiation.
+int max_grid(mk_ctx *h, int op, int bm) {
+  int &o = h->occ[op][bm == 256 ? 0 : 1];
+  if (o == 0) {
+    int b = 0;
+    hipError_t e = op == MK_OP_MOE ? mk::occupancy_moe(bm, &b) : mk::occupancy(op, bm, &b);
+    if (e != hipSuccess || b < 1) {
+      (void)hipGetLastError();
+      b = 1;
+    }
+    o = b;
+  }
+  return std::max(1, o * h->cu_count);
+}
+
+int pick_tile(mk_ctx *h, long tiles256) {
+  if (h->force_tile == 128 || h->force_tile == 256) return h->force_tile;
+  return tiles256 * 2 >= h->cu_count ? 256 : 128;
+}
+
+// Apply the user's role settings to the defaults.  `want_land` / `want_reduce`
+// are the defaults; compute fills the rest of the resident grid (capped by
+// the tile count).  Grid = the sum; at least one workgroup.
+void choose_roles(mk_ctx *h, mk_op op, int gmax, int want_land, int n_tiles, int *land, int *compute) {
+  const mk_roles &r = h->roles[op];
+  int l = r.n_land >= 0 ? r.n_land : want_land;
+  l = std::max(0, std::min(l, 4 * gmax));
+  int c;
+  if (r.n_compute >= 0) c = std::min(r.n_compute, 4 * gmax);
+  else c = std::max(1, std::min(n_tiles, gmax - l));
+  *land = l;
+  *compute = std::max(0, c);
+}
+
+void record(mk_ctx *h, mk_op op, int land, int compute, int reduce, int grid) {
+  h->last[op].n_land = land;
+  h->last[op].n_compute = compute;
+  h->last[op].n_reduce = reduce;
+  h->last_grid[op] = grid;
+  h->launched[op] = true;
+}
+
+mk_status check_common(mk_ctx *h, int world, int rank) {
+  if (!h) return MK_ERR_INVALID;
+  h->err.clear();
+  if (world < 1 || world > MK_MAX_WORLD) return fail(h, MK_ERR_INVALID, "world out of range");
+  if (rank < 0 || rank >= world) return fail(h, MK_ERR_INVALID, "rank out of range");
+  return MK_OK;
+}
+
+mk_status check_gemm_shape(mk_ctx *h, long m, long n, long k) {
+  if (m < 1 || n < 8 || k < 8) return fail(h, MK_ERR_INVALID, "GEMM dimensions too small");
+  if (n % 8 || k % 8) return fail(h, MK_ERR_INVALID, "n and k must be multiples of 8");
+  if (k > (1 << 20) || n > (1 << 24) || m > (1L << 28))
+    return fail(h, MK_ERR_UNSUPPORTED, "GEMM dimensions beyond the supported range");
+  if ((long)256 * k * 2 >= 0x80000000L) return fail(h, MK_ERR_UNSUPPORTED, "k too large");
+  return MK_OK;
+}
+
+mk_status ensure_ws(mk_ctx *h, size_t bytes) {
+  if (bytes <= h->ws_bytes) return MK_OK;
+  // a previous launch may still use the old workspace
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(h, e, "hipDeviceSynchronize");
+  if (h->ws) (void)hipFree(h->ws);
+  h->ws = nullptr;
+  h->ws_bytes = 0;
+  size_t b = std::max(bytes, (size_t)1 << 20);
+  e = hipMalloc(&h->ws, b);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(h, MK_ERR_OOM, "workspace allocation failed");
+  }
+  h->ws_bytes = b;
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mk_status_string(mk_status s) {
+  switch (s) {
+    case MK_OK: return "MK_OK";
+    case MK_ERR_INVALID: return "MK_ERR_INVALID: invalid argument";
+    case MK_ERR_UNSUPPORTED: return "MK_ERR_UNSUPPORTED: unsupported device or shape";
+    case MK_ERR_OOM: return "MK_ERR_OOM: device allocation failed";
+    case MK_ERR_HIP: return "MK_ERR_HIP: HIP runtime error";
+    case MK_ERR_TIMEOUT: return "MK_ERR_TIMEOUT: an in-kernel wait expired";
+  }
+  return "unknown mk_status";
+}
+
+const char *mk_last_error(mk_handle h) { return h ? h->err.c_str() : ""; }
+
+mk_status mk_create(mk_handle *out, const mk_config *cfg) {
+  if (!out || !cfg) return MK_ERR_INVALID;
+  if (cfg->flags != 0) return MK_ERR_INVALID;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev) {
+    (void)hipGetLastError();
+    return MK_ERR_INVALID;
+  }
+  DeviceGuard g(cfg->device);
+  if (!g.ok) return MK_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, cfg->device) != hipSuccess) return MK_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MK_ERR_UNSUPPORTED;
+  mk_ctx *h = new mk_ctx();
+  h->device = cfg->device;
+  h->cu_count = prop.multiProcessorCount;
+  h->timeout_ms = cfg->spin_timeout_ms > 0 ? cfg->spin_timeout_ms : 2000;
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, cfg->device) != hipSuccess || khz <= 0)
+    khz = 100000;
+  h->timeout_ticks = (uint64_t)khz * (uint64_t)h->timeout_ms;
+  if (const char *t = std::getenv("MK_TILE")) h->force_tile = std::atoi(t);
+  for (int i = 0; i < MK_OP_COUNT; ++i) h->roles[i] = mk_roles{-1, -1, -1};
+  if (const char *r = std::getenv("MK_ROLES")) {
+    int l = -1, c = -1, d = -1;
+    if (std::sscanf(r, "%d,%d,%d", &l, &c, &d) >= 1)
+      for (int i = 0; i < MK_OP_COUNT; ++i) h->roles[i] = mk_roles{l, c, d};
+  }
+  const size_t flag_bytes = (size_t)mk::kMaxFlags * mk::kFlagStride * sizeof(uint32_t);
+  hipError_t e = hipMalloc(reinterpret_cast<void **>(&h->ctrl), sizeof(mk::Ctrl));
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&h->flags), flag_bytes);
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&h->cnt), flag_bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    mk_destroy(h);
+    return MK_ERR_OOM;
+  }
+  e = hipMemset(h->ctrl, 0, sizeof(mk::Ctrl));
+  if (e == hipSuccess) e = hipMemset(h->flags, 0, flag_bytes);
+  if (e == hipSuccess) e = hipMemset(h->cnt, 0, flag_bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    mk_destroy(h);
+    return MK_ERR_HIP;
+  }
+  *out = h;
+  return MK_OK;
+}
+
+mk_status mk_destroy(mk_handle h) {
+  if (!h) return MK_ERR_INVALID;
+  DeviceGuard g(h->device);
+  if (h->ctrl) (void)hipFree(h->ctrl);
+  if (h->flags) (void)hipFree(h->flags);
+  if (h->cnt) (void)hipFree(h->cnt);
+  if (h->ws) (void)hipFree(h->ws);
+  delete h;
+  return MK_OK;
+}
+
+mk_status mk_set_roles(mk_handle h, mk_op op, const mk_roles *roles) {
+  if (!h || !roles || op < 0 || op >= MK_OP_COUNT) return MK_ERR_INVALID;
+  h->roles[op] = *roles;
+  return MK_OK;
+}
+
+mk_status mk_get_roles(mk_handle h, mk_op op, mk_roles *roles) {
+  if (!h || !roles || op < 0 || op >= MK_OP_COUNT) return MK_ERR_INVALID;
+  *roles = h->roles[op];
+  return MK_OK;
+}
+
+mk_status mk_last_launch(mk_handle h, mk_op op, mk_roles *roles, int *grid) {
+  if (!h || op < 0 || op >= MK_OP_COUNT || !h->launched[op]) return MK_ERR_INVALID;
+  if (roles) *roles = h->last[op];
+  if (grid) *grid = h->last_grid[op];
+  return MK_OK;
+}
+
+mk_status mk_sync(mk_handle h, mk_stream stream) {
+  if (!h) return MK_ERR_INVALID;
+  DeviceGuard g(h->device);
+  hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(h, e, "hipStreamSynchronize");
+  uint32_t rec[3] = {0, 0, 0};
+  e = hipMemcpy(rec, &h->ctrl->err_code, sizeof(rec), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(h, e, "reading the error record");
+  if (rec[0] != 0) {
+    const uint32_t zero = 0;
+    e = hipMemcpy(&h->ctrl->err_code, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(h, e, "clearing the error record");
+    char buf[160];
+    std::snprintf(buf, sizeof(buf), "in-kernel wait timed out (code %u, wait id 0x%08x, epoch %u)",
+                  rec[0], rec[1], rec[2]);
+    h->err = buf;
+    return rec[0] == MK_ERR_TIMEOUT ? MK_ERR_TIMEOUT : MK_ERR_HIP;
+  }
+  return MK_OK;
+}
+
+// ---------------------------------------------------------------- AllGather + GEMM
+
+mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
+                     const mk_bf16 *const *a_shards, const mk_bf16 *bt, mk_bf16 *c,
+                     mk_bf16 *a_gathered, int m_s, int n, int k, unsigned flags) {
+  mk_status st = check_common(h, world, rank);
+  if (st != MK_OK) return st;
+  if (flags & ~MK_F_PRELANDED) return fail(h, MK_ERR_INVALID, "unknown flag bits");
+  if (!a_shards) return fail(h, MK_ERR_INVALID, "a_shards is NULL");
+  if (m_s < 1) return fail(h, MK_ERR_INVALID, "m_s < 1");
+  st = check_gemm_shape(h, (long)world * m_s, n, k);
+  if (st != MK_OK) return st;
+  DeviceGuard g(h->device);
+  const bool pre = (flags & MK_F_PRELANDED) != 0;
+  mk::AgParams p;
+  std::memset(&p, 0, sizeof(p));
+  const void *dp;
+  for (int q = 0; q < world; ++q) {
+    if (pre && q != rank) continue;  // peers are not read when pre-landed
+    char what[32];
+    std::snprintf(what, sizeof(what), "a_shards[%d]", q);
+    if ((st = resolve(h, a_shards[q], q != rank, &dp, what)) != MK_OK) return st;
+    p.shard[q] = static_cast<const uint16_t *>(dp);
+  }
+  if ((st = resolve(h, bt, false, &dp, "bt")) != MK_OK) return st;
+  p.bt = static_cast<const uint16_t *>(dp);
+  if ((st = resolve(h, c, true, &dp, "c")) != MK_OK) return st;
+  p.c = static_cast<uint16_t *>(const_cast<void *>(dp));
+  if ((st = resolve(h, a_gathered, false, &dp, "a_gathered")) != MK_OK) return st;
+  p.ag = static_cast<uint16_t *>(const_cast<void *>(dp));
+
+  const int M = world * m_s;
+  const int bm = pick_tile(h, (long)cdiv(M, 256) * cdiv(n, 256));
+  p.world = world;
+  p.rank = rank;
+  p.m_s = m_s;
+  p.n = n;
+  p.k = k;
+  p.tiles_m = cdiv(M, bm);
+  p.tiles_n = cdiv(n, bm);
+  p.n_tiles = p.tiles_m * p.tiles_n;
+  p.mb0 = (rank * m_s) / bm;
+  // landing geometry: one flag per lb_rows rows of a shard, items of ~256 KiB
+  p.lb_rows = bm;
+  while ((long)world * cdiv(m_s, p.lb_rows) > mk::kMaxFlags) p.lb_rows *= 2;
+  p.blocks_per_chunk = cdiv(m_s, p.lb_rows);
+  p.item_rows = std::max(1, std::min(p.lb_rows, (256 * 1024) / (k * 2)));
+  p.items_per_block = cdiv(p.lb_rows, p.item_rows);
+  p.n_items = world * p.blocks_per_chunk * p.items_per_block;
+  p.prelanded = pre ? 1 : 0;
+
+  const int gmax = max_grid(h, MK_OP_AG_GEMM, bm);
+  int land = 0, compute = 0;
+  const int want_land = pre ? 0 : std::max(1, std::min(std::min(p.n_items, gmax / 8), 32));
+  choose_roles(h, MK_OP_AG_GEMM, gmax, want_land, p.n_tiles, &land, &compute);
+  if (pre) land = 0;
+  p.n_land = land;
+  p.n_compute = compute;
+  const int grid = std::max(1, land + compute);
+  p.sync = make_sync(h, (uint32_t)(world * p.blocks_per_chunk));
+  hipError_t e = mk::launch_ag(p, bm, grid, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(h, e, "launching the AllGather+GEMM kernel");
+  record(h, MK_OP_AG_GEMM, land, compute, 0, grid);
+  return MK_OK;
+}
+
+// ---------------------------------------------------------------- GEMM + ReduceScatter
+
+mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const mk_bf16 *a,
+                     const mk_bf16 *bt, const float *const *peer_part, mk_bf16 *c_own,
+                     mk_bf16 *const *outbox, int m, int n, int k, unsigned flags) {
+  mk_status st = check_common(h, world, rank);
+  if (st != MK_OK) return st;
+  if (flags) return fail(h, MK_ERR_INVALID, "unknown flag bits");
+  if (world > 1 && (!peer_part || !outbox)) return fail(h, MK_ERR_INVALID, "peer_part / outbox is NULL");
+  st = check_gemm_shape(h, m, n, k);
+  if (st != MK_OK) return st;
+  if (m % world) return fail(h, MK_ERR_INVALID, "m must be a multiple of world");
+  DeviceGuard g(h->device);
+  mk::RsParams p;
+  std::memset(&p, 0, sizeof(p));
+  const void *dp;
+  if ((st = resolve(h, a, false, &dp, "a")) != MK_OK) return st;
+  p.a = static_cast<const uint16_t *>(dp);
+  if ((st = resolve(h, bt, false, &dp, "bt")) != MK_OK) return st;
+  p.bt = static_cast<const uint16_t *>(dp);
+  if ((st = resolve(h, c_own, true, &dp, "c_own")) != MK_OK) return st;
+  p.c_own = static_cast<uint16_t *>(const_cast<void *>(dp));
+  for (int q = 0; q < world; ++q) {
+    if (q == rank) continue;
+    char what[32];
+    std::snprintf(what, sizeof(what), "peer_part[%d]", q);
+    if ((st = resolve(h, peer_part[q], true, &dp, what)) != MK_OK) return st;
+    p.peer[q] = static_cast<const float *>(dp);
+    std::snprintf(what, sizeof(what), "outbox[%d]", q);
+    if ((st = resolve(h, outbox[q], true, &dp, what)) != MK_OK) return st;
+    p.outbox[q] = static_cast<uint16_t *>(const_cast<void *>(dp));
+  }
+  const int bm = pick_tile(h, (long)cdiv(m, 256) * cdiv(n, 256));
+  p.world = world;
+  p.rank = rank;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.ms = m / world;
+  p.tiles_m = cdiv(m, bm);
+  p.tiles_n = cdiv(n, bm);
+  p.n_tiles = p.tiles_m * p.tiles_n;
+  p.mb0 = (rank * p.ms) / bm;
+  const int gmax = max_grid(h, MK_OP_GEMM_RS, bm);
+  int land = 0, compute = 0;
+  choose_roles(h, MK_OP_GEMM_RS, gmax, 0, p.n_tiles, &land, &compute);
+  p.n_compute = compute;
+  const int grid = std::max(1, compute);
+  p.sync = make_sync(h, 0);
+  hipError_t e = mk::launch_rs(p, bm, grid, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(h, e, "launching the GEMM+ReduceScatter kernel");
+  record(h, MK_OP_GEMM_RS, 0, compute, 0, grid);
+  return MK_OK;
+}
+
+// ---------------------------------------------------------------- GEMM + AllReduce
+
+mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const mk_bf16 *a,
+                     const mk_bf16 *bt, const float *const *peer_part, mk_bf16 *c,
+                     mk_bf16 *const *bcast, int n_bcast, int m, int n, int k, unsigned flags) {
+  mk_status st = check_common(h, world, rank);
+  if (st != MK_OK) return st;
+  if (flags) return fail(h, MK_ERR_INVALID, "unknown flag bits");
+  if (n_bcast < 0 || n_bcast > MK_MAX_WORLD) return fail(h, MK_ERR_INVALID, "n_bcast out of range");
+  if (world > 1 && !peer_part) return fail(h, MK_ERR_INVALID, "peer_part is NULL");
+  if (n_bcast > 0 && !bcast) return fail(h, MK_ERR_INVALID, "bcast is NULL");
+  st = check_gemm_shape(h, m, n, k);
+  if (st != MK_OK) return st;
+  DeviceGuard g(h->device);
+  mk::ArParams p;
+  std::memset(&p, 0, sizeof(p));
+  const void *dp;
+  if ((st = resolve(h, a, false, &dp, "a")) != MK_OK) return st;
+  p.a = static_cast<const uint16_t *>(dp);
+  if ((st = resolve(h, bt, false, &dp, "bt")) != MK_OK) return st;
+  p.bt = static_cast<const uint16_t *>(dp);
+  if ((st = resolve(h, c, true, &dp, "c")) != MK_OK) return st;
+  p.c = static_cast<uint16_t *>(const_cast<void *>(dp));
+  for (int q = 0; q < world; ++q) {
+    if (q == rank) continue;
+    char what[32];
+    std::snprintf(what, sizeof(what), "peer_part[%d]", q);
+    if ((st = resolve(h, peer_part[q], true, &dp, what)) != MK_OK) return st;
+    p.peer[q] = static_cast<const float *>(dp);
+  }
+  for (int b = 0; b < n_bcast; ++b) {
+    char what[32];
+    std::snprintf(what, sizeof(what), "bcast[%d]", b);
+    if ((st = resolve(h, bcast[b], true, &dp, what)) != MK_OK) return st;
+    p.bcast[b] = static_cast<uint16_t *>(const_cast<void *>(dp));
+  }
+  const int bm = pick_tile(h, (long)cdiv(m, 256) * cdiv(n, 256));
+  p.world = world;
+  p.rank = rank;
+  p.n_bcast = n_bcast;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.tiles_m = cdiv(m, bm);
+  p.tiles_n = cdiv(n, bm);
+  p.n_tiles = p.tiles_m * p.tiles_n;
+  const int gmax = max_grid(h, MK_OP_GEMM_AR, bm);
+  int land = 0, compute = 0;
+  choose_roles(h, MK_OP_GEMM_AR, gmax, 0, p.n_tiles, &land, &compute);
+  p.n_compute = compute;
+  const int grid = std::max(1, compute);
+  p.sync = make_sync(h, 0);
+  hipError_t e = mk::launch_ar(p, bm, grid, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(h, e, "launching the GEMM+AllReduce kernel");
+  record(h, MK_OP_GEMM_AR, 0, compute, 0, grid);
+  return MK_OK;
+}
+
+// ---------------------------------------------------------------- MoE dispatch + grouped GEMM
+
+mk_status mk_moe_dispatch_gemm(mk_handle h, mk_stream stream, int n_src, int rank,
+                               const mk_bf16 *const *x_src, const float *const *logits_src,
+                               const mk_bf16 *wt, int T, int H, int N, int E, int E_loc,
+                               int top_k, mk_bf16 *y, int32_t *topk_idx, float *topk_gate,
+                               int32_t *slot_token, int32_t *expert_offsets,
+                               int32_t *chunk_offsets, mk_bf16 *x_slots, int cap,
+                               unsigned flags) {
+  if (!h) return MK_ERR_INVALID;
+  h->err.clear();
+  if (n_src < 1 || n_src > MK_MAX_WORLD) return fail(h, MK_ERR_INVALID, "n_src out of range");
+  if (flags & ~MK_F_NO_GATE) return fail(h, MK_ERR_INVALID, "unknown flag bits");
+  if (!x_src || !logits_src) return fail(h, MK_ERR_INVALID, "x_src / logits_src is NULL");
+  if (T < 1 || H < 8 || N < 8 || H % 8 || N % 8) return fail(h, MK_ERR_INVALID, "bad T / H / N");
+  if (top_k < 1 || top_k > 8 || E < top_k || E > 256) return fail(h, MK_ERR_INVALID, "bad E / top_k");
+  if (E_loc < 1 || E_loc > mk::kMaxLocalExperts || rank < 0 || (long)(rank + 1) * E_loc > E)
+    return fail(h, MK_ERR_INVALID, "bad E_loc / rank");
+  const long need = (long)n_src * T * std::min(top_k, E_loc);
+  if (cap < need) return fail(h, MK_ERR_INVALID, "cap < n_src*T*min(top_k, E_loc)");
+  if (cap >= (1 << 23) || (long)n_src * T * top_k >= (1L << 30) || H > (1 << 20))
+    return fail(h, MK_ERR_UNSUPPORTED, "MoE sizes beyond the supported range");
+  DeviceGuard g(h->device);
+  mk::MoeParams p;
+  std::memset(&p, 0, sizeof(p));
+  const void *dp;
+  mk_status st;
+  for (int s = 0; s < n_src; ++s) {
+    char what[32];
+    std::snprintf(what, sizeof(what), "x_src[%d]", s);
+    if ((st = resolve(h, x_src[s], s != rank, &dp, what)) != MK_OK) return st;
+    p.x[s] = static_cast<const uint16_t *>(dp);
+    std::snprintf(what, sizeof(what), "logits_src[%d]", s);
+    if ((st = resolve(h, logits_src[s], true, &dp, what)) != MK_OK) return st;
+    p.logits[s] = static_cast<const float *>(dp);
+  }
+  if ((st = resolve(h, wt, false, &dp, "wt")) != MK_OK) return st;
+  p.wt = static_cast<const uint16_t *>(dp);
+  if ((st = resolve(h, y, true, &dp, "y")) != MK_OK) return st;
+  p.y = static_cast<uint16_t *>(const_cast<void *>(dp));
+  if ((st = resolve(h, topk_idx, true, &dp, "topk_idx")) != MK_OK) return st;
+  p.topk_idx = static_cast<int32_t *>(const_cast<void *>(dp));
+  if ((st = resolve(h, topk_gate, true, &dp, "topk_gate")) != MK_OK) return st;
+  p.topk_gate = static_cast<float *>(const_cast<void *>(dp));
+  if ((st = resolve(h, slot_token, true, &dp, "slot_token")) != MK_OK) return st;
+  p.slot_token = static_cast<int32_t *>(const_cast<void *>(dp));
+  if ((st = resolve(h, expert_offsets, true, &dp, "expert_offsets")) != MK_OK) return st;
+  p.expert_offsets = static_cast<int32_t *>(const_cast<void *>(dp));
+  if ((st = resolve(h, chunk_offsets, true, &dp, "chunk_offsets")) != MK_OK) return st;
+  p.chunk_offsets = static_cast<int32_t *>(const_cast<void *>(dp));
+  if ((st = resolve(h, x_slots, false, &dp, "x_slots")) != MK_OK) return st;
+  p.x_slots = static_cast<uint16_t *>(const_cast<void *>(dp));
+
+  p.S = n_src;
+  p.T = T;
+  p.H = H;
+  p.N = N;
+  p.E = E;
+  p.E_loc = E_loc;
+  p.top_k = top_k;
+  p.rank = rank;
+  p.cap = cap;
+  p.items_per_src = cdiv(T, mk::kRouteTokens);
+  p.n_items = n_src * p.items_per_src;
+  if (p.n_items > mk::kMaxFlags) return fail(h, MK_ERR_UNSUPPORTED, "too many route items");
+  p.no_gate = (flags & MK_F_NO_GATE) ? 1 : 0;
+
+  // expected routed rows decide the tile edge
+  const long exp_rows = (long)n_src * T * top_k * E_loc / E;
+  const int bm = pick_tile(h, (long)(cdiv((int)std::max(1L, exp_rows), 256) + E_loc) * cdiv(N, 256));
+  p.tiles_n = cdiv(N, bm);
+  const long max_row_tiles = cdiv(cap, bm) + E_loc;
+
+  // workspace: item_cnt, item_base, tok_rank, slot_gate, tile list
+  const size_t sz_items = (size_t)p.n_items * E_loc * sizeof(int32_t);
+  const size_t sz_rank = (size_t)n_src * T * top_k * sizeof(int32_t);
+  const size_t sz_gate = (size_t)cap * sizeof(float);
+  const size_t sz_tiles = (size_t)(max_row_tiles + 2) * sizeof(int32_t);
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t total = al(sz_items) * 2 + al(sz_rank) + al(sz_gate) + al(sz_tiles);
+  if ((st = ensure_ws(h, total)) != MK_OK) return st;
+  char *w = static_cast<char *>(h->ws);
+  p.item_cnt = reinterpret_cast<int32_t *>(w);
+  w += al(sz_items);
+  p.item_base = reinterpret_cast<int32_t *>(w);
+  w += al(sz_items);
+  p.tok_rank = reinterpret_cast<int32_t *>(w);
+  w += al(sz_rank);
+  p.slot_gate = reinterpret_cast<float *>(w);
+  w += al(sz_gate);
+  p.tile_base = reinterpret_cast<int32_t *>(w);
+
+  const int gmax = max_grid(h, MK_OP_MOE, bm);
+  const mk_roles &r = h->roles[MK_OP_MOE];
+  int land = r.n_land >= 0 ? r.n_land : std::max(1, std::min(p.n_items, gmax / 8));
+  land = std::max(1, std::min(land, 4 * gmax));  // landing cannot be switched off: compute depends on it
+  int compute = r.n_compute >= 0 ? std::min(r.n_compute, 4 * gmax)
+                                 : (int)std::max(1L, std::min(max_row_tiles * p.tiles_n, (long)gmax - land));
+  compute = std::max(0, compute);
+  p.n_land = land;
+  p.n_compute = compute;
+  const int grid = land + compute;
+  p.sync = make_sync(h, (uint32_t)p.n_items);
+  hipError_t e = mk::launch_moe(p, bm, grid, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(h, e, "launching the MoE dispatch kernel");
+  record(h, MK_OP_MOE, land, compute, 0, grid);
+  return MK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,260 @@
+// Persistent fused kernels: AllGather+GEMM, GEMM+ReduceScatter, GEMM+AllReduce.
+//
+// [P1] German article on mKernel (chatgpz.de), table "Die fuenf
+// verschmolzenen Kerne": AllGather + GEMM (the local GEMM consumes tiles of
+// the peers' shards as they arrive), GEMM + AllReduce (output tiles enter the
+// reduction the moment they are produced) and GEMM + ReduceScatter (each
+// output tile is reduced and forwarded to its owning rank as soon as it is
+// produced).  Section "Was mKernel macht": one persistent kernel whose CTAs
+// assign themselves roles, with tunable counts per role.
+//
+// One launch = one call.  Every workgroup takes a ticket; tickets
+// [0, n_land) land chunks, the next n_compute run GEMM tiles.  Land
+// workgroups take tickets first, so every flag a compute workgroup waits on
+// is owned by a workgroup that is already running.
+#include "mk_params.h"
+
+namespace mk {
+
+// ---------------------------------------------------------------- AllGather + GEMM
+
+__device__ __forceinline__ void ag_land(const AgParams &p, uint32_t *s_word) {
+  const size_t row_bytes = (size_t)p.k * 2;
+  const uint32_t per_chunk = (uint32_t)(p.blocks_per_chunk * p.items_per_block);
+  for (;;) {
+    const uint32_t it = next_index(&p.sync.ctrl->land_ctr, s_word);
+    if (it >= (uint32_t)p.n_items) break;
+    // landing order: peers rank+1, rank+2, ... then the local shard last
+    const int pos = (int)(it / per_chunk);
+    const uint32_t rem = it % per_chunk;
+    const int j = (int)(rem / p.items_per_block), ii = (int)(rem % p.items_per_block);
+    const int q = (p.rank + 1 + pos) % p.world;
+    const int r0 = j * p.lb_rows + ii * p.item_rows;
+    const int r1 = min(r0 + p.item_rows, min((j + 1) * p.lb_rows, p.m_s));
+    if (r1 > r0)
+      wg_copy16(p.ag + ((size_t)q * p.m_s + r0) * p.k, p.shard[q] + (size_t)r0 * p.k,
+                (size_t)(r1 - r0) * row_bytes);
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) arrive(p.sync, (uint32_t)(q * p.blocks_per_chunk + j), (uint32_t)p.items_per_block);
+  }
+}
+
+// Thread 0: wait for every land block overlapping gathered rows [m0, m1).
+__device__ __forceinline__ bool ag_wait_rows(const AgParams &p, int m0, int m1) {
+  int r = m0;
+  while (r < m1) {
+    const int q = r / p.m_s, lr = r - q * p.m_s;
+    const int j = lr / p.lb_rows;
+    const uint32_t f = (uint32_t)(q * p.blocks_per_chunk + j);
+    if (!spin_until_eq(p.sync, flag_ptr(p.sync, f), p.sync.epoch, (uint32_t)((q << 16) | j)))
+      return false;
+    r = q * p.m_s + min((j + 1) * p.lb_rows, p.m_s);
+  }
+  return true;
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32_t *s_word) {
+  using C = TileCfg<BM, BN>;
+  const int M = p.world * p.m_s;
+  const int loc0 = p.rank * p.m_s, loc1 = loc0 + p.m_s;
+  const int ldb = p.k * 2;
+  for (;;) {
+    const uint32_t t = next_index(&p.sync.ctrl->tile_ctr, s_word);
+    if (t >= (uint32_t)p.n_tiles) break;
+    const int mi = (int)t / p.tiles_n, nb = (int)t % p.tiles_n;
+    const int mb = (mi + p.mb0) % p.tiles_m;   // local rows first, then peers in landing order
+    const int m0 = mb * BM, n0 = nb * BN;
+    const int m1 = min(m0 + BM, M);
+    const uint16_t *abase;
+    if (!p.prelanded && m0 >= loc0 && m1 <= loc1) {
+      abase = p.shard[p.rank] + (size_t)(m0 - loc0) * p.k;
+    } else {
+      abase = p.ag + (size_t)m0 * p.k;
+      if (!p.prelanded) {
+        bool ok0 = true;
+        if (threadIdx.x == 0) ok0 = ag_wait_rows(p, m0, m1);
+        if (!wg_sync_ok(ok0, s_word)) break;
+      }
+    }
+    const int valid_n = min(BN, p.n - n0);
+    const i32x4_t ra = make_vdesc(abase, (uint32_t)((m1 - m0) * ldb));
+    const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * ldb));
+    f32x16_t acc[C::FM][C::FN];
+    gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const AccPos<BM, BN> ps = acc_pos<BM, BN>(i, j, g);
+          const int row = m0 + ps.row, col = n0 + ps.col;
+          if (row < m1 && col < p.n) {
+            const f32x16_t &v = acc[i][j];
+            *reinterpret_cast<uint2 *>(p.c + (size_t)row * p.n + col) =
+                pack_bf16x4(v[g * 4 + 0], v[g * 4 + 1], v[g * 4 + 2], v[g * 4 + 3]);
+          }
+        }
+  }
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
+  __shared__ uint32_t s_word;
+  const uint32_t ticket = take_ticket(p.sync, &s_word);
+  if (ticket < (uint32_t)p.n_land) {
+    ag_land(p, &s_word);
+  } else if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
+    ag_compute<BM, BN>(p, smem, &s_word);
+  }
+  finish_launch(p.sync);
+}
+
+// ---------------------------------------------------------------- GEMM + ReduceScatter
+
+template <int BM, int BN>
+__device__ __forceinline__ void rs_compute(const RsParams &p, char *smem, uint32_t *s_word) {
+  using C = TileCfg<BM, BN>;
+  const int lda = p.k * 2;
+  for (;;) {
+    const uint32_t t = next_index(&p.sync.ctrl->tile_ctr, s_word);
+    if (t >= (uint32_t)p.n_tiles) break;
+    const int mi = (int)t / p.tiles_n, nb = (int)t % p.tiles_n;
+    const int mb = (mi + p.mb0) % p.tiles_m;   // own slice first: its epilogue is the heaviest
+    const int m0 = mb * BM, n0 = nb * BN;
+    const int m1 = min(m0 + BM, p.m);
+    const int valid_n = min(BN, p.n - n0);
+    const i32x4_t ra = make_vdesc(p.a + (size_t)m0 * p.k, (uint32_t)((m1 - m0) * lda));
+    const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * lda));
+    f32x16_t acc[C::FM][C::FN];
+    gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const AccPos<BM, BN> ps = acc_pos<BM, BN>(i, j, g);
+          const int row = m0 + ps.row, col = n0 + ps.col;
+          if (row >= m1 || col >= p.n) continue;
+          const f32x16_t &v = acc[i][j];
+          float x0 = v[g * 4 + 0], x1 = v[g * 4 + 1], x2 = v[g * 4 + 2], x3 = v[g * 4 + 3];
+          const int q = row / p.ms;
+          const size_t off = (size_t)(row - q * p.ms) * p.n + col;
+          if (q == p.rank) {
+            for (int r = 0; r < p.world; ++r) {
+              if (r == p.rank) continue;
+              const float4 pp = *reinterpret_cast<const float4 *>(p.peer[r] + off);
+              x0 += pp.x; x1 += pp.y; x2 += pp.z; x3 += pp.w;
+            }
+            *reinterpret_cast<uint2 *>(p.c_own + off) = pack_bf16x4(x0, x1, x2, x3);
+          } else {
+            *reinterpret_cast<uint2 *>(p.outbox[q] + off) = pack_bf16x4(x0, x1, x2, x3);
+          }
+        }
+  }
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
+  __shared__ uint32_t s_word;
+  const uint32_t ticket = take_ticket(p.sync, &s_word);
+  if (ticket < (uint32_t)p.n_compute) rs_compute<BM, BN>(p, smem, &s_word);
+  finish_launch(p.sync);
+}
+
+// ---------------------------------------------------------------- GEMM + AllReduce
+
+template <int BM, int BN>
+__device__ __forceinline__ void ar_compute(const ArParams &p, char *smem, uint32_t *s_word) {
+  using C = TileCfg<BM, BN>;
+  const int lda = p.k * 2;
+  for (;;) {
+    const uint32_t t = next_index(&p.sync.ctrl->tile_ctr, s_word);
+    if (t >= (uint32_t)p.n_tiles) break;
+    const int mb = (int)t / p.tiles_n, nb = (int)t % p.tiles_n;
+    const int m0 = mb * BM, n0 = nb * BN;
+    const int m1 = min(m0 + BM, p.m);
+    const int valid_n = min(BN, p.n - n0);
+    const i32x4_t ra = make_vdesc(p.a + (size_t)m0 * p.k, (uint32_t)((m1 - m0) * lda));
+    const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * lda));
+    f32x16_t acc[C::FM][C::FN];
+    gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const AccPos<BM, BN> ps = acc_pos<BM, BN>(i, j, g);
+          const int row = m0 + ps.row, col = n0 + ps.col;
+          if (row >= m1 || col >= p.n) continue;
+          const f32x16_t &v = acc[i][j];
+          float x0 = v[g * 4 + 0], x1 = v[g * 4 + 1], x2 = v[g * 4 + 2], x3 = v[g * 4 + 3];
+          const size_t off = (size_t)row * p.n + col;
+          for (int r = 0; r < p.world; ++r) {
+            if (r == p.rank) continue;
+            const float4 pp = *reinterpret_cast<const float4 *>(p.peer[r] + off);
+            x0 += pp.x; x1 += pp.y; x2 += pp.z; x3 += pp.w;
+          }
+          const uint2 o = pack_bf16x4(x0, x1, x2, x3);
+          *reinterpret_cast<uint2 *>(p.c + off) = o;
+          for (int b = 0; b < p.n_bcast; ++b) *reinterpret_cast<uint2 *>(p.bcast[b] + off) = o;
+        }
+  }
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_ar_kernel(ArParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
+  __shared__ uint32_t s_word;
+  const uint32_t ticket = take_ticket(p.sync, &s_word);
+  if (ticket < (uint32_t)p.n_compute) ar_compute<BM, BN>(p, smem, &s_word);
+  finish_launch(p.sync);
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <typename K, typename P>
+static hipError_t launch(K kernel, int grid, hipStream_t stream, const P &params) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, params);
+  return hipGetLastError();
+}
+
+hipError_t launch_ag(const AgParams &p, int bm, int grid, hipStream_t s) {
+  if (bm == 256) return launch(ag_gemm_kernel<256, 256>, grid, s, p);
+  return launch(ag_gemm_kernel<128, 128>, grid, s, p);
+}
+hipError_t launch_rs(const RsParams &p, int bm, int grid, hipStream_t s) {
+  if (bm == 256) return launch(gemm_rs_kernel<256, 256>, grid, s, p);
+  return launch(gemm_rs_kernel<128, 128>, grid, s, p);
+}
+hipError_t launch_ar(const ArParams &p, int bm, int grid, hipStream_t s) {
+  if (bm == 256) return launch(gemm_ar_kernel<256, 256>, grid, s, p);
+  return launch(gemm_ar_kernel<128, 128>, grid, s, p);
+}
+
+// Resident workgroups per CU of each instantiation (queried once per handle).
+hipError_t occupancy(int op, int bm, int *blocks_per_cu) {
+  const void *f = nullptr;
+  switch (op) {
+    case MK_OP_AG_GEMM:
+      f = bm == 256 ? (const void *)ag_gemm_kernel<256, 256> : (const void *)ag_gemm_kernel<128, 128>;
+      break;
+    case MK_OP_GEMM_RS:
+      f = bm == 256 ? (const void *)gemm_rs_kernel<256, 256> : (const void *)gemm_rs_kernel<128, 128>;
+      break;
+    case MK_OP_GEMM_AR:
+      f = bm == 256 ? (const void *)gemm_ar_kernel<256, 256> : (const void *)gemm_ar_kernel<128, 128>;
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, 0);
+}
+
+}  // namespace mk

@@ -1,0 +1,353 @@
+// Persistent fused MoE dispatch + grouped GEMM.
+//
+// [P1] German article on mKernel (chatgpz.de), table "Die fuenf
+// verschmolzenen Kerne", row "MoE-Versand + GEMM": tokens are routed to the
+// ranks that own their experts and each expert's GEMM runs in the same kernel
+// on the tokens as soon as they land, with no staging-buffer round trip.
+//
+// Phases inside one launch, chained by flags:
+//   route  (every workgroup)   top-k over the logits, softmax gates, and per
+//                              (route item, local expert) counts and ranks
+//   scan   (ticket-0 workgroup) exclusive scan of the counts in
+//                              (expert, source, token) order -> slot offsets,
+//                              then the grouped-GEMM tile list; publishes
+//                              scan_ready
+//   land   (land workgroups)   copies each routed token row straight into its
+//                              expert slot and releases that route item's flag
+//   compute (compute workgroups) grouped-GEMM tiles over the expert slots; a
+//                              tile waits for the flags of the route items whose
+//                              tokens fill its rows; y = bf16(gate * acc)
+// A route item is kRouteTokens consecutive tokens of one source rank.
+#include "mk_params.h"
+
+namespace mk {
+
+struct MoeShared {
+  uint32_t word;
+  int32_t wave_cnt[4][kMaxLocalExperts];
+  int32_t scan_tmp[4];
+  int32_t list_tok[kRouteTokens * 8];   // (slot << 8 | token-in-item) of the item's local rows
+  int32_t n_list;
+  int32_t tile_base[kMaxLocalExperts + 2];
+  int32_t expert_off[kMaxLocalExperts + 1];
+};
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Block-wide exclusive scan of one int per thread; returns the prefix and
+// writes the block total to *total.  Uses tmp[4].
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *tmp, int32_t *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int32_t t = tmp[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+// ---------------------------------------------------------------- route
+
+__device__ __forceinline__ void moe_route_item(const MoeParams &p, int item, MoeShared &sh) {
+  const int s = item / p.items_per_src, b = item % p.items_per_src;
+  const int t = b * kRouteTokens + (int)threadIdx.x;
+  const bool valid = t < p.T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // top-k by value, descending, kept sorted in sel/selv (fixed-size,
+  // fully unrolled so the arrays stay in registers).  A new expert goes
+  // before the first kept entry it is strictly larger than, so equal logits
+  // keep the lower expert id first.
+  int sel[8];
+  float selv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { sel[j] = -1; selv[j] = 0.f; }
+  if (valid) {
+    const float *lg = p.logits[s] + (size_t)t * p.E;
+    for (int e = 0; e < p.E; ++e) {
+      const float v = lg[e];
+#pragma unroll
+      for (int j = 7; j >= 0; --j) {
+        if (j >= p.top_k) continue;
+        const bool here = sel[j] < 0 || v > selv[j];
+        const bool above = j > 0 && (sel[j - 1] < 0 || v > selv[j - 1]);
+        if (here) {
+          if (above) { sel[j] = sel[j - 1]; selv[j] = selv[j - 1]; }
+          else { sel[j] = e; selv[j] = v; }
+        }
+      }
+    }
+    const float mx = selv[0];
+    float sum = 0.f;
+    for (int e = 0; e < p.E; ++e) sum += expf(lg[e] - mx);
+    const size_t o = ((size_t)s * p.T + t) * p.top_k;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= p.top_k) continue;
+      p.topk_idx[o + j] = sel[j];
+      p.topk_gate[o + j] = expf(selv[j] - mx) / sum;
+    }
+  }
+  // per local expert: count and rank of this item's tokens (token order)
+  const int e_lo = p.rank * p.E_loc;
+  int my_rank[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) my_rank[j] = -1;
+  for (int e = 0; e < p.E_loc; ++e) {
+    bool mine = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mine |= (j < p.top_k) && valid && sel[j] == e_lo + e;
+    const uint64_t m = __ballot(mine);
+    const int r = __popcll(m & lanemask_lt());
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < p.top_k && valid && sel[j] == e_lo + e) my_rank[j] = r;
+    if (lane == 0) sh.wave_cnt[wave][e] = __popcll(m);
+  }
+  __syncthreads();
+  for (int e = 0; e < p.E_loc; ++e) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += sh.wave_cnt[w][e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < p.top_k && valid && sel[j] == e_lo + e) my_rank[j] += before;
+  }
+  if (valid) {
+    const size_t o = ((size_t)s * p.T + t) * p.top_k;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < p.top_k) p.tok_rank[o + j] = my_rank[j];
+  }
+  if (threadIdx.x < (unsigned)p.E_loc) {
+    int tot = 0;
+    for (int w = 0; w < 4; ++w) tot += sh.wave_cnt[w][threadIdx.x];
+    p.item_cnt[(size_t)item * p.E_loc + threadIdx.x] = tot;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- scan
+
+template <int BM>
+__device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
+  int32_t running = 0;
+  for (int e = 0; e < p.E_loc; ++e) {
+    if (threadIdx.x == 0) p.expert_offsets[e] = running;
+    for (int base = 0; base < p.n_items; base += kThreads) {
+      const int i = base + (int)threadIdx.x;
+      const int32_t v = i < p.n_items ? p.item_cnt[(size_t)i * p.E_loc + e] : 0;
+      int32_t total;
+      const int32_t ex = block_exclusive_scan(v, sh.scan_tmp, &total);
+      if (i < p.n_items) {
+        p.item_base[(size_t)i * p.E_loc + e] = running + ex;
+        if (i % p.items_per_src == 0) p.chunk_offsets[e * (p.S + 1) + i / p.items_per_src] = running + ex;
+      }
+      running += total;
+    }
+    if (threadIdx.x == 0) p.chunk_offsets[e * (p.S + 1) + p.S] = running;
+  }
+  if (threadIdx.x == 0) {
+    p.expert_offsets[p.E_loc] = running;
+    p.tile_base[1] = running;
+  }
+  __syncthreads();
+  // grouped-GEMM row tiles in m-tile-major order across experts (tokens of
+  // the first sources land first and fill every expert's first rows)
+  if (threadIdx.x == 0) {
+    int ntile_rows = 0, max_mt = 0;
+    for (int e = 0; e < p.E_loc; ++e)
+      max_mt = max(max_mt, (p.expert_offsets[e + 1] - p.expert_offsets[e] + BM - 1) / BM);
+    for (int mt = 0; mt < max_mt; ++mt)
+      for (int e = 0; e < p.E_loc; ++e)
+        if (mt * BM < p.expert_offsets[e + 1] - p.expert_offsets[e])
+          p.tile_base[2 + ntile_rows++] = (e << 16) | mt;
+    p.tile_base[0] = ntile_rows;
+  }
+}
+
+// ---------------------------------------------------------------- land
+
+__device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, MoeShared &sh) {
+  const int s = item / p.items_per_src, b = item % p.items_per_src;
+  const int t = b * kRouteTokens + (int)threadIdx.x;
+  const int e_lo = p.rank * p.E_loc;
+  if (threadIdx.x == 0) sh.n_list = 0;
+  __syncthreads();
+  if (t < p.T) {
+    const size_t o = ((size_t)s * p.T + t) * p.top_k;
+    for (int j = 0; j < p.top_k; ++j) {
+      const int e = p.topk_idx[o + j] - e_lo;
+      if (e >= 0 && e < p.E_loc) {
+        const int slot = p.item_base[(size_t)item * p.E_loc + e] + p.tok_rank[o + j];
+        p.slot_token[slot] = s * p.T + t;
+        p.slot_gate[slot] = p.topk_gate[o + j];
+        const int k = atomicAdd(&sh.n_list, 1);
+        sh.list_tok[k] = (slot << 8) | (int)threadIdx.x;
+      }
+    }
+  }
+  __syncthreads();
+  const int n = (int)uniform((uint32_t)sh.n_list);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t row_vec = (size_t)p.H / 8;   // 16-byte vectors per token row
+  for (int r = wave; r < n; r += 4) {
+    const int v = sh.list_tok[r];
+    const int slot = v >> 8, tt = b * kRouteTokens + (v & 255);
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(p.x[s] + (size_t)tt * p.H);
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(p.x_slots + (size_t)slot * p.H);
+    size_t i = lane;
+    for (; i + 3 * 64 < row_vec; i += 4 * 64) {
+      const u32x4_t a0 = src[i], a1 = src[i + 64], a2 = src[i + 128], a3 = src[i + 192];
+      dst[i] = a0; dst[i + 64] = a1; dst[i + 128] = a2; dst[i + 192] = a3;
+    }
+    for (; i < row_vec; i += 64) dst[i] = src[i];
+  }
+}
+
+// ---------------------------------------------------------------- compute
+
+// Thread 0: wait for every route item whose tokens of local expert e fall in
+// slots [slot0, slot1).  item_base[i][e] is non-decreasing in i.
+__device__ __forceinline__ bool moe_wait_rows(const MoeParams &p, int e, int slot0, int slot1) {
+  // first item whose range for e ends after slot0
+  int lo = 0, hi = p.n_items;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int end = p.item_base[(size_t)mid * p.E_loc + e] + p.item_cnt[(size_t)mid * p.E_loc + e];
+    if (end > slot0) hi = mid; else lo = mid + 1;
+  }
+  for (int i = lo; i < p.n_items; ++i) {
+    if (p.item_base[(size_t)i * p.E_loc + e] >= slot1) break;
+    if (!spin_until_eq(p.sync, flag_ptr(p.sync, (uint32_t)i), p.sync.epoch, (uint32_t)i)) return false;
+  }
+  return true;
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeShared &sh) {
+  using C = TileCfg<BM, BN>;
+  if (threadIdx.x <= (unsigned)p.E_loc) sh.expert_off[threadIdx.x] = p.expert_offsets[threadIdx.x];
+  if (threadIdx.x == 0) sh.tile_base[0] = p.tile_base[0];
+  __syncthreads();
+  const int n_row_tiles = (int)uniform((uint32_t)sh.tile_base[0]);
+  const int n_tiles = n_row_tiles * p.tiles_n;
+  const int ld = p.H * 2;
+  for (;;) {
+    const uint32_t t = next_index(&p.sync.ctrl->tile_ctr, &sh.word);
+    if (t >= (uint32_t)n_tiles) break;
+    const int rt = (int)t / p.tiles_n, nb = (int)t % p.tiles_n;
+    const int code = (int)uniform((uint32_t)p.tile_base[2 + rt]);
+    const int e = code >> 16, mt = code & 0xFFFF;
+    const int slot0 = (int)uniform((uint32_t)sh.expert_off[e]) + mt * BM;
+    const int slot1 = min(slot0 + BM, (int)uniform((uint32_t)sh.expert_off[e + 1]));
+    const int n0 = nb * BN;
+    bool ok0 = true;
+    if (threadIdx.x == 0) ok0 = moe_wait_rows(p, e, slot0, slot1);
+    if (!wg_sync_ok(ok0, &sh.word)) break;
+    const int valid_n = min(BN, p.N - n0);
+    const i32x4_t ra = make_vdesc(p.x_slots + (size_t)slot0 * p.H, (uint32_t)((slot1 - slot0) * ld));
+    const i32x4_t rb = make_vdesc(p.wt + ((size_t)e * p.N + n0) * p.H, (uint32_t)(valid_n * ld));
+    f32x16_t acc[C::FM][C::FN];
+    gemm_tile<BM, BN>(smem, ra, ld, rb, ld, p.H, acc);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const AccPos<BM, BN> p0 = acc_pos<BM, BN>(i, 0, 0);
+      const int slot = slot0 + p0.row;
+      if (slot >= slot1) continue;
+      const float gt = p.no_gate ? 1.f : p.slot_gate[slot];
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + acc_pos<BM, BN>(i, j, g).col;
+          if (col >= p.N) continue;
+          const f32x16_t &v = acc[i][j];
+          float x0 = v[g * 4 + 0], x1 = v[g * 4 + 1], x2 = v[g * 4 + 2], x3 = v[g * 4 + 3];
+          if (!p.no_gate) { x0 *= gt; x1 *= gt; x2 *= gt; x3 *= gt; }
+          *reinterpret_cast<uint2 *>(p.y + (size_t)slot * p.N + col) = pack_bf16x4(x0, x1, x2, x3);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- kernel
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void moe_kernel(MoeParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
+  __shared__ MoeShared sh;
+  const uint32_t ticket = take_ticket(p.sync, &sh.word);
+  Ctrl *ctrl = p.sync.ctrl;
+
+  // route: every workgroup takes route items until none are left
+  for (;;) {
+    const uint32_t it = next_index(&ctrl->route_ctr, &sh.word);
+    if (it >= (uint32_t)p.n_items) break;
+    moe_route_item(p, (int)it, sh);
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) add_acq_rel(&ctrl->route_done, 1u);
+  }
+
+  bool ok = true;
+  if (ticket == 0) {
+    bool ok0 = true;
+    if (threadIdx.x == 0) ok0 = spin_until_ge(p.sync, &ctrl->route_done, (uint32_t)p.n_items, 0xFFFF0001u);
+    ok = wg_sync_ok(ok0, &sh.word);
+    if (ok) {
+      moe_scan<BM>(p, sh);
+      __threadfence();
+      __syncthreads();
+      if (threadIdx.x == 0) st_release(&ctrl->scan_ready, p.sync.epoch);
+    }
+  }
+  if (ok && ticket < (uint32_t)(p.n_land + p.n_compute)) {
+    bool ok0 = true;
+    if (threadIdx.x == 0) ok0 = spin_until_eq(p.sync, &ctrl->scan_ready, p.sync.epoch, 0xFFFF0002u);
+    ok = wg_sync_ok(ok0, &sh.word);
+  }
+  if (ok) {
+    if (ticket < (uint32_t)p.n_land) {
+      for (;;) {
+        const uint32_t it = next_index(&ctrl->land_ctr, &sh.word);
+        if (it >= (uint32_t)p.n_items) break;
+        moe_land_item(p, (int)it, sh);
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) st_release(flag_ptr(p.sync, it), p.sync.epoch);
+      }
+    } else if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
+      moe_compute<BM, BN>(p, smem, sh);
+    }
+  }
+  finish_launch(p.sync);
+}
+
+hipError_t launch_moe(const MoeParams &p, int bm, int grid, hipStream_t s) {
+  if (bm == 256)
+    hipLaunchKernelGGL((moe_kernel<256, 256>), dim3(grid), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((moe_kernel<128, 128>), dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t occupancy_moe(int bm, int *blocks_per_cu) {
+  const void *f = bm == 256 ? (const void *)moe_kernel<256, 256> : (const void *)moe_kernel<128, 128>;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, 0);
+}
+
+}  // namespace mk

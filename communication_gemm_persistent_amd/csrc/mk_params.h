@@ -1,0 +1,83 @@
+// Kernel parameter blocks shared by the host launcher and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/mk.h"
+#include "mk_device.h"
+
+namespace mk {
+
+// AllGather + GEMM.  Landing unit: a "land block" of lb_rows rows of one
+// shard (one ready flag each), copied as items_per_block items of item_rows
+// rows.  Flag of block j of shard q: q * blocks_per_chunk + j.
+struct AgParams {
+  Sync sync;
+  const uint16_t *shard[MK_MAX_WORLD];
+  const uint16_t *bt;
+  uint16_t *c;
+  uint16_t *ag;
+  int world, rank, m_s, n, k;
+  int n_land, n_compute;
+  int tiles_m, tiles_n, n_tiles, mb0;
+  int lb_rows, blocks_per_chunk, item_rows, items_per_block, n_items;
+  int prelanded;
+};
+
+// GEMM + ReduceScatter.
+struct RsParams {
+  Sync sync;
+  const uint16_t *a;
+  const uint16_t *bt;
+  const float *peer[MK_MAX_WORLD];
+  uint16_t *c_own;
+  uint16_t *outbox[MK_MAX_WORLD];
+  int world, rank, m, n, k, ms;
+  int n_compute;
+  int tiles_m, tiles_n, n_tiles, mb0;
+};
+
+// GEMM + AllReduce.
+struct ArParams {
+  Sync sync;
+  const uint16_t *a;
+  const uint16_t *bt;
+  const float *peer[MK_MAX_WORLD];
+  uint16_t *c;
+  uint16_t *bcast[MK_MAX_WORLD];
+  int world, rank, n_bcast, m, n, k;
+  int n_compute;
+  int tiles_m, tiles_n, n_tiles;
+};
+
+// MoE dispatch + grouped GEMM.  Route items are blocks of kRouteTokens
+// tokens of one source; an item's flag says all of its local tokens landed.
+constexpr int kRouteTokens = 256;
+constexpr int kMaxLocalExperts = 32;
+
+struct MoeParams {
+  Sync sync;
+  const uint16_t *x[MK_MAX_WORLD];
+  const float *logits[MK_MAX_WORLD];
+  const uint16_t *wt;
+  uint16_t *y;
+  int32_t *topk_idx;
+  float *topk_gate;
+  int32_t *slot_token;
+  int32_t *expert_offsets;
+  int32_t *chunk_offsets;
+  uint16_t *x_slots;
+  // workspace
+  int32_t *item_cnt;    // [n_items, E_loc] tokens of item routed to local expert e
+  int32_t *item_base;   // [n_items, E_loc] first slot of (item, e)
+  int32_t *tok_rank;    // [S*T, top_k] rank of the token within (item, e); -1 if not local
+  float *slot_gate;     // [cap]
+  int32_t *tile_base;   // [E_loc + 1] first GEMM tile of each expert
+  int S, T, H, N, E, E_loc, top_k, rank, cap;
+  int items_per_src, n_items;
+  int n_land, n_compute;
+  int tiles_n;
+  int no_gate;
+};
+
+}  // namespace mk

@@ -1,0 +1,252 @@
+"""ctypes binding of libmk (include/mk.h): argument marshalling only.
+
+Every operation runs in the HIP library; this module checks dtypes, shapes and
+contiguity of torch tensors, passes their data pointers and the current HIP
+stream, and turns status codes into exceptions.  It never computes anything
+itself and has no fallback: if libmk.so is missing, load() raises.
+
+bf16 tensors may be torch.bfloat16 or int16 / uint16 bit patterns.  Peer
+buffers may live on the GPU or in pinned host memory (pin_memory=True).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmk.so")
+
+MK_OK = 0
+MK_ERR_INVALID = 1
+MK_ERR_UNSUPPORTED = 2
+MK_ERR_OOM = 3
+MK_ERR_HIP = 4
+MK_ERR_TIMEOUT = 5
+
+OP_AG_GEMM = 0
+OP_GEMM_RS = 1
+OP_GEMM_AR = 2
+OP_MOE = 3
+
+F_PRELANDED = 0x1
+F_NO_GATE = 0x2
+
+MAX_WORLD = 16
+
+# Names declared in include/mk.h (the CPU tests check the library exports them).
+EXPORTS = ("mk_create", "mk_destroy", "mk_set_roles", "mk_get_roles", "mk_last_launch",
+           "mk_sync", "mk_status_string", "mk_last_error", "mk_ag_gemm", "mk_gemm_rs",
+           "mk_gemm_ar", "mk_moe_dispatch_gemm")
+
+
+class MkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("device", ctypes.c_int), ("spin_timeout_ms", ctypes.c_int),
+                ("flags", ctypes.c_uint)]
+
+
+class Roles(ctypes.Structure):
+    _fields_ = [("n_land", ctypes.c_int), ("n_compute", ctypes.c_int), ("n_reduce", ctypes.c_int)]
+
+    def as_tuple(self) -> Tuple[int, int, int]:
+        return (self.n_land, self.n_compute, self.n_reduce)
+
+
+_lib: Optional[ctypes.CDLL] = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_u = ctypes.c_uint
+_pp = ctypes.POINTER(ctypes.c_void_p)
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmk.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m communication_gemm_persistent_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.mk_create.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_Config)]
+    lib.mk_destroy.argtypes = [_vp]
+    lib.mk_set_roles.argtypes = [_vp, _i, ctypes.POINTER(Roles)]
+    lib.mk_get_roles.argtypes = [_vp, _i, ctypes.POINTER(Roles)]
+    lib.mk_last_launch.argtypes = [_vp, _i, ctypes.POINTER(Roles), ctypes.POINTER(_i)]
+    lib.mk_sync.argtypes = [_vp, _vp]
+    lib.mk_status_string.argtypes = [_i]
+    lib.mk_status_string.restype = ctypes.c_char_p
+    lib.mk_last_error.argtypes = [_vp]
+    lib.mk_last_error.restype = ctypes.c_char_p
+    lib.mk_ag_gemm.argtypes = [_vp, _vp, _i, _i, _pp, _vp, _vp, _vp, _i, _i, _i, _u]
+    lib.mk_gemm_rs.argtypes = [_vp, _vp, _i, _i, _vp, _vp, _pp, _vp, _pp, _i, _i, _i, _u]
+    lib.mk_gemm_ar.argtypes = [_vp, _vp, _i, _i, _vp, _vp, _pp, _vp, _pp, _i, _i, _i, _i, _u]
+    lib.mk_moe_dispatch_gemm.argtypes = [_vp, _vp, _i, _i, _pp, _pp, _vp, _i, _i, _i, _i, _i, _i,
+                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _u]
+    for name in EXPORTS:
+        if name not in ("mk_status_string", "mk_last_error"):
+            getattr(lib, name).restype = _i
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- marshalling
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtypes, shape=None) -> int:
+    if t is None:
+        return 0
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+    return t.data_ptr()
+
+
+def _ptr_array(ptrs: Sequence[int]):
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p or None
+    return arr
+
+
+def _stream(stream, device: int) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Handle:
+    """One libmk handle bound to a device; calls on it must be stream-ordered."""
+
+    def __init__(self, device: int = 0, spin_timeout_ms: int = 0):
+        self.lib = load()
+        self.device = device
+        h = _vp()
+        cfg = _Config(device, spin_timeout_ms, 0)
+        self._check(self.lib.mk_create(ctypes.byref(h), ctypes.byref(cfg)), "mk_create", None)
+        self.h = h
+
+    # -- housekeeping
+    def close(self) -> None:
+        if getattr(self, "h", None):
+            self.lib.mk_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def _check(self, st: int, what: str, h) -> None:
+        if st != MK_OK:
+            detail = self.lib.mk_last_error(h).decode() if h else ""
+            msg = self.lib.mk_status_string(st).decode()
+            raise MkError(st, f"{what}: {msg}" + (f" ({detail})" if detail else ""))
+
+    def set_roles(self, op: int, n_land: int = -1, n_compute: int = -1, n_reduce: int = -1) -> None:
+        r = Roles(n_land, n_compute, n_reduce)
+        self._check(self.lib.mk_set_roles(self.h, op, ctypes.byref(r)), "mk_set_roles", self.h)
+
+    def get_roles(self, op: int) -> Tuple[int, int, int]:
+        r = Roles()
+        self._check(self.lib.mk_get_roles(self.h, op, ctypes.byref(r)), "mk_get_roles", self.h)
+        return r.as_tuple()
+
+    def last_launch(self, op: int) -> Tuple[Tuple[int, int, int], int]:
+        r = Roles()
+        g = _i()
+        self._check(self.lib.mk_last_launch(self.h, op, ctypes.byref(r), ctypes.byref(g)),
+                    "mk_last_launch", self.h)
+        return r.as_tuple(), g.value
+
+    def sync(self, stream=None) -> None:
+        self._check(self.lib.mk_sync(self.h, _vp(_stream(stream, self.device))), "mk_sync", self.h)
+
+    # -- operations
+    def ag_gemm(self, shards: Sequence[torch.Tensor], bt: torch.Tensor, c: torch.Tensor,
+                a_gathered: torch.Tensor, rank: int = 0, flags: int = 0, stream=None) -> None:
+        W = len(shards)
+        m_s, k = shards[rank].shape
+        n = bt.shape[0]
+        sp = [0 if (s is None and q != rank and flags & F_PRELANDED)
+              else _ptr(s, f"shards[{q}]", _BF16, (m_s, k)) for q, s in enumerate(shards)]
+        st = self.lib.mk_ag_gemm(self.h, _vp(_stream(stream, self.device)), W, rank, _ptr_array(sp),
+                                 _ptr(bt, "bt", _BF16, (n, k)), _ptr(c, "c", _BF16, (W * m_s, n)),
+                                 _ptr(a_gathered, "a_gathered", _BF16, (W * m_s, k)),
+                                 m_s, n, k, flags)
+        self._check(st, "mk_ag_gemm", self.h)
+
+    def gemm_rs(self, a: torch.Tensor, bt: torch.Tensor, peer_part: Sequence[Optional[torch.Tensor]],
+                c_own: torch.Tensor, outbox: Sequence[Optional[torch.Tensor]], rank: int = 0,
+                flags: int = 0, stream=None) -> None:
+        W = len(peer_part)
+        m, k = a.shape
+        n = bt.shape[0]
+        ms = m // W
+        pp = [0 if q == rank else _ptr(peer_part[q], f"peer_part[{q}]", (torch.float32,), (ms, n))
+              for q in range(W)]
+        ob = [0 if q == rank else _ptr(outbox[q], f"outbox[{q}]", _BF16, (ms, n)) for q in range(W)]
+        st = self.lib.mk_gemm_rs(self.h, _vp(_stream(stream, self.device)), W, rank,
+                                 _ptr(a, "a", _BF16), _ptr(bt, "bt", _BF16, (n, k)), _ptr_array(pp),
+                                 _ptr(c_own, "c_own", _BF16, (ms, n)), _ptr_array(ob), m, n, k, flags)
+        self._check(st, "mk_gemm_rs", self.h)
+
+    def gemm_ar(self, a: torch.Tensor, bt: torch.Tensor, peer_part: Sequence[Optional[torch.Tensor]],
+                c: torch.Tensor, bcast: Sequence[torch.Tensor], rank: int = 0, flags: int = 0,
+                stream=None) -> None:
+        W = len(peer_part)
+        m, k = a.shape
+        n = bt.shape[0]
+        pp = [0 if q == rank else _ptr(peer_part[q], f"peer_part[{q}]", (torch.float32,), (m, n))
+              for q in range(W)]
+        bc = [_ptr(b, f"bcast[{i}]", _BF16, (m, n)) for i, b in enumerate(bcast)]
+        st = self.lib.mk_gemm_ar(self.h, _vp(_stream(stream, self.device)), W, rank,
+                                 _ptr(a, "a", _BF16), _ptr(bt, "bt", _BF16, (n, k)), _ptr_array(pp),
+                                 _ptr(c, "c", _BF16, (m, n)), _ptr_array(bc), len(bcast), m, n, k,
+                                 flags)
+        self._check(st, "mk_gemm_ar", self.h)
+
+    def moe_dispatch_gemm(self, x: Sequence[torch.Tensor], logits: Sequence[torch.Tensor],
+                          wt: torch.Tensor, E: int, top_k: int, y: torch.Tensor,
+                          topk_idx: torch.Tensor, topk_gate: torch.Tensor,
+                          slot_token: torch.Tensor, expert_offsets: torch.Tensor,
+                          chunk_offsets: torch.Tensor, x_slots: torch.Tensor, rank: int = 0,
+                          flags: int = 0, stream=None) -> None:
+        S = len(x)
+        T, H = x[0].shape
+        E_loc, N, _ = wt.shape
+        cap = y.shape[0]
+        xp = [_ptr(xx, f"x[{s}]", _BF16, (T, H)) for s, xx in enumerate(x)]
+        lp = [_ptr(ll, f"logits[{s}]", (torch.float32,), (T, E)) for s, ll in enumerate(logits)]
+        i32 = (torch.int32,)
+        st = self.lib.mk_moe_dispatch_gemm(
+            self.h, _vp(_stream(stream, self.device)), S, rank, _ptr_array(xp), _ptr_array(lp),
+            _ptr(wt, "wt", _BF16, (E_loc, N, H)), T, H, N, E, E_loc, top_k,
+            _ptr(y, "y", _BF16, (cap, N)), _ptr(topk_idx, "topk_idx", i32, (S * T, top_k)),
+            _ptr(topk_gate, "topk_gate", (torch.float32,), (S * T, top_k)),
+            _ptr(slot_token, "slot_token", i32, (cap,)),
+            _ptr(expert_offsets, "expert_offsets", i32, (E_loc + 1,)),
+            _ptr(chunk_offsets, "chunk_offsets", i32, (E_loc, S + 1)),
+            _ptr(x_slots, "x_slots", _BF16, (cap, H)), cap, flags)
+        self._check(st, "mk_moe_dispatch_gemm", self.h)
