@@ -1,0 +1,353 @@
+"""Benchmark of the fused AllGather+GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+
+One step = one persistent fused AllGather+GEMM launch of one rank's share of
+a tensor-parallel MLP up-projection with 8 emulated ranks: local shard
+[1024, 8192] bf16 plus 7 peer shards landing from a separate HBM region,
+B [8192, 3584] bf16, C [8192, 3584] bf16 (481.04 GFLOP).  W untimed warm-up
+steps, then K timed steps between device synchronisations; every step is
+also bracketed by HIP events on the stream the kernel runs on, which gives
+the kernel's average duration for the roofline.
+
+Also measured and reported in the same JSON line (context, not the value):
+  * overlap efficiency = max(GEMM alone, transfer alone) / fused, where GEMM
+    alone is the same launch with A already gathered and transfer alone the
+    same launch with no compute workgroups;
+  * the same with the peers in pinned host memory (landing over PCIe);
+  * the fused call with the 256 MB Infinity Cache flushed before each step;
+  * GEMM+ReduceScatter, GEMM+AllReduce and MoE dispatch + grouped GEMM at
+    their workload sizes (--quick skips these);
+  * the CPU oracle timed on a bounded sample of the same workload.
+Exactly one JSON line goes to stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+WORKLOAD = "ag_gemm_w8_8192x3584x8192"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "communication_gemm_persistent_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(src_hash: str):
+    """HBM bytes per launch measured by rocprofv3 counters for this exact kernel
+    source (profiles/ag_gemm_w8_counters.json), else None."""
+    p = os.path.join(ROOT, "profiles", "ag_gemm_w8_8192x3584x8192_counters.json")
+    try:
+        with open(p) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share; peers are emulated by buffers. "
+              "Runs on more than one GPU are not supported.", file=sys.stderr)
+        return 2
+
+    import torch
+    from communication_gemm_persistent_amd import inputs as I
+    from communication_gemm_persistent_amd import mk
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    h = mk.Handle(0, spin_timeout_ms=5000)
+
+    def to_dev(bits_np, where="hbm"):
+        t = torch.from_numpy(np.ascontiguousarray(bits_np).view(np.int16)).view(torch.bfloat16)
+        return t.pin_memory() if where == "host" else t.to(dev)
+
+    def to_dev_f32(x, where="hbm"):
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+        return t.pin_memory() if where == "host" else t.to(dev)
+
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        flush_buf.fill_(1)
+
+    def time_calls(fn, reps, warm, flushed=False):
+        """Per-call kernel durations (ms) from events on the launch stream."""
+        for _ in range(warm):
+            fn()
+        h.sync()
+        durs = []
+        for _ in range(reps):
+            if flushed:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            durs.append((e0, e1))
+        h.sync()
+        return [a.elapsed_time(b) for a, b in durs]
+
+    # ------------------------------------------------------------ headline workload
+    wl = I.CONFIGS[WORKLOAD]
+    p = wl.params
+    W, m_s, n, k = p["world"], p["m_s"], p["n"], p["k"]
+    flops = wl.flops()
+    log(f"[bench] generating {WORKLOAD} inputs")
+    d = I.gen_workload(WORKLOAD)
+    shards = [to_dev(s) for s in d["shards"]]
+    bt = to_dev(I.transpose_bits(d["b"]))
+    c = torch.empty((W * m_s, n), dtype=torch.bfloat16, device=dev)
+    ag = torch.empty((W * m_s, k), dtype=torch.bfloat16, device=dev)
+
+    def fused():
+        h.ag_gemm(shards, bt, c, ag, rank=0)
+
+    log("[bench] warm-up")
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} fused steps")
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fused()
+        e1.record(stream)
+        events.append((e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    h.sync()
+    kern_ms = [a.elapsed_time(b) for a, b in events]
+    ms_step = wall * 1e3 / args.steps
+    kern_avg = float(np.mean(kern_ms))
+    value = flops * args.steps / wall / 1e12
+    roles_fused, grid_fused = h.last_launch(mk.OP_AG_GEMM)
+
+    # overlap efficiency: GEMM alone (pre-landed) and transfer alone (no compute)
+    reps = max(10, args.steps // 2)
+    log("[bench] GEMM alone / transfer alone")
+    t_gemm = float(np.median(time_calls(lambda: h.ag_gemm(shards, bt, c, ag, rank=0,
+                                                          flags=mk.F_PRELANDED), reps, 3)))
+    h.set_roles(mk.OP_AG_GEMM, n_land=roles_fused[0], n_compute=0)
+    t_xfer = float(np.median(time_calls(fused, reps, 3)))
+    h.set_roles(mk.OP_AG_GEMM)
+    t_fused_med = float(np.median(kern_ms))
+    t_fused_flushed = float(np.median(time_calls(fused, reps, 2, flushed=True)))
+    t_gemm_flushed = float(np.median(time_calls(lambda: h.ag_gemm(shards, bt, c, ag, rank=0,
+                                                                  flags=mk.F_PRELANDED),
+                                                reps, 2, flushed=True)))
+    landed_bytes = (W - 1) * m_s * k * 2
+
+    # peers in pinned host memory: landing reads cross PCIe
+    log("[bench] PCIe (pinned host) peers")
+    shards_host = [shards[0]] + [to_dev(s, "host") for s in d["shards"][1:]]
+
+    def fused_host():
+        h.ag_gemm(shards_host, bt, c, ag, rank=0)
+
+    t_fused_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
+    h.set_roles(mk.OP_AG_GEMM, n_land=roles_fused[0], n_compute=0)
+    t_xfer_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
+    h.set_roles(mk.OP_AG_GEMM)
+    del shards_host
+
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile(src_hash)
+    achieved = flops / (kern_avg * 1e-3) / 1e12
+    result = {
+        "metric": "fused AG+GEMM TFLOP/s & % bf16 MFMA peak; overlap eff. vs GEMM-alone",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "emulated_world": W, "rank": 0, "m_shard": m_s,
+                   "m": W * m_s, "n": n, "k": k, "peers": "separate HBM region",
+                   "roles": {"land": roles_fused[0], "compute": roles_fused[1]},
+                   "grid": grid_fused},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel_avg_ms": round(kern_avg, 4),
+                     "kernel_source_hash": src_hash},
+        "overlap": {
+            "t_fused_ms": round(t_fused_med, 4), "t_gemm_alone_ms": round(t_gemm, 4),
+            "t_transfer_alone_ms": round(t_xfer, 4),
+            "efficiency": round(max(t_gemm, t_xfer) / t_fused_med, 4),
+            "gemm_alone_over_fused": round(t_gemm / t_fused_med, 4),
+            "gemm_alone_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 2),
+            "landing_GBps": round(2 * landed_bytes / (t_xfer * 1e-3) / 1e9, 1),
+            "mall_flushed": {"t_fused_ms": round(t_fused_flushed, 4),
+                             "t_gemm_alone_ms": round(t_gemm_flushed, 4),
+                             "fused_tflops": round(flops / (t_fused_flushed * 1e-3) / 1e12, 2)},
+            "pcie_host_peers": {"t_fused_ms": round(t_fused_host, 4),
+                                "t_transfer_alone_ms": round(t_xfer_host, 4),
+                                "pcie_read_GBps": round(landed_bytes / (t_xfer_host * 1e-3) / 1e9, 2),
+                                "efficiency": round(max(t_gemm, t_xfer_host) / t_fused_host, 4)},
+        },
+    }
+    del shards, bt, c, ag, d
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ other fused ops
+    if not args.quick:
+        result["other_ops"] = other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev)
+
+    # ------------------------------------------------------------ CPU baseline
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(I, flops)
+    h.close()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev):
+    import torch
+    out = {}
+    # GEMM + ReduceScatter
+    name = "gemm_rs_w8_8192x8192x3584"
+    log(f"[bench] {name}")
+    wl = I.CONFIGS[name]
+    p = wl.params
+    d = I.gen_workload(name)
+    W, m, n, k = p["world"], p["m"], p["n"], p["k"]
+    ms = m // W
+    a, bt = to_dev(d["a"]), to_dev(I.transpose_bits(d["b"]))
+    peers = [None] + [to_dev_f32(x) for x in d["peers"][1:]]
+    c_own = torch.empty((ms, n), dtype=torch.bfloat16, device=dev)
+    outbox = [None] + [torch.empty((ms, n), dtype=torch.bfloat16, device=dev) for _ in range(W - 1)]
+    t = float(np.median(time_calls(lambda: h.gemm_rs(a, bt, peers, c_own, outbox, rank=0), 20, 3)))
+    byts = (W - 1) * ms * n * 4 + ms * n * 2 + (W - 1) * ms * n * 2
+    out[name] = {"ms": round(t, 4), "tflops": round(wl.flops() / (t * 1e-3) / 1e12, 2),
+                 "reduce_scatter_GBps": round(byts / (t * 1e-3) / 1e9, 1),
+                 "roles": h.last_launch(mk.OP_GEMM_RS)[0]}
+    del a, bt, peers, c_own, outbox, d
+    torch.cuda.empty_cache()
+
+    # GEMM + AllReduce
+    name = "gemm_ar_w8_2048x8192x1024"
+    log(f"[bench] {name}")
+    wl = I.CONFIGS[name]
+    p = wl.params
+    d = I.gen_workload(name)
+    W, m, n, k, nb = p["world"], p["m"], p["n"], p["k"], p["n_bcast"]
+    a, bt = to_dev(d["a"]), to_dev(I.transpose_bits(d["b"]))
+    peers = [None] + [to_dev_f32(x) for x in d["peers"][1:]]
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    bc = [torch.empty((m, n), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
+    t = float(np.median(time_calls(lambda: h.gemm_ar(a, bt, peers, c, bc, rank=0), 20, 3)))
+    byts = (W - 1) * m * n * 4 + (1 + nb) * m * n * 2 + (m * k + n * k) * 2
+    out[name] = {"ms": round(t, 4), "tflops": round(wl.flops() / (t * 1e-3) / 1e12, 2),
+                 "hbm_GBps": round(byts / (t * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                 "roles": h.last_launch(mk.OP_GEMM_AR)[0]}
+    del a, bt, peers, c, bc, d
+    torch.cuda.empty_cache()
+
+    # MoE dispatch + grouped GEMM
+    name = "moe_s8_t4096_h4096_n1536_e64"
+    log(f"[bench] {name}")
+    wl = I.CONFIGS[name]
+    p = wl.params
+    d = I.gen_workload(name)
+    S, T, H, N, E, E_loc, top_k = (p[x] for x in ("S", "T", "H", "N", "E", "E_loc", "top_k"))
+    cap = S * T * min(top_k, E_loc)
+    x = [to_dev(v) for v in d["x"]]
+    lg = [to_dev_f32(v) for v in d["logits"]]
+    wt = to_dev(I.transpose_bits(d["w"]))
+    y = torch.empty((cap, N), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((S * T, top_k), dtype=torch.int32, device=dev)
+    gate = torch.empty((S * T, top_k), dtype=torch.float32, device=dev)
+    st = torch.empty((cap,), dtype=torch.int32, device=dev)
+    eo = torch.empty((E_loc + 1,), dtype=torch.int32, device=dev)
+    co = torch.empty((E_loc, S + 1), dtype=torch.int32, device=dev)
+    xs = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+
+    def moe():
+        h.moe_dispatch_gemm(x, lg, wt, E, top_k, y, idx, gate, st, eo, co, xs, rank=0)
+
+    t = float(np.median(time_calls(moe, 20, 3)))
+    n_slots = int(eo[-1].item())
+    fl = wl.flops(n_slots)
+    byts = S * T * E * 4 + 2 * n_slots * H * 2 + n_slots * H * 2 + E_loc * H * N * 2 + n_slots * N * 2
+    out[name] = {"ms": round(t, 4), "n_slots": n_slots, "tflops": round(fl / (t * 1e-3) / 1e12, 2),
+                 "GBps": round(byts / (t * 1e-3) / 1e9, 1), "roles": h.last_launch(mk.OP_MOE)[0]}
+    del x, lg, wt, y, idx, gate, st, eo, co, xs, d
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(I, flops_full):
+    """The float64 CPU oracle on a bounded sample of the headline workload:
+    the first R output rows (all 3584 columns, K = 8192, the gather included),
+    R chosen from a short calibration so the sample takes about 10 s."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    log("[bench] CPU oracle baseline")
+    d = I.gen_workload(WORKLOAD)
+    m_total = 8192
+    rows = np.arange(128)
+    t0 = time.perf_counter()
+    O.ag_gemm_rows(d["shards"], d["b"], rows)
+    t_cal = time.perf_counter() - t0
+    R = int(min(m_total, max(128, 128 * 10.0 / max(t_cal, 1e-3))))
+    rows = np.arange(R)
+    t0 = time.perf_counter()
+    O.ag_gemm_rows(d["shards"], d["b"], rows)
+    t = time.perf_counter() - t0
+    fl = flops_full * R / m_total
+    return {"value": round(fl / t / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{R} of {m_total} output rows of {WORKLOAD} (all columns, K=8192), "
+                      f"float64 numpy matmul with the gather, {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -33,6 +33,7 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format,
 
 // Error codes recorded on the device (match mk_status values).
 constexpr uint32_t kErrTimeout = MK_ERR_TIMEOUT;
+constexpr uint32_t kErrInternal = 100;  // an index check failed; reported as MK_ERR_HIP
 
 // One control block per handle.  Every counter lives on its own 64-byte line.
 struct Ctrl {

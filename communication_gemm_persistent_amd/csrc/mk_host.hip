@@ -305,8 +305,12 @@ mk_status mk_sync(mk_handle h, mk_stream stream) {
     e = hipMemcpy(&h->ctrl->err_code, &zero, sizeof(zero), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(h, e, "clearing the error record");
     char buf[160];
-    std::snprintf(buf, sizeof(buf), "in-kernel wait timed out (code %u, wait id 0x%08x, epoch %u)",
-                  rec[0], rec[1], rec[2]);
+    if (rec[0] == MK_ERR_TIMEOUT)
+      std::snprintf(buf, sizeof(buf), "in-kernel wait timed out (wait id 0x%08x, epoch %u)",
+                    rec[1], rec[2]);
+    else
+      std::snprintf(buf, sizeof(buf), "in-kernel index check failed (code %u, info 0x%08x, epoch %u)",
+                    rec[0], rec[1], rec[2]);
     h->err = buf;
     return rec[0] == MK_ERR_TIMEOUT ? MK_ERR_TIMEOUT : MK_ERR_HIP;
   }

@@ -193,6 +193,10 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, MoeS
       const int e = p.topk_idx[o + j] - e_lo;
       if (e >= 0 && e < p.E_loc) {
         const int slot = p.item_base[(size_t)item * p.E_loc + e] + p.tok_rank[o + j];
+        if (slot < 0 || slot >= p.cap) {  // cannot happen when routing and scan agree
+          raise_error(p.sync, kErrInternal, (uint32_t)item);
+          continue;
+        }
         p.slot_token[slot] = s * p.T + t;
         p.slot_gate[slot] = p.topk_gate[o + j];
         const int k = atomicAdd(&sh.n_list, 1);
@@ -254,6 +258,10 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
     const int e = code >> 16, mt = code & 0xFFFF;
     const int slot0 = (int)uniform((uint32_t)sh.expert_off[e]) + mt * BM;
     const int slot1 = min(slot0 + BM, (int)uniform((uint32_t)sh.expert_off[e + 1]));
+    if (e >= p.E_loc || slot0 < 0 || slot1 > p.cap || slot1 <= slot0) {
+      if (threadIdx.x == 0) raise_error(p.sync, kErrInternal, t);
+      break;
+    }
     const int n0 = nb * BN;
     bool ok0 = true;
     if (threadIdx.x == 0) ok0 = moe_wait_rows(p, e, slot0, slot1);

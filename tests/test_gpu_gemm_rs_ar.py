@@ -1,0 +1,180 @@
+"""GPU parity of GEMM+ReduceScatter and GEMM+AllReduce against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from communication_gemm_persistent_amd import inputs as I
+from tests.gpu_util import bits, dev_bf16, dev_f32, empty_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def handle(mk):
+    h = mk.Handle(0, spin_timeout_ms=10000)
+    yield h
+    h.close()
+
+
+# ---------------------------------------------------------------- ReduceScatter
+
+def run_rs(h, d, rank, where="hbm", out_where="hbm"):
+    W = len(d["peers"])
+    m, k = d["a"].shape
+    n = d["b"].shape[1]
+    ms = m // W
+    a = dev_bf16(d["a"])
+    bt = dev_bf16(I.transpose_bits(d["b"]))
+    peers = [None if p is None else dev_f32(p, where) for p in d["peers"]]
+    c_own = empty_bf16((ms, n))
+    outbox = [None if q == rank else empty_bf16((ms, n), out_where) for q in range(W)]
+    h.gemm_rs(a, bt, peers, c_own, outbox, rank=rank)
+    h.sync()
+    return bits(c_own), [None if o is None else bits(o) for o in outbox]
+
+
+def check_rs(d, rank, c_own, outbox, exact):
+    ref = O.gemm_rs(d["a"], d["b"], d["peers"], rank=rank)
+    cmp = O.assert_bits_equal if exact else O.assert_close_bf16
+    cmp(c_own, ref["c_own"], "c_own")
+    for q, o in enumerate(outbox):
+        if q != rank:
+            cmp(o, ref["outbox"][q], f"outbox[{q}]")
+
+
+@pytest.mark.parametrize("shape", [(4, 0, 512, 256, 128), (3, 2, 450, 200, 72), (8, 5, 1024, 264, 96),
+                                   (1, 0, 64, 8, 8), (2, 1, 2, 16, 520)])
+@pytest.mark.parametrize("variant", [I.FLOAT, I.INTEGER])
+def test_gemm_rs_shapes(handle, shape, variant):
+    W, rank, m, n, k = shape
+    print(f"gemm_rs W={W} rank={rank} m={m} n={n} k={k} variant={variant}", flush=True)
+    d = I.gen_rs(W, m, n, k, rank=rank, variant=variant, config=300 + W)
+    c_own, outbox = run_rs(handle, d, rank)
+    check_rs(d, rank, c_own, outbox, exact=variant == I.INTEGER)
+
+
+@pytest.mark.parametrize("where,out_where", [("host", "hbm"), ("hbm", "host"), ("host", "host")])
+def test_gemm_rs_peers_in_host_memory(handle, where, out_where):
+    d = I.gen_rs(4, 512, 256, 136, rank=1, variant=I.INTEGER, config=310)
+    c_own, outbox = run_rs(handle, d, 1, where=where, out_where=out_where)
+    check_rs(d, 1, c_own, outbox, exact=True)
+
+
+def test_gemm_rs_w_rank_emulation_on_gpu(handle):
+    """Run the GPU op as every rank, feeding each rank the others' outboxes as its
+    peer partials: the concatenated own slices are bf16(sum_r A_r @ B_r)."""
+    W, m, n, k = 4, 512, 256, 64
+    A = [I.draw_bf16(1, 320, r, (m, k), "normal") for r in range(W)]
+    B = [I.draw_bf16(1, 320, 10 + r, (k, n), "normal") for r in range(W)]
+    zero = np.zeros((m // W, n), np.float32)
+    outs = []
+    for r in range(W):
+        d = dict(a=A[r], b=B[r], peers=[None if q == r else zero for q in range(W)])
+        outs.append(run_rs(handle, d, r)[1])
+    slices = []
+    for r in range(W):
+        peers = [None if q == r else O.bf16_to_f64(outs[q][r]).astype(np.float32) for q in range(W)]
+        slices.append(run_rs(handle, dict(a=A[r], b=B[r], peers=peers), r)[0])
+    tot = sum(O.bf16_to_f64(A[r]).astype(np.int64) @ O.bf16_to_f64(B[r]).astype(np.int64)
+              for r in range(W))
+    assert np.abs(tot).max() <= 256          # every partial and sum is exact in bf16
+    O.assert_bits_equal(np.concatenate(slices), O.f64_to_bf16(tot.astype(np.float64)),
+                        "reduce-scatter slices vs the full sum")
+
+
+@pytest.mark.parametrize("variant", [I.FLOAT, I.INTEGER])
+def test_gemm_rs_w8_full_size_sampled(handle, variant):
+    name = "gemm_rs_w8_8192x8192x3584"
+    print(f"{name} variant={variant}", flush=True)
+    d = I.gen_workload(name, variant)
+    c_own, outbox = run_rs(handle, d, 0)
+    W, ms = 8, 1024
+    full = np.concatenate([c_own] + [outbox[q] for q in range(1, W)])
+    assert not np.isnan(O.bf16_to_f64(full)).any(), "unwritten output elements"
+    g = np.random.default_rng(1)
+    rows = np.array(sorted(set([0, 1023, 1024, 8191] + list(g.integers(0, 8192, 40)))))
+    ref = O.gemm_rs_rows(d["a"], d["b"], d["peers"], 0, rows)
+    if variant == I.INTEGER:
+        O.assert_bits_equal(full[rows], ref, "rows (integer inputs)")
+    else:
+        O.assert_close_bf16(full[rows], ref, "rows")
+
+
+# ---------------------------------------------------------------- AllReduce
+
+def run_ar(h, d, rank, n_bcast, where="hbm", out_where="hbm"):
+    W = len(d["peers"])
+    m, k = d["a"].shape
+    n = d["b"].shape[1]
+    a = dev_bf16(d["a"])
+    bt = dev_bf16(I.transpose_bits(d["b"]))
+    peers = [None if p is None else dev_f32(p, where) for p in d["peers"]]
+    c = empty_bf16((m, n))
+    bc = [empty_bf16((m, n), out_where) for _ in range(n_bcast)]
+    h.gemm_ar(a, bt, peers, c, bc, rank=rank)
+    h.sync()
+    return bits(c), [bits(b) for b in bc]
+
+
+@pytest.mark.parametrize("shape", [(4, 0, 256, 512, 128, 3), (3, 1, 300, 200, 72, 2),
+                                   (8, 7, 129, 264, 1024, 7), (1, 0, 8, 8, 8, 0), (2, 0, 520, 136, 40, 1)])
+@pytest.mark.parametrize("variant", [I.FLOAT, I.INTEGER])
+def test_gemm_ar_shapes(handle, shape, variant):
+    W, rank, m, n, k, nb = shape
+    print(f"gemm_ar W={W} rank={rank} m={m} n={n} k={k} n_bcast={nb} variant={variant}", flush=True)
+    d = I.gen_ar(W, m, n, k, rank=rank, variant=variant, config=330 + W)
+    c, bc = run_ar(handle, d, rank, nb)
+    ref = O.gemm_ar(d["a"], d["b"], d["peers"], rank=rank, n_bcast=nb)
+    if variant == I.INTEGER:
+        O.assert_bits_equal(c, ref["c"], "c")
+    else:
+        O.assert_close_bf16(c, ref["c"], "c")
+    for i, b in enumerate(bc):
+        O.assert_bits_equal(b, c, f"bcast[{i}] vs c")
+
+
+def test_gemm_ar_host_memory_peers_and_bcast(handle):
+    d = I.gen_ar(4, 256, 256, 64, rank=2, variant=I.INTEGER, config=340)
+    c, bc = run_ar(handle, d, 2, 3, where="host", out_where="host")
+    O.assert_bits_equal(c, O.gemm_ar(d["a"], d["b"], d["peers"], rank=2)["c"], "c")
+    for b in bc:
+        O.assert_bits_equal(b, c, "bcast vs c")
+
+
+def test_gemm_ar_equals_rs_then_gather(handle):
+    """At small integer shapes AllReduce equals ReduceScatter followed by a gather."""
+    W, m, n, k = 4, 256, 128, 64
+    A = [I.draw_bf16(1, 345, r, (m, k), "normal") for r in range(W)]
+    B = [I.draw_bf16(1, 345, 10 + r, (k, n), "normal") for r in range(W)]
+    P = [O.bf16_to_f64(A[r]) @ O.bf16_to_f64(B[r]) for r in range(W)]
+    for r in (0, 3):
+        d_ar = dict(a=A[r], b=B[r], peers=[None if q == r else P[q].astype(np.float32)
+                                           for q in range(W)])
+        c, _ = run_ar(handle, d_ar, r, 0)
+        slices = []
+        for rr in range(W):
+            ms = m // W
+            d_rs = dict(a=A[rr], b=B[rr], peers=[None if q == rr else
+                                                 P[q][rr * ms:(rr + 1) * ms].astype(np.float32)
+                                                 for q in range(W)])
+            slices.append(run_rs(handle, d_rs, rr)[0])
+        O.assert_bits_equal(c, np.concatenate(slices), f"AR vs RS+gather (rank {r})")
+
+
+@pytest.mark.parametrize("variant", [I.FLOAT, I.INTEGER])
+def test_gemm_ar_w8_full_size_sampled(handle, variant):
+    name = "gemm_ar_w8_2048x8192x1024"
+    print(f"{name} variant={variant}", flush=True)
+    d = I.gen_workload(name, variant)
+    c, bc = run_ar(handle, d, 0, 7)
+    assert not np.isnan(O.bf16_to_f64(c)).any(), "unwritten output elements"
+    for i, b in enumerate(bc):
+        O.assert_bits_equal(b, c, f"bcast[{i}] vs c")
+    g = np.random.default_rng(2)
+    rows = np.array(sorted(set([0, 2047] + list(g.integers(0, 2048, 40)))))
+    ref = O.gemm_ar_rows(d["a"], d["b"], d["peers"], 0, rows)
+    if variant == I.INTEGER:
+        O.assert_bits_equal(c[rows], ref, "rows (integer inputs)")
+    else:
+        O.assert_close_bf16(c[rows], ref, "rows")

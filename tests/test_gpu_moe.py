@@ -1,0 +1,136 @@
+"""GPU parity of MoE dispatch + grouped GEMM against the CPU oracle.
+
+Routing (top-k ids), the slot permutation (slot_token), expert and chunk
+offsets and the landed rows are compared bit for bit; gates to 1e-5 relative
+(fp32 softmax against the float64 oracle); expert outputs with the float
+tolerance, and bit for bit when the gate is not applied on integer inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from communication_gemm_persistent_amd import inputs as I
+from tests.gpu_util import bits, dev_bf16, dev_f32, empty_bf16, np_i32
+
+pytestmark = pytest.mark.gpu
+
+GATE_RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def handle(mk):
+    h = mk.Handle(0, spin_timeout_ms=10000)
+    yield h
+    h.close()
+
+
+def run_moe(h, d, E, top_k, rank=0, where="hbm", flags=0):
+    S = len(d["x"])
+    T, H = d["x"][0].shape
+    E_loc, _, N = d["w"].shape
+    cap = S * T * min(top_k, E_loc)
+    x = [dev_bf16(xx, "hbm" if s == rank else where) for s, xx in enumerate(d["x"])]
+    lg = [dev_f32(l, "hbm" if s == rank else where) for s, l in enumerate(d["logits"])]
+    wt = dev_bf16(I.transpose_bits(d["w"]))
+    y = empty_bf16((cap, N))
+    idx = torch.full((S * T, top_k), -7, dtype=torch.int32, device="cuda")
+    gate = torch.zeros((S * T, top_k), dtype=torch.float32, device="cuda")
+    slot_token = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    eoff = torch.full((E_loc + 1,), -7, dtype=torch.int32, device="cuda")
+    coff = torch.full((E_loc, S + 1), -7, dtype=torch.int32, device="cuda")
+    xs = empty_bf16((cap, H))
+    h.moe_dispatch_gemm(x, lg, wt, E, top_k, y, idx, gate, slot_token, eoff, coff, xs,
+                        rank=rank, flags=flags)
+    h.sync()
+    return dict(y=bits(y), idx=np_i32(idx), gate=np_i32(gate), slot_token=np_i32(slot_token),
+                expert_offsets=np_i32(eoff), chunk_offsets=np_i32(coff), x_slots=bits(xs))
+
+
+def check_moe(d, out, top_k, rank, variant, no_gate=False, slots=None):
+    ref = O.moe_dispatch_gemm(d["x"], d["logits"], d["w"], top_k=top_k, rank=rank,
+                              apply_gate=not no_gate, slots=slots)
+    n = ref["n_slots"]
+    O.assert_bits_equal(out["idx"], ref["idx"], "topk_idx")
+    g_ref = ref["gate"]
+    bad = np.abs(out["gate"] - g_ref) > GATE_RTOL * np.abs(g_ref)
+    assert not bad.any(), f"topk_gate: {bad.sum()} outside 1e-5 relative"
+    O.assert_bits_equal(out["expert_offsets"], ref["expert_offsets"], "expert_offsets")
+    O.assert_bits_equal(out["chunk_offsets"], ref["chunk_offsets"], "chunk_offsets")
+    O.assert_bits_equal(out["slot_token"][:n], ref["slot_token"], "slot_token")
+    sel = np.arange(n) if slots is None else np.asarray(slots)
+    O.assert_bits_equal(out["x_slots"][sel], ref["x_slots"][sel], "x_slots")
+    y = out["y"][sel]
+    if no_gate and variant == I.INTEGER:
+        O.assert_bits_equal(y, ref["y"], "y (integer inputs, no gate)")
+    else:
+        O.assert_close_bf16(y, ref["y"], "y")
+    return ref
+
+
+SMALL = [  # S, T, H, N, E, E_loc, top_k, rank
+    (3, 300, 264, 136, 16, 4, 2, 1),
+    (2, 256, 64, 64, 8, 8, 2, 0),
+    (4, 100, 128, 264, 32, 2, 1, 3),
+    (2, 513, 72, 80, 12, 3, 3, 2),
+    (1, 40, 32, 16, 4, 1, 4, 0),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL)
+@pytest.mark.parametrize("variant", [I.FLOAT, I.INTEGER])
+def test_moe_small(handle, cfg, variant):
+    S, T, H, N, E, E_loc, top_k, rank = cfg
+    print(f"moe S={S} T={T} H={H} N={N} E={E} E_loc={E_loc} top_k={top_k} rank={rank} "
+          f"variant={variant}", flush=True)
+    d = I.gen_moe(S, T, H, N, E, E_loc, variant, config=400 + S)
+    out = run_moe(handle, d, E, top_k, rank=rank)
+    check_moe(d, out, top_k, rank, variant)
+
+
+@pytest.mark.parametrize("cfg", SMALL[:3])
+def test_moe_no_gate_integer_bit_exact(handle, mk, cfg):
+    S, T, H, N, E, E_loc, top_k, rank = cfg
+    d = I.gen_moe(S, T, H, N, E, E_loc, I.INTEGER, config=410 + S)
+    out = run_moe(handle, d, E, top_k, rank=rank, flags=mk.F_NO_GATE)
+    check_moe(d, out, top_k, rank, I.INTEGER, no_gate=True)
+
+
+def test_moe_ties_and_peers_in_host_memory(handle):
+    S, T, H, N, E, E_loc, top_k = 3, 200, 64, 64, 16, 4, 2
+    d = I.gen_moe(S, T, H, N, E, E_loc, I.FLOAT, config=420)
+    for s in range(S):                      # forced ties at the top and among local experts
+        lg = d["logits"][s]
+        lg[::3, 1] = lg[::3, 2] = lg[::3].max(axis=1) + 1.0
+        lg[1::5, :] = 0.5
+    out = run_moe(handle, d, E, top_k, rank=0, where="host")
+    check_moe(d, out, top_k, 0, I.FLOAT)
+
+
+def test_moe_no_local_tokens(handle):
+    """Degenerate case: no token picks a local expert -> zero slots, no tiles."""
+    S, T, H, N, E, E_loc, top_k = 2, 64, 32, 32, 8, 2, 1
+    d = I.gen_moe(S, T, H, N, E, E_loc, I.FLOAT, config=430)
+    for s in range(S):
+        d["logits"][s][:, :E_loc] = -50.0
+    out = run_moe(handle, d, E, top_k, rank=0)
+    assert out["expert_offsets"].tolist() == [0] * (E_loc + 1)
+    check_moe(d, out, top_k, 0, I.FLOAT)
+
+
+@pytest.mark.parametrize("variant", [I.FLOAT, I.INTEGER])
+def test_moe_full_size(handle, variant):
+    name = "moe_s8_t4096_h4096_n1536_e64"
+    p = I.CONFIGS[name].params
+    print(f"{name} variant={variant}", flush=True)
+    d = I.gen_workload(name, variant)
+    out = run_moe(handle, d, p["E"], p["top_k"], rank=0)
+    n = int(out["expert_offsets"][-1])
+    g = np.random.default_rng(3)
+    eo = out["expert_offsets"]
+    slots = sorted(set([0, n - 1] + [int(v) for v in eo[:-1]] + [int(v) - 1 for v in eo[1:]]
+                       + list(g.integers(0, n, 48))))
+    check_moe(d, out, p["top_k"], 0, variant, slots=np.array(slots))
+    # every landed row is the token row its slot names
+    x_all = np.concatenate(d["x"])
+    O.assert_bits_equal(out["x_slots"][:n], x_all[out["slot_token"][:n]], "x_slots (all rows)")

@@ -1,0 +1,115 @@
+"""GPU tests of the launch protocol: bounded waits, error reporting, argument
+validation and role control.
+
+Failure handling is forced from the host: a handle with a tiny spin limit and
+no land workgroups leaves the ready flags unset, so every wait expires by its
+own bound and the launch completes normally with MK_ERR_TIMEOUT recorded.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from communication_gemm_persistent_amd import inputs as I
+from tests.gpu_util import bits, dev_bf16, empty_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _ag_buffers(d, rank=0):
+    W = len(d["shards"])
+    m_s, k = d["shards"][0].shape
+    n = d["b"].shape[1]
+    shards = [dev_bf16(s) for s in d["shards"]]
+    bt = dev_bf16(I.transpose_bits(d["b"]))
+    return shards, bt, empty_bf16((W * m_s, n)), empty_bf16((W * m_s, k))
+
+
+def test_withheld_chunks_time_out_and_handle_recovers(mk):
+    d = I.gen_ag(4, 256, 256, 128, I.INTEGER, config=500)
+    shards, bt, c, ag = _ag_buffers(d)
+    with mk.Handle(0, spin_timeout_ms=50) as h:
+        h.set_roles(mk.OP_AG_GEMM, n_land=0)          # nobody lands the peers' chunks
+        h.ag_gemm(shards, bt, c, ag, rank=0)
+        with pytest.raises(mk.MkError) as ei:
+            h.sync()
+        assert ei.value.status == mk.MK_ERR_TIMEOUT
+        h.sync()                                      # the error record was cleared
+        h.set_roles(mk.OP_AG_GEMM)                    # defaults again
+        h.ag_gemm(shards, bt, c, ag, rank=0)
+        h.sync()
+        O.assert_bits_equal(bits(c), O.ag_gemm(d["shards"], d["b"])["c"], "after recovery")
+
+
+def test_invalid_arguments_launch_nothing(mk):
+    d = I.gen_ag(2, 64, 64, 64, I.FLOAT, config=501)
+    shards, bt, c, ag = _ag_buffers(d)
+    with mk.Handle(0) as h:
+        lib = h.lib
+
+        def call(**kw):
+            a = dict(world=2, rank=0, m_s=64, n=64, k=64, flags=0,
+                     shards=[s.data_ptr() for s in shards], bt=bt.data_ptr(), c=c.data_ptr(),
+                     ag=ag.data_ptr())
+            a.update(kw)
+            arr = (ctypes.c_void_p * len(a["shards"]))(*a["shards"])
+            return lib.mk_ag_gemm(h.h, None, a["world"], a["rank"], arr, a["bt"], a["c"], a["ag"],
+                                  a["m_s"], a["n"], a["k"], a["flags"])
+
+        assert call() == mk.MK_OK
+        h.sync()
+        assert call(k=60) == mk.MK_ERR_INVALID            # K not a multiple of 8
+        assert call(n=12) == mk.MK_ERR_INVALID            # N not a multiple of 8
+        assert call(world=17) == mk.MK_ERR_INVALID
+        assert call(rank=2) == mk.MK_ERR_INVALID
+        assert call(flags=0x80) == mk.MK_ERR_INVALID
+        assert call(bt=bt.data_ptr() + 2) == mk.MK_ERR_INVALID   # misaligned
+        pageable = np.zeros(64 * 64, np.uint16)
+        assert call(shards=[shards[0].data_ptr(), pageable.ctypes.data]) == mk.MK_ERR_INVALID
+        assert call(ag=0) == mk.MK_ERR_INVALID
+        assert b"a_gathered" in lib.mk_last_error(h.h)
+
+
+def test_roles_query_and_transfer_only_launch(mk):
+    d = I.gen_ag(4, 256, 256, 128, I.FLOAT, config=502)
+    shards, bt, c, ag = _ag_buffers(d)
+    with mk.Handle(0) as h:
+        assert h.get_roles(mk.OP_AG_GEMM) == (-1, -1, -1)
+        h.set_roles(mk.OP_AG_GEMM, n_land=6, n_compute=0)   # transfer alone
+        h.ag_gemm(shards, bt, c, ag, rank=0)
+        h.sync()
+        roles, grid = h.last_launch(mk.OP_AG_GEMM)
+        assert roles == (6, 0, 0) and grid == 6
+        O.assert_bits_equal(bits(ag), O.all_gather(d["shards"]), "a_gathered with no compute")
+        h.set_roles(mk.OP_AG_GEMM, n_land=3, n_compute=9)
+        h.ag_gemm(shards, bt, c, ag, rank=0)
+        h.sync()
+        assert h.last_launch(mk.OP_AG_GEMM) == ((3, 9, 0), 12)
+
+
+def test_moe_keeps_at_least_one_land_workgroup(mk):
+    S, T, H, N, E, E_loc, top_k = 2, 64, 32, 32, 8, 2, 2
+    d = I.gen_moe(S, T, H, N, E, E_loc, I.FLOAT, config=503)
+    from tests.test_gpu_moe import check_moe, run_moe
+    with mk.Handle(0, spin_timeout_ms=5000) as h:
+        h.set_roles(mk.OP_MOE, n_land=0, n_compute=3)
+        out = run_moe(h, d, E, top_k)
+        assert h.last_launch(mk.OP_MOE)[0][:2] == (1, 3)
+        check_moe(d, out, top_k, 0, I.FLOAT)
+
+
+def test_two_handles_interleaved_on_one_stream(mk):
+    d = I.gen_ag(3, 128, 128, 64, I.INTEGER, config=504)
+    shards, bt, c1, ag1 = _ag_buffers(d)
+    _, _, c2, ag2 = _ag_buffers(d)
+    ref = O.ag_gemm(d["shards"], d["b"])["c"]
+    with mk.Handle(0) as h1, mk.Handle(0) as h2:
+        for _ in range(5):
+            h1.ag_gemm(shards, bt, c1, ag1, rank=0)
+            h2.ag_gemm(shards, bt, c2, ag2, rank=0)
+        h1.sync()
+        h2.sync()
+    O.assert_bits_equal(bits(c1), ref, "handle 1")
+    O.assert_bits_equal(bits(c2), ref, "handle 2")
