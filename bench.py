@@ -74,6 +74,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--profile-run", choices=["fused", "gemm_alone", "transfer_alone", "copy"],
+                    help="only launch the named kernel a few times (for rocprofv3 counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share; peers are emulated by buffers. "
@@ -97,6 +99,9 @@ def main() -> int:
     def to_dev_f32(x, where="hbm"):
         t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
         return t.pin_memory() if where == "host" else t.to(dev)
+
+    if args.profile_run:
+        return profile_run(args.profile_run, h, I, mk, to_dev, dev)
 
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
@@ -240,6 +245,44 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(I, flops)
     h.close()
     print(json.dumps(result), flush=True)
+    return 0
+
+
+COPY_BYTES = 256 << 20
+
+
+def profile_run(which, h, I, mk, to_dev, dev):
+    """Launch one kernel kind 5 times (after 2 warm-ups) and exit: the program
+    that rocprofv3 wraps for counter passes.  "copy" is a plain device copy of
+    COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    if which == "copy":
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(7):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": which, "bytes": COPY_BYTES}))
+        return 0
+    wl = I.CONFIGS[WORKLOAD]
+    p = wl.params
+    W, m_s, n, k = p["world"], p["m_s"], p["n"], p["k"]
+    d = I.gen_workload(WORKLOAD)
+    shards = [to_dev(s) for s in d["shards"]]
+    bt = to_dev(I.transpose_bits(d["b"]))
+    c = torch.empty((W * m_s, n), dtype=torch.bfloat16, device=dev)
+    ag = torch.empty((W * m_s, k), dtype=torch.bfloat16, device=dev)
+    flags = 0
+    if which == "gemm_alone":
+        h.ag_gemm(shards, bt, c, ag, rank=0)      # gathers A once
+        flags = mk.F_PRELANDED
+    if which == "transfer_alone":
+        h.set_roles(mk.OP_AG_GEMM, n_land=32, n_compute=0)
+    for _ in range(7):
+        h.ag_gemm(shards, bt, c, ag, rank=0, flags=flags)
+    h.sync()
+    print(json.dumps({"profile_run": which, "workload": WORKLOAD,
+                      "roles": h.last_launch(mk.OP_AG_GEMM)}))
     return 0
 
 

@@ -24,7 +24,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kThreads = 256;     // 4 waves of 64 lanes
+constexpr int kMaxWaves = 8;      // workgroups have up to 8 waves of 64 lanes
 constexpr int kBK = 64;           // K elements per pipeline stage (128 bytes of bf16 per row)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset that always fails the range check -> 0
 constexpr int kFlagStride = 16;   // uint32 words between flags (64 bytes)
@@ -139,14 +139,24 @@ __device__ __forceinline__ bool spin_until_ge(const Sync &s, const uint32_t *p, 
 }
 
 // Arrival of one work item of flag `f`, which completes after `target` items.
-// Called by one thread after the whole workgroup's stores are fenced and
-// barriered.  The last arrival resets the counter and publishes the flag.
+// Called by one thread after every thread of the workgroup has waited for
+// its own stores (wait_stores) and the workgroup has passed a barrier: the
+// release fence writes this XCD's L2 back, so the item's data is in memory
+// before the count moves.  The last arrival acquires the other arrivals'
+// releases, resets the counter and publishes the flag.
 __device__ __forceinline__ void arrive(const Sync &s, uint32_t f, uint32_t target) {
-  uint32_t old = add_acq_rel(cnt_ptr(s, f), 1u);
+  fence_release();
+  const uint32_t old = add_relaxed(cnt_ptr(s, f), 1u);
   if (old + 1 == target) {
+    fence_acquire();
     st_relaxed(cnt_ptr(s, f), 0u);
     st_release(flag_ptr(s, f), s.epoch);
   }
+}
+
+// Wait for this thread's outstanding global stores (and loads).
+__device__ __forceinline__ void wait_stores() {
+  __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0)
 }
 
 // Values that thread 0 broadcasts through LDS are identical in every lane,
@@ -205,12 +215,29 @@ __device__ __forceinline__ void finish_launch(const Sync &s) {
 
 // Broadcast a wait result from thread 0 to the workgroup; on success every
 // thread's later loads observe the data published before the flag.
-__device__ __forceinline__ bool wg_sync_ok(bool ok_thread0, uint32_t *lds_word) {
+//
+// heavy_acquire = false skips the agent-scope acquire (an invalidate of this
+// XCD's whole L2) and is used only for data that no workgroup of this launch
+// can have cached before it was published: a landing buffer whose land
+// blocks start and end on 128-byte cache-line boundaries and which is only
+// read after its flags are seen.  Each launch starts with the caches
+// invalidated, so no line of such a block can be in any L1/L2 before the
+// block lands, and the writer's release already wrote it back to memory.
+__device__ __forceinline__ bool wg_sync_ok(bool ok_thread0, uint32_t *lds_word,
+                                           bool heavy_acquire = true) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    if (ok_thread0) fence_acquire();
+    if (ok_thread0 && heavy_acquire) fence_acquire();
     *lds_word = ok_thread0 ? 1u : 0u;
   }
+  __syncthreads();
+  return uniform(*lds_word) != 0;
+}
+
+// Broadcast a flag value of thread 0 without any memory ordering.
+__device__ __forceinline__ bool wg_broadcast(bool v_thread0, uint32_t *lds_word) {
+  __syncthreads();
+  if (threadIdx.x == 0) *lds_word = v_thread0 ? 1u : 0u;
   __syncthreads();
   return uniform(*lds_word) != 0;
 }
@@ -229,16 +256,17 @@ __device__ __forceinline__ void wg_copy16(void *__restrict__ dst, const void *__
   const u32x4_t *s = reinterpret_cast<const u32x4_t *>(src);
   u32x4_t *d = reinterpret_cast<u32x4_t *>(dst);
   const size_t n = bytes >> 4;
+  const size_t nt = blockDim.x;
   constexpr int U = 8;
   size_t i = threadIdx.x;
-  for (; i + (size_t)(U - 1) * kThreads < n; i += (size_t)U * kThreads) {
+  for (; i + (size_t)(U - 1) * nt < n; i += (size_t)U * nt) {
     u32x4_t v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&s[i + (size_t)u * kThreads]);
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&s[i + (size_t)u * nt]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) d[i + (size_t)u * kThreads] = v[u];
+    for (int u = 0; u < U; ++u) d[i + (size_t)u * nt] = v[u];
   }
-  for (; i < n; i += kThreads) d[i] = __builtin_nontemporal_load(&s[i]);
+  for (; i < n; i += nt) d[i] = __builtin_nontemporal_load(&s[i]);
 }
 
 // ---------------------------------------------------------------- GEMM tile engine
@@ -252,24 +280,36 @@ __device__ __forceinline__ void wg_copy16(void *__restrict__ dst, const void *__
 // which the epilogues store as 8-byte bf16 / 16-byte fp32 vectors.
 //
 // LDS layout of one operand stage: row r occupies 128 bytes (64 bf16 of K);
-// its eight 16-byte chunks are stored at position p = c ^ (r & 7) for logical
-// chunk c, so the 32 rows read by one MFMA fragment load hit distinct banks.
-// Stages are filled by buffer_load ... lds (16 bytes per lane, the lane's
-// destination fixed at base + 16*lane); the swizzle is realised by choosing
-// which global chunk each lane fetches.  Rows past the matrix or chunks past
-// K use an out-of-range offset and read as zero.
+// its eight 16-byte chunks are stored at position p = c ^ ((r >> 1) & 7) for
+// logical chunk c.  A fragment read serves 16 lanes (16 rows, 256 bytes) per
+// LDS cycle; with a 128-byte row pitch, rows r and r+1 already fall in
+// different halves of the 64 banks, and the (r >> 1) swizzle spreads the 8
+// even (and the 8 odd) rows over distinct 16-byte bank groups, so the 16
+// reads hit 16 distinct groups.  Stages are filled by buffer_load ... lds
+// (16 bytes per lane, the lane's destination fixed at base + 16*lane); the
+// swizzle is realised by choosing which global chunk each lane fetches.  Rows
+// past the matrix or chunks past K use an out-of-range offset and read as
+// zero.
 
 template <int BM, int BN>
 struct TileCfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  // 256x256 tiles run 8 waves (2 per SIMD, a 2 x 4 grid of 128x64 blocks)
+  // so one wave's LDS-read waits are covered by the other wave's MFMAs;
+  // smaller tiles run 4 waves in a 2 x 2 grid.
+  static constexpr int WAVES_M = 2;
+  static constexpr int WAVES_N = (BM >= 256 && BN >= 256) ? 4 : 2;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  static constexpr int LOADS_A = BM / 32;  // buffer loads per wave per stage
-  static constexpr int LOADS_B = BN / 32;
+  static constexpr int LOADS_A = BM / (8 * WAVES);  // buffer loads per wave per stage
+  static constexpr int LOADS_B = BN / (8 * WAVES);
   static constexpr int LOADS = LOADS_A + LOADS_B;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile must split into 2x2 waves of 32x32 blocks");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave blocks are built from 32x32 MFMAs");
+  static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "stage rows split over waves");
 };
 
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
@@ -301,17 +341,17 @@ __device__ __forceinline__ void dma16(i32x4_t vdesc, uint32_t m0_base, uint32_t 
                : "memory");
 }
 
-template <int ROWS>
+template <int ROWS, int WAVES>
 __device__ __forceinline__ void stage_operand(i32x4_t vdesc, uint32_t lds, int ld_bytes, int k0,
                                               int K, int wave, int lane) {
-  constexpr int PER_WAVE = ROWS / 32;
+  constexpr int PER_WAVE = ROWS / (8 * WAVES);
   const int rsub = lane >> 3;
-  const int c = (lane & 7) ^ rsub;
-  const int kk = k0 + c * 8;
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int j = wave * PER_WAVE + i;        // 8-row group filled by this instruction
     const int row = j * 8 + rsub;
+    const int c = (lane & 7) ^ ((row >> 1) & 7);  // logical chunk stored at this lane's slot
+    const int kk = k0 + c * 8;
     const uint32_t off = (kk < K) ? (uint32_t)(row * ld_bytes + kk * 2) : kOOB;
     dma16(vdesc, __builtin_amdgcn_readfirstlane(lds + j * 1024), off);
   }
@@ -335,35 +375,70 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// One K-substep (16 elements) of fragments for a wave: FM A rows-blocks and
+// FN B^T row-blocks, one 16-byte LDS read each.
 template <int BM, int BN>
-__device__ __forceinline__ void mma_stage(const char *ldsA, const char *ldsB,
-                                          f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN],
-                                          int wm, int wn, int lane) {
+struct Frags {
+  bf16x8_t a[TileCfg<BM, BN>::FM];
+  bf16x8_t b[TileCfg<BM, BN>::FN];
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void load_frags(Frags<BM, BN> &f, const char *stage, int ks, int wm,
+                                           int wn, int lane) {
   using C = TileCfg<BM, BN>;
   const int r32 = lane & 31;
-  const int sw = lane & 7;
+  const int c = ks * 2 + (lane >> 5);
+  const int coff = ((c ^ ((lane >> 1) & 7)) << 4);
+  const char *pa = stage + (wm * C::WM + r32) * 128 + coff;
+  const char *pb = stage + C::A_BYTES + (wn * C::WN + r32) * 128 + coff;
+  // issue order = first use in mma_frags (i outer, j inner): a[0] and every
+  // b[j] are needed by the first FN MFMAs, a[i] only at MFMA i*FN
+  f.a[0] = *reinterpret_cast<const bf16x8_t *>(pa);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int c = ks * 2 + (lane >> 5);
-    const int coff = ((c ^ sw) << 4);
-    bf16x8_t a[C::FM], b[C::FN];
+  for (int j = 0; j < C::FN; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t *>(pb + j * 32 * 128);
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_t *>(ldsA + (wm * C::WM + i * 32 + r32) * 128 + coff);
+  for (int i = 1; i < C::FM; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t *>(pa + i * 32 * 128);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void mma_frags(const Frags<BM, BN> &f,
+                                          f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN]) {
+  using C = TileCfg<BM, BN>;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
-      b[j] = *reinterpret_cast<const bf16x8_t *>(ldsB + (wn * C::WN + j * 32 + r32) * 128 + coff);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
+
+// Interleave the next substep's LDS reads with this substep's MFMAs: one
+// read, then MFMAs, repeated, so the reads' latency hides under the MFMAs.
+template <int BM, int BN>
+__device__ __forceinline__ void interleave_reads_and_mfmas() {
+  using C = TileCfg<BM, BN>;
+  constexpr int R = C::FM + C::FN, M = C::FM * C::FN;
+  constexpr int per = M / R > 0 ? M / R : 1;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  for (int r = 0; r < R; ++r) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, per, 0); // MFMAs
   }
+  __builtin_amdgcn_sched_group_barrier(0x008, M - per * R > 0 ? M - per * R : 0, 0);
 }
 
 // Run the K loop of one tile.  va covers rows [m0, m0 + valid_m) of A with
 // row pitch lda_bytes; vb rows [n0, n0 + valid_n) of Bt.  smem holds two
 // stages.  On return the accumulators hold the tile and smem is free.
+//
+// Pipeline (per 64-wide K stage kb, 4 substeps of 16):
+//   substeps 0..2: read the next substep's fragments, MFMAs of this one
+//   then: wait for this wave's DMA of stage kb+1, barrier (every wave's DMA
+//   landed; every wave's reads of stage kb done), start the DMA of stage
+//   kb+2 into stage kb's buffer, read stage kb+1's first fragments, MFMAs of
+//   substep 3.
+// The fragment stream never drains and each DMA has a full stage of MFMAs
+// to land.
 template <int BM, int BN>
 __device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes, i32x4_t vb,
                                           int ldb_bytes, int K,
@@ -371,7 +446,7 @@ __device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes,
   using C = TileCfg<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -379,21 +454,44 @@ __device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes,
 
   const uint32_t base = lds_addr(smem);
   const int nk = (K + kBK - 1) / kBK;
-  stage_operand<BM>(va, base, lda_bytes, 0, K, wave, lane);
-  stage_operand<BN>(vb, base + C::A_BYTES, ldb_bytes, 0, K, wave, lane);
-  for (int kb = 0; kb < nk; ++kb) {
-    // This wave's loads of stage kb are done; after the barrier every wave's
-    // are, and every wave has finished reading the other stage's buffer,
-    // which the prefetch of stage kb+1 overwrites.
+  stage_operand<BM, C::WAVES>(va, base, lda_bytes, 0, K, wave, lane);
+  stage_operand<BN, C::WAVES>(vb, base + C::A_BYTES, ldb_bytes, 0, K, wave, lane);
+  if (nk > 1) {
+    stage_operand<BM, C::WAVES>(va, base + C::STAGE_BYTES, lda_bytes, kBK, K, wave, lane);
+    stage_operand<BN, C::WAVES>(vb, base + C::STAGE_BYTES + C::A_BYTES, ldb_bytes, kBK, K, wave, lane);
+    wait_vmcnt<C::LOADS>();
+  } else {
     wait_vmcnt<0>();
+  }
+  wg_barrier();
+  // f0 / f1 alternate so no fragment set is ever copied; at the loop head f0
+  // holds substep 0 of stage kb.  The last stage's final read of the other
+  // buffer is harmless (its data is not used).
+  Frags<BM, BN> f0, f1;
+  load_frags<BM, BN>(f0, smem, 0, wm, wn, lane);
+  for (int kb = 0; kb < nk; ++kb) {
+    const char *st = smem + (kb & 1) * C::STAGE_BYTES;
+    load_frags<BM, BN>(f1, st, 1, wm, wn, lane);
+    mma_frags<BM, BN>(f0, acc);
+    interleave_reads_and_mfmas<BM, BN>();
+    load_frags<BM, BN>(f0, st, 2, wm, wn, lane);
+    mma_frags<BM, BN>(f1, acc);
+    interleave_reads_and_mfmas<BM, BN>();
+    load_frags<BM, BN>(f1, st, 3, wm, wn, lane);
+    mma_frags<BM, BN>(f0, acc);
+    interleave_reads_and_mfmas<BM, BN>();
+    // every LDS read of stage kb has returned (substep 3's fragments are in
+    // registers) and this wave's DMA of stage kb+1 has landed
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (0 << 8));  // vmcnt(0) lgkmcnt(0)
     wg_barrier();
-    if (kb + 1 < nk) {
-      const uint32_t nxt = base + ((kb + 1) & 1) * C::STAGE_BYTES;
-      stage_operand<BM>(va, nxt, lda_bytes, (kb + 1) * kBK, K, wave, lane);
-      stage_operand<BN>(vb, nxt + C::A_BYTES, ldb_bytes, (kb + 1) * kBK, K, wave, lane);
+    if (kb + 2 < nk) {
+      const uint32_t dst = base + (kb & 1) * C::STAGE_BYTES;
+      stage_operand<BM, C::WAVES>(va, dst, lda_bytes, (kb + 2) * kBK, K, wave, lane);
+      stage_operand<BN, C::WAVES>(vb, dst + C::A_BYTES, ldb_bytes, (kb + 2) * kBK, K, wave, lane);
     }
-    const char *cur = smem + (kb & 1) * C::STAGE_BYTES;
-    mma_stage<BM, BN>(cur, cur + C::A_BYTES, acc, wm, wn, lane);
+    load_frags<BM, BN>(f0, smem + ((kb + 1) & 1) * C::STAGE_BYTES, 0, wm, wn, lane);
+    mma_frags<BM, BN>(f1, acc);
+    interleave_reads_and_mfmas<BM, BN>();
   }
   wg_barrier();  // every wave is done reading; the caller may refill either stage
 }
@@ -410,7 +508,7 @@ __device__ __forceinline__ AccPos<BM, BN> acc_pos(int i, int j, int g) {
   using C = TileCfg<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   AccPos<BM, BN> p;
   p.row = wm * C::WM + i * 32 + (lane & 31);
   p.col = wn * C::WN + j * 32 + g * 8 + (lane >> 5) * 4;

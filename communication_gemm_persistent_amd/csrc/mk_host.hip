@@ -324,7 +324,7 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
                      mk_bf16 *a_gathered, int m_s, int n, int k, unsigned flags) {
   mk_status st = check_common(h, world, rank);
   if (st != MK_OK) return st;
-  if (flags & ~MK_F_PRELANDED) return fail(h, MK_ERR_INVALID, "unknown flag bits");
+  if (flags & ~(MK_F_PRELANDED | MK_F_STATIC_ROLES)) return fail(h, MK_ERR_INVALID, "unknown flag bits");
   if (!a_shards) return fail(h, MK_ERR_INVALID, "a_shards is NULL");
   if (m_s < 1) return fail(h, MK_ERR_INVALID, "m_s < 1");
   st = check_gemm_shape(h, (long)world * m_s, n, k);
@@ -375,6 +375,13 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   if (pre) land = 0;
   p.n_land = land;
   p.n_compute = compute;
+  const bool dynamic = (flags & MK_F_STATIC_ROLES) == 0;
+  p.land_joins_compute = (dynamic && compute > 0) ? 1 : 0;
+  p.help_land = (dynamic && !pre) ? 1 : 0;
+  // land blocks on 128-byte boundaries of a_gathered allow the light acquire
+  const bool aligned = (reinterpret_cast<uintptr_t>(p.ag) % 128 == 0) &&
+                       ((size_t)p.lb_rows * k * 2) % 128 == 0 && ((size_t)m_s * k * 2) % 128 == 0;
+  p.light_acquire = aligned ? 1 : 0;
   const int grid = std::max(1, land + compute);
   p.sync = make_sync(h, (uint32_t)(world * p.blocks_per_chunk));
   hipError_t e = mk::launch_ag(p, bm, grid, reinterpret_cast<hipStream_t>(stream));

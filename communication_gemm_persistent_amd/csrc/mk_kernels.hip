@@ -18,26 +18,45 @@ namespace mk {
 
 // ---------------------------------------------------------------- AllGather + GEMM
 
-__device__ __forceinline__ void ag_land(const AgParams &p, uint32_t *s_word) {
+// Land item `it`: landing order is peers rank+1, rank+2, ... then the local
+// shard last.  Every thread copies its share, waits for its stores, and
+// thread 0 records the arrival after the barrier.
+__device__ __forceinline__ void ag_land_item(const AgParams &p, uint32_t it) {
   const size_t row_bytes = (size_t)p.k * 2;
   const uint32_t per_chunk = (uint32_t)(p.blocks_per_chunk * p.items_per_block);
+  const int pos = (int)(it / per_chunk);
+  const uint32_t rem = it % per_chunk;
+  const int j = (int)(rem / p.items_per_block), ii = (int)(rem % p.items_per_block);
+  const int q = (p.rank + 1 + pos) % p.world;
+  const int r0 = j * p.lb_rows + ii * p.item_rows;
+  const int r1 = min(r0 + p.item_rows, min((j + 1) * p.lb_rows, p.m_s));
+  if (r1 > r0)
+    wg_copy16(p.ag + ((size_t)q * p.m_s + r0) * p.k, p.shard[q] + (size_t)r0 * p.k,
+              (size_t)(r1 - r0) * row_bytes);
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) arrive(p.sync, (uint32_t)(q * p.blocks_per_chunk + j), (uint32_t)p.items_per_block);
+}
+
+__device__ __forceinline__ void ag_land(const AgParams &p, uint32_t *s_word) {
   for (;;) {
     const uint32_t it = next_index(&p.sync.ctrl->land_ctr, s_word);
     if (it >= (uint32_t)p.n_items) break;
-    // landing order: peers rank+1, rank+2, ... then the local shard last
-    const int pos = (int)(it / per_chunk);
-    const uint32_t rem = it % per_chunk;
-    const int j = (int)(rem / p.items_per_block), ii = (int)(rem % p.items_per_block);
-    const int q = (p.rank + 1 + pos) % p.world;
-    const int r0 = j * p.lb_rows + ii * p.item_rows;
-    const int r1 = min(r0 + p.item_rows, min((j + 1) * p.lb_rows, p.m_s));
-    if (r1 > r0)
-      wg_copy16(p.ag + ((size_t)q * p.m_s + r0) * p.k, p.shard[q] + (size_t)r0 * p.k,
-                (size_t)(r1 - r0) * row_bytes);
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) arrive(p.sync, (uint32_t)(q * p.blocks_per_chunk + j), (uint32_t)p.items_per_block);
+    ag_land_item(p, it);
   }
+}
+
+// Thread 0: are all land blocks overlapping gathered rows [m0, m1) ready?
+__device__ __forceinline__ bool ag_rows_ready(const AgParams &p, int m0, int m1) {
+  int r = m0;
+  while (r < m1) {
+    const int q = r / p.m_s, lr = r - q * p.m_s;
+    const int j = lr / p.lb_rows;
+    if (ld_relaxed(flag_ptr(p.sync, (uint32_t)(q * p.blocks_per_chunk + j))) != p.sync.epoch)
+      return false;
+    r = q * p.m_s + min((j + 1) * p.lb_rows, p.m_s);
+  }
+  return true;
 }
 
 // Thread 0: wait for every land block overlapping gathered rows [m0, m1).
@@ -52,6 +71,25 @@ __device__ __forceinline__ bool ag_wait_rows(const AgParams &p, int m0, int m1) 
     r = q * p.m_s + min((j + 1) * p.lb_rows, p.m_s);
   }
   return true;
+}
+
+// Make gathered rows [m0, m1) available to the workgroup.  While they are
+// missing, the workgroup lands the next unlanded items itself (landing order
+// matches tile order, so these are the rows needed soonest); once nothing is
+// left to land it waits.  Returns false on timeout / abort.
+__device__ __forceinline__ bool ag_acquire_rows(const AgParams &p, int m0, int m1, uint32_t *s_word) {
+  for (;;) {
+    bool ready = false;
+    if (threadIdx.x == 0) ready = ag_rows_ready(p, m0, m1);
+    if (wg_broadcast(ready, s_word)) break;
+    if (!p.help_land) break;
+    const uint32_t it = next_index(&p.sync.ctrl->land_ctr, s_word);
+    if (it >= (uint32_t)p.n_items) break;
+    ag_land_item(p, it);
+  }
+  bool ok0 = true;
+  if (threadIdx.x == 0) ok0 = ag_wait_rows(p, m0, m1);
+  return wg_sync_ok(ok0, s_word, !p.light_acquire);
 }
 
 template <int BM, int BN>
@@ -72,11 +110,7 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
       abase = p.shard[p.rank] + (size_t)(m0 - loc0) * p.k;
     } else {
       abase = p.ag + (size_t)m0 * p.k;
-      if (!p.prelanded) {
-        bool ok0 = true;
-        if (threadIdx.x == 0) ok0 = ag_wait_rows(p, m0, m1);
-        if (!wg_sync_ok(ok0, s_word)) break;
-      }
+      if (!p.prelanded && !ag_acquire_rows(p, m0, m1, s_word)) break;
     }
     const int valid_n = min(BN, p.n - n0);
     const i32x4_t ra = make_vdesc(abase, (uint32_t)((m1 - m0) * ldb));
@@ -101,14 +135,18 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
 }
 
 template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void ag_gemm_kernel(AgParams p) {
+__global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void ag_gemm_kernel(AgParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
   const uint32_t ticket = take_ticket(p.sync, &s_word);
   if (ticket < (uint32_t)p.n_land) {
     ag_land(p, &s_word);
+    if (p.land_joins_compute) ag_compute<BM, BN>(p, smem, &s_word);
   } else if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
     ag_compute<BM, BN>(p, smem, &s_word);
+    // with dynamic roles nobody may have been assigned the items no tile
+    // waits for (the local shard's copy is landed last): drain the queue
+    if (p.help_land) ag_land(p, &s_word);
   }
   finish_launch(p.sync);
 }
@@ -159,7 +197,7 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, char *smem, uint32
 }
 
 template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(RsParams p) {
+__global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_rs_kernel(RsParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
   const uint32_t ticket = take_ticket(p.sync, &s_word);
@@ -209,7 +247,7 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, char *smem, uint32
 }
 
 template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void gemm_ar_kernel(ArParams p) {
+__global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_ar_kernel(ArParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
   const uint32_t ticket = take_ticket(p.sync, &s_word);
@@ -220,22 +258,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ar_kernel(ArParams p) {
 // ---------------------------------------------------------------- launchers
 
 template <typename K, typename P>
-static hipError_t launch(K kernel, int grid, hipStream_t stream, const P &params) {
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, params);
+static hipError_t launch(K kernel, int threads, int grid, hipStream_t stream, const P &params) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, stream, params);
   return hipGetLastError();
 }
 
+using Big = TileCfg<256, 256>;
+using Small = TileCfg<128, 128>;
+
 hipError_t launch_ag(const AgParams &p, int bm, int grid, hipStream_t s) {
-  if (bm == 256) return launch(ag_gemm_kernel<256, 256>, grid, s, p);
-  return launch(ag_gemm_kernel<128, 128>, grid, s, p);
+  if (bm == 256) return launch(ag_gemm_kernel<256, 256>, Big::THREADS, grid, s, p);
+  return launch(ag_gemm_kernel<128, 128>, Small::THREADS, grid, s, p);
 }
 hipError_t launch_rs(const RsParams &p, int bm, int grid, hipStream_t s) {
-  if (bm == 256) return launch(gemm_rs_kernel<256, 256>, grid, s, p);
-  return launch(gemm_rs_kernel<128, 128>, grid, s, p);
+  if (bm == 256) return launch(gemm_rs_kernel<256, 256>, Big::THREADS, grid, s, p);
+  return launch(gemm_rs_kernel<128, 128>, Small::THREADS, grid, s, p);
 }
 hipError_t launch_ar(const ArParams &p, int bm, int grid, hipStream_t s) {
-  if (bm == 256) return launch(gemm_ar_kernel<256, 256>, grid, s, p);
-  return launch(gemm_ar_kernel<128, 128>, grid, s, p);
+  if (bm == 256) return launch(gemm_ar_kernel<256, 256>, Big::THREADS, grid, s, p);
+  return launch(gemm_ar_kernel<128, 128>, Small::THREADS, grid, s, p);
 }
 
 // Resident workgroups per CU of each instantiation (queried once per handle).
@@ -254,7 +295,8 @@ hipError_t occupancy(int op, int bm, int *blocks_per_cu) {
     default:
       return hipErrorInvalidValue;
   }
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f,
+                                                      bm == 256 ? Big::THREADS : Small::THREADS, 0);
 }
 
 }  // namespace mk

@@ -24,8 +24,8 @@ namespace mk {
 
 struct MoeShared {
   uint32_t word;
-  int32_t wave_cnt[4][kMaxLocalExperts];
-  int32_t scan_tmp[4];
+  int32_t wave_cnt[kMaxWaves][kMaxLocalExperts];
+  int32_t scan_tmp[kMaxWaves];
   int32_t list_tok[kRouteTokens * 8];   // (slot << 8 | token-in-item) of the item's local rows
   int32_t n_list;
   int32_t tile_base[kMaxLocalExperts + 2];
@@ -38,7 +38,7 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 }
 
 // Block-wide exclusive scan of one int per thread; returns the prefix and
-// writes the block total to *total.  Uses tmp[4].
+// writes the block total to *total.  Uses tmp[blockDim.x / 64].
 __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *tmp, int32_t *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t x = v;
@@ -50,8 +50,8 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *tmp,
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   int32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  const int nw = blockDim.x >> 6;
+  for (int w = 0; w < nw; ++w) {
     const int32_t t = tmp[w];
     if (w < wave) before += t;
     all += t;
@@ -65,8 +65,9 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *tmp,
 
 __device__ __forceinline__ void moe_route_item(const MoeParams &p, int item, MoeShared &sh) {
   const int s = item / p.items_per_src, b = item % p.items_per_src;
+  // one token per thread; threads past kRouteTokens only join the counts
   const int t = b * kRouteTokens + (int)threadIdx.x;
-  const bool valid = t < p.T;
+  const bool valid = threadIdx.x < (unsigned)kRouteTokens && t < p.T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // top-k by value, descending, kept sorted in sel/selv (fixed-size,
   // fully unrolled so the arrays stay in registers).  A new expert goes
@@ -134,7 +135,7 @@ __device__ __forceinline__ void moe_route_item(const MoeParams &p, int item, Moe
   }
   if (threadIdx.x < (unsigned)p.E_loc) {
     int tot = 0;
-    for (int w = 0; w < 4; ++w) tot += sh.wave_cnt[w][threadIdx.x];
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += sh.wave_cnt[w][threadIdx.x];
     p.item_cnt[(size_t)item * p.E_loc + threadIdx.x] = tot;
   }
   __syncthreads();
@@ -147,7 +148,7 @@ __device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
   int32_t running = 0;
   for (int e = 0; e < p.E_loc; ++e) {
     if (threadIdx.x == 0) p.expert_offsets[e] = running;
-    for (int base = 0; base < p.n_items; base += kThreads) {
+    for (int base = 0; base < p.n_items; base += (int)blockDim.x) {
       const int i = base + (int)threadIdx.x;
       const int32_t v = i < p.n_items ? p.item_cnt[(size_t)i * p.E_loc + e] : 0;
       int32_t total;
@@ -187,7 +188,7 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, MoeS
   const int e_lo = p.rank * p.E_loc;
   if (threadIdx.x == 0) sh.n_list = 0;
   __syncthreads();
-  if (t < p.T) {
+  if (threadIdx.x < (unsigned)kRouteTokens && t < p.T) {
     const size_t o = ((size_t)s * p.T + t) * p.top_k;
     for (int j = 0; j < p.top_k; ++j) {
       const int e = p.topk_idx[o + j] - e_lo;
@@ -208,7 +209,8 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, MoeS
   const int n = (int)uniform((uint32_t)sh.n_list);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t row_vec = (size_t)p.H / 8;   // 16-byte vectors per token row
-  for (int r = wave; r < n; r += 4) {
+  const int nw = blockDim.x >> 6;
+  for (int r = wave; r < n; r += nw) {
     const int v = sh.list_tok[r];
     const int slot = v >> 8, tt = b * kRouteTokens + (v & 255);
     const u32x4_t *src = reinterpret_cast<const u32x4_t *>(p.x[s] + (size_t)tt * p.H);
@@ -295,7 +297,7 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
 // ---------------------------------------------------------------- kernel
 
 template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void moe_kernel(MoeParams p) {
+__global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ MoeShared sh;
   const uint32_t ticket = take_ticket(p.sync, &sh.word);
@@ -306,9 +308,12 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(MoeParams p) {
     const uint32_t it = next_index(&ctrl->route_ctr, &sh.word);
     if (it >= (uint32_t)p.n_items) break;
     moe_route_item(p, (int)it, sh);
-    __threadfence();
+    wait_stores();
     __syncthreads();
-    if (threadIdx.x == 0) add_acq_rel(&ctrl->route_done, 1u);
+    if (threadIdx.x == 0) {
+      fence_release();
+      add_relaxed(&ctrl->route_done, 1u);
+    }
   }
 
   bool ok = true;
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(MoeParams p) {
     ok = wg_sync_ok(ok0, &sh.word);
     if (ok) {
       moe_scan<BM>(p, sh);
-      __threadfence();
+      wait_stores();
       __syncthreads();
       if (threadIdx.x == 0) st_release(&ctrl->scan_ready, p.sync.epoch);
     }
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(MoeParams p) {
         const uint32_t it = next_index(&ctrl->land_ctr, &sh.word);
         if (it >= (uint32_t)p.n_items) break;
         moe_land_item(p, (int)it, sh);
-        __threadfence();
+        wait_stores();
         __syncthreads();
         if (threadIdx.x == 0) st_release(flag_ptr(p.sync, it), p.sync.epoch);
       }
@@ -347,15 +352,16 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(MoeParams p) {
 
 hipError_t launch_moe(const MoeParams &p, int bm, int grid, hipStream_t s) {
   if (bm == 256)
-    hipLaunchKernelGGL((moe_kernel<256, 256>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((moe_kernel<256, 256>), dim3(grid), dim3(TileCfg<256, 256>::THREADS), 0, s, p);
   else
-    hipLaunchKernelGGL((moe_kernel<128, 128>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((moe_kernel<128, 128>), dim3(grid), dim3(TileCfg<128, 128>::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t occupancy_moe(int bm, int *blocks_per_cu) {
   const void *f = bm == 256 ? (const void *)moe_kernel<256, 256> : (const void *)moe_kernel<128, 128>;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      blocks_per_cu, f, bm == 256 ? TileCfg<256, 256>::THREADS : TileCfg<128, 128>::THREADS, 0);
 }
 
 }  // namespace mk

@@ -22,6 +22,9 @@ struct AgParams {
   int tiles_m, tiles_n, n_tiles, mb0;
   int lb_rows, blocks_per_chunk, item_rows, items_per_block, n_items;
   int prelanded;
+  int land_joins_compute;  // land workgroups run tiles once nothing is left to land
+  int help_land;           // compute workgroups land items while their rows are missing
+  int light_acquire;       // land blocks are cache-line aligned (see wg_sync_ok)
 };
 
 // GEMM + ReduceScatter.

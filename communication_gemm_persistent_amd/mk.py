@@ -32,6 +32,7 @@ OP_MOE = 3
 
 F_PRELANDED = 0x1
 F_NO_GATE = 0x2
+F_STATIC_ROLES = 0x4
 
 MAX_WORLD = 16
 

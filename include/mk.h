@@ -95,6 +95,10 @@ typedef struct {
 /* Per-call option bits. */
 #define MK_F_PRELANDED 0x1u /* AG: a_gathered already holds the gathered A; skip landing (GEMM alone) */
 #define MK_F_NO_GATE 0x2u   /* MoE: store x @ W_e without the gate factor */
+#define MK_F_STATIC_ROLES 0x4u /* AG: every workgroup keeps its ticket role for the whole launch
+                                 (by default compute workgroups land chunks while their rows
+                                 are missing, and land workgroups run tiles once landing is
+                                 done) */
 
 /* Create a handle on cfg->device: checks the device is gfx950, allocates the
  * control block (tickets, counters, per-chunk flags, error record).  No

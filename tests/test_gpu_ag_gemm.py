@@ -142,3 +142,24 @@ def test_ag_gemm_w8_full_size_sampled(handle, variant, mk):
         # the same launch with A already gathered (GEMM alone) gives the same bits
         c_pre, _ = run_ag(handle, d, rank=0, flags=mk.F_PRELANDED, a_gathered=dev_bf16(ag))
         O.assert_bits_equal(c_pre, c, "fused vs pre-landed")
+
+
+@pytest.mark.parametrize("shape", [(8, 1024, 512, 1024), (3, 300, 200, 72)])
+def test_ag_gemm_new_data_in_the_same_buffers(handle, shape):
+    """Consecutive calls on the same device buffers with different contents:
+    no call may see data a previous call left in a cache."""
+    W, m_s, n, k = shape
+    shards = [torch.empty((m_s, k), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    bt = torch.empty((n, k), dtype=torch.bfloat16, device="cuda")
+    c = empty_bf16((W * m_s, n))
+    ag = empty_bf16((W * m_s, k))
+    for call in range(4):
+        d = I.gen_ag(W, m_s, n, k, I.INTEGER, config=250 + call)
+        for q in range(W):
+            shards[q].copy_(dev_bf16(d["shards"][q]))
+        bt.copy_(dev_bf16(I.transpose_bits(d["b"])))
+        handle.ag_gemm(shards, bt, c, ag, rank=call % W)
+        handle.sync()
+        ref = O.ag_gemm(d["shards"], d["b"])
+        O.assert_bits_equal(bits(ag), ref["a_gathered"], f"a_gathered, call {call}")
+        O.assert_bits_equal(bits(c), ref["c"], f"C, call {call}")

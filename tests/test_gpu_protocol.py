@@ -32,7 +32,7 @@ def test_withheld_chunks_time_out_and_handle_recovers(mk):
     shards, bt, c, ag = _ag_buffers(d)
     with mk.Handle(0, spin_timeout_ms=50) as h:
         h.set_roles(mk.OP_AG_GEMM, n_land=0)          # nobody lands the peers' chunks
-        h.ag_gemm(shards, bt, c, ag, rank=0)
+        h.ag_gemm(shards, bt, c, ag, rank=0, flags=mk.F_STATIC_ROLES)
         with pytest.raises(mk.MkError) as ei:
             h.sync()
         assert ei.value.status == mk.MK_ERR_TIMEOUT
@@ -70,6 +70,32 @@ def test_invalid_arguments_launch_nothing(mk):
         assert call(shards=[shards[0].data_ptr(), pageable.ctypes.data]) == mk.MK_ERR_INVALID
         assert call(ag=0) == mk.MK_ERR_INVALID
         assert b"a_gathered" in lib.mk_last_error(h.h)
+
+
+def test_dynamic_roles_land_without_land_workgroups(mk):
+    """With the default dynamic roles, compute workgroups land missing chunks
+    themselves, so even n_land = 0 completes."""
+    d = I.gen_ag(4, 256, 256, 128, I.INTEGER, config=505)
+    shards, bt, c, ag = _ag_buffers(d)
+    with mk.Handle(0, spin_timeout_ms=2000) as h:
+        h.set_roles(mk.OP_AG_GEMM, n_land=0, n_compute=5)
+        h.ag_gemm(shards, bt, c, ag, rank=0)
+        h.sync()
+        ref = O.ag_gemm(d["shards"], d["b"])
+        O.assert_bits_equal(bits(ag), ref["a_gathered"], "a_gathered")
+        O.assert_bits_equal(bits(c), ref["c"], "C")
+
+
+def test_static_roles_give_identical_bits(mk):
+    d = I.gen_ag(4, 512, 512, 256, I.FLOAT, config=506)
+    shards, bt, c, ag = _ag_buffers(d)
+    with mk.Handle(0) as h:
+        h.ag_gemm(shards, bt, c, ag, rank=0)
+        h.sync()
+        dyn = bits(c)
+        h.ag_gemm(shards, bt, c, ag, rank=0, flags=mk.F_STATIC_ROLES)
+        h.sync()
+        O.assert_bits_equal(bits(c), dyn, "static vs dynamic roles")
 
 
 def test_roles_query_and_transfer_only_launch(mk):
