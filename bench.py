@@ -74,6 +74,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the fused call with peers in pinned host memory and with "
+                         "the Infinity Cache flushed (these reuse the fused kernel, so a "
+                         "profile of such a run mixes their durations into its average)")
     ap.add_argument("--profile-run", choices=["fused", "gemm_alone", "transfer_alone", "copy"],
                     help="only launch the named kernel a few times (for rocprofv3 counter runs)")
     args = ap.parse_args()
@@ -174,24 +178,32 @@ def main() -> int:
     t_xfer = float(np.median(time_calls(fused, reps, 3)))
     h.set_roles(mk.OP_AG_GEMM)
     t_fused_med = float(np.median(kern_ms))
-    t_fused_flushed = float(np.median(time_calls(fused, reps, 2, flushed=True)))
-    t_gemm_flushed = float(np.median(time_calls(lambda: h.ag_gemm(shards, bt, c, ag, rank=0,
-                                                                  flags=mk.F_PRELANDED),
-                                                reps, 2, flushed=True)))
     landed_bytes = (W - 1) * m_s * k * 2
+    extra = {}
+    if args.extra:
+        t_fused_flushed = float(np.median(time_calls(fused, reps, 2, flushed=True)))
+        t_gemm_flushed = float(np.median(time_calls(
+            lambda: h.ag_gemm(shards, bt, c, ag, rank=0, flags=mk.F_PRELANDED), reps, 2,
+            flushed=True)))
+        extra["mall_flushed"] = {"t_fused_ms": round(t_fused_flushed, 4),
+                                 "t_gemm_alone_ms": round(t_gemm_flushed, 4),
+                                 "fused_tflops": round(flops / (t_fused_flushed * 1e-3) / 1e12, 2)}
+        # peers in pinned host memory: landing reads cross PCIe
+        log("[bench] PCIe (pinned host) peers")
+        shards_host = [shards[0]] + [to_dev(s, "host") for s in d["shards"][1:]]
 
-    # peers in pinned host memory: landing reads cross PCIe
-    log("[bench] PCIe (pinned host) peers")
-    shards_host = [shards[0]] + [to_dev(s, "host") for s in d["shards"][1:]]
+        def fused_host():
+            h.ag_gemm(shards_host, bt, c, ag, rank=0)
 
-    def fused_host():
-        h.ag_gemm(shards_host, bt, c, ag, rank=0)
-
-    t_fused_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
-    h.set_roles(mk.OP_AG_GEMM, n_land=roles_fused[0], n_compute=0)
-    t_xfer_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
-    h.set_roles(mk.OP_AG_GEMM)
-    del shards_host
+        t_fused_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
+        h.set_roles(mk.OP_AG_GEMM, n_land=roles_fused[0], n_compute=0)
+        t_xfer_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
+        h.set_roles(mk.OP_AG_GEMM)
+        del shards_host
+        extra["pcie_host_peers"] = {
+            "t_fused_ms": round(t_fused_host, 4), "t_transfer_alone_ms": round(t_xfer_host, 4),
+            "pcie_read_GBps": round(landed_bytes / (t_xfer_host * 1e-3) / 1e9, 2),
+            "efficiency": round(max(t_gemm, t_xfer_host) / t_fused_host, 4)}
 
     src_hash = kernel_source_hash()
     traffic = traffic_from_profile(src_hash)
@@ -224,13 +236,7 @@ def main() -> int:
             "gemm_alone_over_fused": round(t_gemm / t_fused_med, 4),
             "gemm_alone_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 2),
             "landing_GBps": round(2 * landed_bytes / (t_xfer * 1e-3) / 1e9, 1),
-            "mall_flushed": {"t_fused_ms": round(t_fused_flushed, 4),
-                             "t_gemm_alone_ms": round(t_gemm_flushed, 4),
-                             "fused_tflops": round(flops / (t_fused_flushed * 1e-3) / 1e12, 2)},
-            "pcie_host_peers": {"t_fused_ms": round(t_fused_host, 4),
-                                "t_transfer_alone_ms": round(t_xfer_host, 4),
-                                "pcie_read_GBps": round(landed_bytes / (t_xfer_host * 1e-3) / 1e9, 2),
-                                "efficiency": round(max(t_gemm, t_xfer_host) / t_fused_host, 4)},
+            **extra,
         },
     }
     del shards, bt, c, ag, d

@@ -134,12 +134,22 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
   }
 }
 
-template <int BM, int BN>
+// MODE selects one of three instantiations so that profiles tell them apart:
+//   kAgFused      land + compute (the fused operation)
+//   kAgGemmOnly   A already gathered (MK_F_PRELANDED): compute only
+//   kAgLandOnly   n_compute = 0: landing only (transfer alone)
+constexpr int kAgFused = 0, kAgGemmOnly = 1, kAgLandOnly = 2;
+
+template <int BM, int BN, int MODE>
 __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void ag_gemm_kernel(AgParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
   const uint32_t ticket = take_ticket(p.sync, &s_word);
-  if (ticket < (uint32_t)p.n_land) {
+  if (MODE == kAgLandOnly) {
+    if (ticket < (uint32_t)p.n_land) ag_land(p, &s_word);
+  } else if (MODE == kAgGemmOnly) {
+    if (ticket < (uint32_t)p.n_compute) ag_compute<BM, BN>(p, smem, &s_word);
+  } else if (ticket < (uint32_t)p.n_land) {
     ag_land(p, &s_word);
     if (p.land_joins_compute) ag_compute<BM, BN>(p, smem, &s_word);
   } else if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
@@ -266,9 +276,17 @@ static hipError_t launch(K kernel, int threads, int grid, hipStream_t stream, co
 using Big = TileCfg<256, 256>;
 using Small = TileCfg<128, 128>;
 
+template <int BM, int BN>
+static hipError_t launch_ag_tile(const AgParams &p, int grid, hipStream_t s) {
+  constexpr int T = TileCfg<BM, BN>::THREADS;
+  if (p.prelanded) return launch(ag_gemm_kernel<BM, BN, kAgGemmOnly>, T, grid, s, p);
+  if (p.n_compute == 0) return launch(ag_gemm_kernel<BM, BN, kAgLandOnly>, T, grid, s, p);
+  return launch(ag_gemm_kernel<BM, BN, kAgFused>, T, grid, s, p);
+}
+
 hipError_t launch_ag(const AgParams &p, int bm, int grid, hipStream_t s) {
-  if (bm == 256) return launch(ag_gemm_kernel<256, 256>, Big::THREADS, grid, s, p);
-  return launch(ag_gemm_kernel<128, 128>, Small::THREADS, grid, s, p);
+  if (bm == 256) return launch_ag_tile<256, 256>(p, grid, s);
+  return launch_ag_tile<128, 128>(p, grid, s);
 }
 hipError_t launch_rs(const RsParams &p, int bm, int grid, hipStream_t s) {
   if (bm == 256) return launch(gemm_rs_kernel<256, 256>, Big::THREADS, grid, s, p);
@@ -284,7 +302,8 @@ hipError_t occupancy(int op, int bm, int *blocks_per_cu) {
   const void *f = nullptr;
   switch (op) {
     case MK_OP_AG_GEMM:
-      f = bm == 256 ? (const void *)ag_gemm_kernel<256, 256> : (const void *)ag_gemm_kernel<128, 128>;
+      f = bm == 256 ? (const void *)ag_gemm_kernel<256, 256, kAgFused>
+                    : (const void *)ag_gemm_kernel<128, 128, kAgFused>;
       break;
     case MK_OP_GEMM_RS:
       f = bm == 256 ? (const void *)gemm_rs_kernel<256, 256> : (const void *)gemm_rs_kernel<128, 128>;
