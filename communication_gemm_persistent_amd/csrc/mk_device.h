@@ -442,7 +442,8 @@ __device__ __forceinline__ void interleave_reads_and_mfmas() {
 template <int BM, int BN>
 __device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes, i32x4_t vb,
                                           int ldb_bytes, int K,
-                                          f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN]) {
+                                          f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN],
+                                          int kb_begin = 0, int kb_end = -1) {
   using C = TileCfg<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -453,12 +454,14 @@ __device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes,
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16_t{};
 
   const uint32_t base = lds_addr(smem);
-  const int nk = (K + kBK - 1) / kBK;
-  stage_operand<BM, C::WAVES>(va, base, lda_bytes, 0, K, wave, lane);
-  stage_operand<BN, C::WAVES>(vb, base + C::A_BYTES, ldb_bytes, 0, K, wave, lane);
+  // stages [kb_begin, kb_end) of the K loop
+  const int k0 = kb_begin * kBK;
+  const int nk = (kb_end < 0 ? (K + kBK - 1) / kBK : kb_end) - kb_begin;
+  stage_operand<BM, C::WAVES>(va, base, lda_bytes, k0, K, wave, lane);
+  stage_operand<BN, C::WAVES>(vb, base + C::A_BYTES, ldb_bytes, k0, K, wave, lane);
   if (nk > 1) {
-    stage_operand<BM, C::WAVES>(va, base + C::STAGE_BYTES, lda_bytes, kBK, K, wave, lane);
-    stage_operand<BN, C::WAVES>(vb, base + C::STAGE_BYTES + C::A_BYTES, ldb_bytes, kBK, K, wave, lane);
+    stage_operand<BM, C::WAVES>(va, base + C::STAGE_BYTES, lda_bytes, k0 + kBK, K, wave, lane);
+    stage_operand<BN, C::WAVES>(vb, base + C::STAGE_BYTES + C::A_BYTES, ldb_bytes, k0 + kBK, K, wave, lane);
     wait_vmcnt<C::LOADS>();
   } else {
     wait_vmcnt<0>();
@@ -486,8 +489,8 @@ __device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes,
     wg_barrier();
     if (kb + 2 < nk) {
       const uint32_t dst = base + (kb & 1) * C::STAGE_BYTES;
-      stage_operand<BM, C::WAVES>(va, dst, lda_bytes, (kb + 2) * kBK, K, wave, lane);
-      stage_operand<BN, C::WAVES>(vb, dst + C::A_BYTES, ldb_bytes, (kb + 2) * kBK, K, wave, lane);
+      stage_operand<BM, C::WAVES>(va, dst, lda_bytes, k0 + (kb + 2) * kBK, K, wave, lane);
+      stage_operand<BN, C::WAVES>(vb, dst + C::A_BYTES, ldb_bytes, k0 + (kb + 2) * kBK, K, wave, lane);
     }
     load_frags<BM, BN>(f0, smem + ((kb + 1) & 1) * C::STAGE_BYTES, 0, wm, wn, lane);
     mma_frags<BM, BN>(f1, acc);
@@ -513,6 +516,60 @@ __device__ __forceinline__ AccPos<BM, BN> acc_pos(int i, int j, int g) {
   p.row = wm * C::WM + i * 32 + (lane & 31);
   p.col = wn * C::WN + j * 32 + g * 8 + (lane >> 5) * 4;
   return p;
+}
+
+// Epilogue through LDS.  The accumulator tile passes through LDS in blocks
+// of kEpiRows rows; every thread then takes 4 consecutive columns of a row,
+// so each wave instruction covers a whole row (1 KiB of fp32 for BN = 256)
+// and the epilogue's global loads and stores are fully contiguous.  LDS rows
+// are padded by 16 bytes so the 32 rows one accumulator write spans fall in
+// distinct bank groups.  f(row, col, v) is called for every 4-column group
+// (row, col relative to the tile) of the tile, each exactly once.
+constexpr int kEpiRows = 64;
+
+template <int BM, int BN, class F>
+__device__ __forceinline__ void staged_epilogue(
+    const f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN], char *smem, F &&f) {
+  using C = TileCfg<BM, BN>;
+  constexpr int PITCH = BN * 4 + 16;
+  static_assert(kEpiRows * PITCH <= C::LDS_BYTES, "epilogue block must fit the LDS stages");
+  static_assert(BM % kEpiRows == 0 && kEpiRows % 32 == 0, "epilogue blocks of whole MFMA rows");
+  constexpr int CHUNKS = kEpiRows * (BN / 4);
+  static_assert(CHUNKS % C::THREADS == 0, "chunks split evenly over threads");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+#pragma unroll
+  for (int r0 = 0; r0 < BM; r0 += kEpiRows) {
+    wg_barrier();  // the previous block's reads (or the K loop's) are done
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int row0 = wm * C::WM + i * 32;
+      if (row0 < r0 || row0 >= r0 + kEpiRows) continue;
+      char *rp = smem + (row0 - r0 + (lane & 31)) * PITCH;
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = wn * C::WN + j * 32 + g * 8 + (lane >> 5) * 4;
+          f32x4_t v;
+          v[0] = acc[i][j][g * 4 + 0];
+          v[1] = acc[i][j][g * 4 + 1];
+          v[2] = acc[i][j][g * 4 + 2];
+          v[3] = acc[i][j][g * 4 + 3];
+          *reinterpret_cast<f32x4_t *>(rp + col * 4) = v;
+        }
+    }
+    wg_barrier();
+#pragma unroll
+    for (int k = 0; k < CHUNKS / C::THREADS; ++k) {
+      const int idx = (int)threadIdx.x + k * C::THREADS;
+      const int rr = idx / (BN / 4), c4 = idx % (BN / 4);
+      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(smem + rr * PITCH + c4 * 16);
+      f(r0 + rr, c4 * 4, v);
+    }
+  }
+  wg_barrier();  // LDS is free again for the next tile's stages
 }
 
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {

@@ -170,7 +170,7 @@ mk_status check_common(mk_ctx *h, int world, int rank) {
 mk_status check_gemm_shape(mk_ctx *h, long m, long n, long k) {
   if (m < 1 || n < 8 || k < 8) return fail(h, MK_ERR_INVALID, "GEMM dimensions too small");
   if (n % 8 || k % 8) return fail(h, MK_ERR_INVALID, "n and k must be multiples of 8");
-  if (k > (1 << 20) || n > (1 << 24) || m > (1L << 28))
+  if (k > (1 << 20) || n > (1 << 22) || m > (1L << 28))
     return fail(h, MK_ERR_UNSUPPORTED, "GEMM dimensions beyond the supported range");
   if ((long)256 * k * 2 >= 0x80000000L) return fail(h, MK_ERR_UNSUPPORTED, "k too large");
   return MK_OK;

@@ -179,30 +179,28 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, char *smem, uint32
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * lda));
     f32x16_t acc[C::FM][C::FN];
     gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
+    const int cols = min(BN, p.n - n0);
+    auto epi = [&](int r, int cc, const f32x4_t &v) {
+      const int row = m0 + r;
+      if (row >= m1 || cc >= cols) return;
+      const int q = row / p.ms;
+      const size_t off = (size_t)(row - q * p.ms) * p.n + n0 + cc;
+      f32x4_t x = v;
+      if (q == p.rank) {
+        // all peers' loads are issued before any is used
+        f32x4_t pv[MK_MAX_WORLD];
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+        for (int w = 0; w < MK_MAX_WORLD; ++w)
+          if (w < p.world && w != p.rank) pv[w] = *reinterpret_cast<const f32x4_t *>(p.peer[w] + off);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const AccPos<BM, BN> ps = acc_pos<BM, BN>(i, j, g);
-          const int row = m0 + ps.row, col = n0 + ps.col;
-          if (row >= m1 || col >= p.n) continue;
-          const f32x16_t &v = acc[i][j];
-          float x0 = v[g * 4 + 0], x1 = v[g * 4 + 1], x2 = v[g * 4 + 2], x3 = v[g * 4 + 3];
-          const int q = row / p.ms;
-          const size_t off = (size_t)(row - q * p.ms) * p.n + col;
-          if (q == p.rank) {
-            for (int r = 0; r < p.world; ++r) {
-              if (r == p.rank) continue;
-              const float4 pp = *reinterpret_cast<const float4 *>(p.peer[r] + off);
-              x0 += pp.x; x1 += pp.y; x2 += pp.z; x3 += pp.w;
-            }
-            *reinterpret_cast<uint2 *>(p.c_own + off) = pack_bf16x4(x0, x1, x2, x3);
-          } else {
-            *reinterpret_cast<uint2 *>(p.outbox[q] + off) = pack_bf16x4(x0, x1, x2, x3);
-          }
-        }
+        for (int w = 0; w < MK_MAX_WORLD; ++w)
+          if (w < p.world && w != p.rank) x += pv[w];
+        *reinterpret_cast<uint2 *>(p.c_own + off) = pack_bf16x4(x[0], x[1], x[2], x[3]);
+      } else {
+        *reinterpret_cast<uint2 *>(p.outbox[q] + off) = pack_bf16x4(x[0], x[1], x[2], x[3]);
+      }
+    };
+    staged_epilogue<BM, BN>(acc, smem, epi);
   }
 }
 
@@ -232,27 +230,26 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, char *smem, uint32
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * lda));
     f32x16_t acc[C::FM][C::FN];
     gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
+    const int cols = min(BN, p.n - n0);
+    auto epi = [&](int r, int cc, const f32x4_t &v) {
+      const int row = m0 + r;
+      if (row >= m1 || cc >= cols) return;
+      const size_t off = (size_t)row * p.n + n0 + cc;
+      f32x4_t pv[MK_MAX_WORLD];
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+      for (int w = 0; w < MK_MAX_WORLD; ++w)
+        if (w < p.world && w != p.rank) pv[w] = *reinterpret_cast<const f32x4_t *>(p.peer[w] + off);
+      f32x4_t x = v;
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
+      for (int w = 0; w < MK_MAX_WORLD; ++w)
+        if (w < p.world && w != p.rank) x += pv[w];
+      const uint2 o = pack_bf16x4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<uint2 *>(p.c + off) = o;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const AccPos<BM, BN> ps = acc_pos<BM, BN>(i, j, g);
-          const int row = m0 + ps.row, col = n0 + ps.col;
-          if (row >= m1 || col >= p.n) continue;
-          const f32x16_t &v = acc[i][j];
-          float x0 = v[g * 4 + 0], x1 = v[g * 4 + 1], x2 = v[g * 4 + 2], x3 = v[g * 4 + 3];
-          const size_t off = (size_t)row * p.n + col;
-          for (int r = 0; r < p.world; ++r) {
-            if (r == p.rank) continue;
-            const float4 pp = *reinterpret_cast<const float4 *>(p.peer[r] + off);
-            x0 += pp.x; x1 += pp.y; x2 += pp.z; x3 += pp.w;
-          }
-          const uint2 o = pack_bf16x4(x0, x1, x2, x3);
-          *reinterpret_cast<uint2 *>(p.c + off) = o;
-          for (int b = 0; b < p.n_bcast; ++b) *reinterpret_cast<uint2 *>(p.bcast[b] + off) = o;
-        }
+      for (int b = 0; b < MK_MAX_WORLD; ++b)
+        if (b < p.n_bcast) *reinterpret_cast<uint2 *>(p.bcast[b] + off) = o;
+    };
+    staged_epilogue<BM, BN>(acc, smem, epi);
   }
 }
 
