@@ -10,6 +10,8 @@
 // themselves compute / communication roles, tile/chunk-granular overlap).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -427,7 +429,8 @@ __device__ __forceinline__ void interleave_reads_and_mfmas() {
   __builtin_amdgcn_sched_group_barrier(0x008, M - per * R > 0 ? M - per * R : 0, 0);
 }
 
-// Run the K loop of one tile.  va covers rows [m0, m0 + valid_m) of A with
+// Run the K loop of one tile with every wave doing both jobs (tiles of
+// four waves, one per SIMD).  va covers rows [m0, m0 + valid_m) of A with
 // row pitch lda_bytes; vb rows [n0, n0 + valid_n) of Bt.  smem holds two
 // stages.  On return the accumulators hold the tile and smem is free.
 //
@@ -440,10 +443,9 @@ __device__ __forceinline__ void interleave_reads_and_mfmas() {
 // The fragment stream never drains and each DMA has a full stage of MFMAs
 // to land.
 template <int BM, int BN>
-__device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes, i32x4_t vb,
-                                          int ldb_bytes, int K,
-                                          f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN],
-                                          int kb_begin = 0, int kb_end = -1) {
+__device__ __forceinline__ void gemm_tile_interleaved(
+    char *smem, i32x4_t va, int lda_bytes, i32x4_t vb, int ldb_bytes, int K,
+    f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN]) {
   using C = TileCfg<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -454,14 +456,12 @@ __device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes,
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16_t{};
 
   const uint32_t base = lds_addr(smem);
-  // stages [kb_begin, kb_end) of the K loop
-  const int k0 = kb_begin * kBK;
-  const int nk = (kb_end < 0 ? (K + kBK - 1) / kBK : kb_end) - kb_begin;
-  stage_operand<BM, C::WAVES>(va, base, lda_bytes, k0, K, wave, lane);
-  stage_operand<BN, C::WAVES>(vb, base + C::A_BYTES, ldb_bytes, k0, K, wave, lane);
+  const int nk = (K + kBK - 1) / kBK;
+  stage_operand<BM, C::WAVES>(va, base, lda_bytes, 0, K, wave, lane);
+  stage_operand<BN, C::WAVES>(vb, base + C::A_BYTES, ldb_bytes, 0, K, wave, lane);
   if (nk > 1) {
-    stage_operand<BM, C::WAVES>(va, base + C::STAGE_BYTES, lda_bytes, k0 + kBK, K, wave, lane);
-    stage_operand<BN, C::WAVES>(vb, base + C::STAGE_BYTES + C::A_BYTES, ldb_bytes, k0 + kBK, K, wave, lane);
+    stage_operand<BM, C::WAVES>(va, base + C::STAGE_BYTES, lda_bytes, kBK, K, wave, lane);
+    stage_operand<BN, C::WAVES>(vb, base + C::STAGE_BYTES + C::A_BYTES, ldb_bytes, kBK, K, wave, lane);
     wait_vmcnt<C::LOADS>();
   } else {
     wait_vmcnt<0>();
@@ -489,14 +489,179 @@ __device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes,
     wg_barrier();
     if (kb + 2 < nk) {
       const uint32_t dst = base + (kb & 1) * C::STAGE_BYTES;
-      stage_operand<BM, C::WAVES>(va, dst, lda_bytes, k0 + (kb + 2) * kBK, K, wave, lane);
-      stage_operand<BN, C::WAVES>(vb, dst + C::A_BYTES, ldb_bytes, k0 + (kb + 2) * kBK, K, wave, lane);
+      stage_operand<BM, C::WAVES>(va, dst, lda_bytes, (kb + 2) * kBK, K, wave, lane);
+      stage_operand<BN, C::WAVES>(vb, dst + C::A_BYTES, ldb_bytes, (kb + 2) * kBK, K, wave, lane);
     }
     load_frags<BM, BN>(f0, smem + ((kb + 1) & 1) * C::STAGE_BYTES, 0, wm, wn, lane);
     mma_frags<BM, BN>(f1, acc);
     interleave_reads_and_mfmas<BM, BN>();
   }
   wg_barrier();  // every wave is done reading; the caller may refill either stage
+}
+
+// Barrier that is also a scheduling fence: no instruction moves across it,
+// so a phase's MFMAs stay between the barriers that delimit the phase.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Per-lane part of a stage DMA's buffer offset.  Instruction g fetches rows
+// 8g .. 8g+7; lane l serves row 8g + (l >> 3), logical K chunk
+// c = (l & 7) ^ ((row >> 1) & 7).  Since (row >> 1) & 7 = 4 (g & 1) + (l >> 4),
+// c depends on g only through its parity, so two per-lane offsets cover
+// every instruction; the row-group and K parts are uniform and added per
+// instruction, which keeps no per-instruction value alive across the loop.
+__device__ __forceinline__ int dma_chunk(int lane, int par) { return (lane & 7) ^ (par * 4 + (lane >> 4)); }
+
+// One DMA instruction: row group g of an operand (buffer descriptor vdesc,
+// row pitch ld_bytes), K values [k0, k0 + 64), into LDS at lds_rows (the
+// operand's region of a stage plus 1024 g).  lane_off is the lane's offset
+// for g's parity; chunks at or past K and rows past the descriptor's range
+// read as zero.  k0 >= K fetches zeros only (no memory is touched).
+__device__ __forceinline__ void dma_row_group(i32x4_t vdesc, uint32_t lds_rows, uint32_t lane_off,
+                                              int lane_c8, int ld_bytes, int k0, int K, int g) {
+  const uint32_t uni = (uint32_t)__builtin_amdgcn_readfirstlane(g * 8 * ld_bytes + k0 * 2);
+  const uint32_t off = lane_c8 < K - k0 ? lane_off + uni : kOOB;
+  dma16(vdesc, __builtin_amdgcn_readfirstlane(lds_rows), off);
+}
+
+// K loop of the 8-wave 256x256 tile as two groups that take turns
+// ("ping-pong").  Waves w and w + 4 share a SIMD; waves 0..3 (tile rows
+// 0..127) form group 0, waves 4..7 (rows 128..255) group 1.  Every wave
+// alternates a MEMORY phase (read all fragments of one 64-wide stage from
+// LDS into registers) and a COMPUTE phase (the stage's 32 MFMAs, from
+// registers only).  Group 1 runs one phase behind group 0, so in every
+// phase one wave of each SIMD feeds the matrix core while its partner waits
+// on LDS.  Workgroup barriers delimit the phases; barriers match by count,
+// so the groups' extra barriers at the start and the end pair up.
+//
+//   phase 2t   : group 0 MEMORY(t)   group 1 COMPUTE(t-1)
+//   phase 2t+1 : group 0 COMPUTE(t)  group 1 MEMORY(t)
+//
+// Refills are spread over every phase, 4 DMA instructions per wave each,
+// because issuing a whole stage at once stalls the issuing wave for as long
+// as the address unit takes to accept it.  Wave (group q, index i) owns row
+// groups 16 q + 4 i .. +3 (8 rows each) of both operands and fetches them
+// for every stage: its "own" operand (A for group 0, whose rows it alone
+// reads; B for group 1) in COMPUTE(t) for stage t+2, the other one in
+// MEMORY(t) for stage t+1.  Stage s lives in buffer s & 1.
+//   phase 2t   G0 MEMORY(t):  B rows 0..127, stage t+1.  The buffer's last
+//                             reads were in phases 2t-2 and 2t-1.
+//   phase 2t   G1 COMPUTE(t-1): B rows 128..255, stage t+1.  Same buffer.
+//   phase 2t+1 G0 COMPUTE(t): A rows 0..127, stage t+2.  Last read by G0 in
+//                             phase 2t.
+//   phase 2t+1 G1 MEMORY(t):  A rows 128..255, stage t+1.  Last read by G1
+//                             in phase 2t-1.
+// Every stage-t+1 part is read from phase 2t+2 on (A rows 128..255 from
+// 2t+3), and its issuer waits for it before the barrier that opens that
+// phase: G0 at the end of COMPUTE(t) (B; A top of t+1 was issued a phase
+// earlier still), G1 at the end of MEMORY(t) (B) and of COMPUTE(t) (A).
+// Each such wait is vmcnt(4): only the 4 instructions issued since may be
+// in flight.  Refills of stages past the last are zero fills (offset out of
+// range) of buffers nothing reads again, so the counts are the same in
+// every iteration; they are drained at the end.
+template <int BM, int BN>
+__device__ __forceinline__ void gemm_tile_pingpong(
+    char *smem, i32x4_t va, int lda_bytes, i32x4_t vb, int ldb_bytes, int K,
+    f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN]) {
+  using C = TileCfg<BM, BN>;
+  static_assert(BM == 256 && BN == 256 && C::WAVES == 8 && C::WAVES_N == 4,
+                "two groups of four waves, one group per half of the A rows");
+  constexpr int G = 4;                      // waves per group
+  constexpr int R = 4;                      // row groups per wave and operand
+  constexpr int MFMAS = 4 * C::FM * C::FN;  // per stage (32)
+  constexpr int TAIL = 0;                   // MFMAs issued after the closing barrier
+  constexpr int DMA_EVERY = 8;              // MFMAs between refill instructions
+  static_assert(TAIL >= 0 && TAIL < MFMAS && DMA_EVERY * (R - 1) < MFMAS - TAIL,
+                "refills are issued before the wait");
+  static_assert(BM / 8 == 2 * G * R && BN / 8 == 2 * G * R, "row groups per wave");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int group = wave / G;
+  const bool g0 = group == 0;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16_t{};
+
+  const uint32_t base = lds_addr(smem);
+  const int nk = (K + kBK - 1) / kBK;
+  const int ld = lda_bytes;  // every caller passes equal pitches (2 K bytes)
+  const int rg = wave * R;   // first owned row group (= 16 group + 4 index)
+  const uint32_t lane_off[2] = {(uint32_t)((lane >> 3) * ld + dma_chunk(lane, 0) * 16),
+                                (uint32_t)((lane >> 3) * ld + dma_chunk(lane, 1) * 16)};
+  const int lane_c8[2] = {dma_chunk(lane, 0) * 8, dma_chunk(lane, 1) * 8};
+  // own operand (fetched in COMPUTE) and other operand (fetched in MEMORY)
+  const i32x4_t v_own = g0 ? va : vb, v_oth = g0 ? vb : va;
+  const uint32_t lds_own = base + (g0 ? 0u : (uint32_t)C::A_BYTES) + rg * 1024;
+  const uint32_t lds_oth = base + (g0 ? (uint32_t)C::A_BYTES : 0u) + rg * 1024;
+  auto fetch = [&](bool own, int stage, int d) {
+    dma_row_group(own ? v_own : v_oth,
+                  (own ? lds_own : lds_oth) + (stage & 1) * C::STAGE_BYTES + d * 1024,
+                  lane_off[d & 1], lane_c8[d & 1], ld, stage * kBK, K, rg + d);
+  };
+  // prologue, in the order the loop's waits expect: own 0, other 0, own 1
+#pragma unroll
+  for (int d = 0; d < R; ++d) fetch(true, 0, d);
+#pragma unroll
+  for (int d = 0; d < R; ++d) fetch(false, 0, d);
+#pragma unroll
+  for (int d = 0; d < R; ++d) fetch(true, 1, d);
+  wait_vmcnt<R>();                    // stage 0 landed
+  phase_barrier();
+  if (!g0) phase_barrier();           // group 1 starts one phase late
+  Frags<BM, BN> f[4];
+  for (int t = 0; t < nk; ++t) {
+    // MEMORY(t): fragments of stage t, then the other operand of stage t+1
+    const char *st = smem + (t & 1) * C::STAGE_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) load_frags<BM, BN>(f[ks], st, ks, wm, wn, lane);
+#pragma unroll
+    for (int d = 0; d < R; ++d) fetch(false, t + 1, d);
+    if (g0)
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    else  // B rows 128..255 of stage t+1
+      __builtin_amdgcn_s_waitcnt(R | (7 << 4) | (0 << 8));               // vmcnt(4) lgkmcnt(0)
+    phase_barrier();
+    // COMPUTE(t): MFMAs from registers; the own operand of stage t+2
+    // between the first ones.  The wave meets the closing barrier TAIL
+    // MFMAs early and issues those after it, so the matrix core stays busy
+    // while the barrier resolves and the partner wave starts its COMPUTE
+    // (the MFMAs touch no LDS, so the barrier's guarantees are unchanged).
+#pragma unroll
+    for (int m = 0; m < MFMAS; ++m) {
+      if (TAIL > 0 && m == MFMAS - TAIL) {
+        wait_vmcnt<R>();  // G0: B rows 0..127 and A rows 0..127 of t+1; G1: A rows 128..255 of t+1
+        phase_barrier();
+      }
+      const int ks = m / (C::FM * C::FN), i = (m / C::FN) % C::FM, j = m % C::FN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks].b[j], f[ks].a[i], acc[i][j], 0, 0, 0);
+      if (m % DMA_EVERY == 0 && m / DMA_EVERY < R) fetch(true, t + 2, m / DMA_EVERY);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (TAIL == 0) {
+      wait_vmcnt<R>();
+      phase_barrier();
+    }
+  }
+  if (g0) phase_barrier();            // pairs with group 1's last barrier
+  wait_vmcnt<0>();                    // the zero fills past the last stage
+  wg_barrier();  // every wave is done reading; the caller may refill either stage
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes, i32x4_t vb,
+                                          int ldb_bytes, int K,
+                                          f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN]) {
+  if constexpr (TileCfg<BM, BN>::WAVES == 8)
+    gemm_tile_pingpong<BM, BN>(smem, va, lda_bytes, vb, ldb_bytes, K, acc);
+  else
+    gemm_tile_interleaved<BM, BN>(smem, va, lda_bytes, vb, ldb_bytes, K, acc);
 }
 
 // Position of accumulator group g (4 consecutive columns) of block (i, j).
