@@ -49,6 +49,7 @@ struct Ctrl {
   uint32_t route_ctr;   uint32_t _p7[15];
   uint32_t route_done;  uint32_t _p8[15];
   uint32_t scan_ready;  uint32_t _p9[15];
+  uint32_t xq[8 * 16];  // per-XCD tile queue counters, one 64-byte line each
 };
 
 // Per-launch synchronisation state passed to every kernel.
@@ -190,6 +191,59 @@ __device__ __forceinline__ uint32_t next_index(uint32_t *ctr, uint32_t *lds_word
   return uniform(*lds_word);
 }
 
+// XCD (accelerator die) the workgroup runs on: hardware register XCC_ID,
+// bits 3:0.  Each XCD has its own L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (kXcds - 1);
+}
+
+// Next tile of a tiles_m x tiles_n grid, as mi * tiles_n + nb, or -1 when
+// none is left (all threads get the value).  map selects the order:
+//   kMapGlobal  one queue, m-major (every n-block of m-block 0, then 1, ...)
+//   kMapBlocks  XCD x owns m-blocks [x tiles_m / 8, (x+1) tiles_m / 8)
+//   kMapStrided XCD x owns m-blocks x, x + 8, x + 16, ...
+// With an XCD map, every owned m-block of n-block 0 comes first, then of
+// n-block 1, ..., so the tiles one XCD runs at a time share a few A and B
+// slabs in its L2 (the stride also spreads neighbouring m-blocks, which may
+// cost alike, over the XCDs); a workgroup drains its own XCD's queue first,
+// then the others in turn.
+constexpr int kMapGlobal = 0, kMapBlocks = 1, kMapStrided = 2;
+__device__ __forceinline__ int next_tile(const Sync &s, int tiles_m, int tiles_n, int xcd, int map,
+                                         uint32_t *lds_word) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int r = -1;
+    if (map == kMapGlobal) {
+      const uint32_t i = add_relaxed(&s.ctrl->xq[0], 1u);
+      if (i < (uint32_t)(tiles_m * tiles_n)) r = (int)i;
+    } else {
+      for (int k = 0; k < kXcds && r < 0; ++k) {
+        const int x = (xcd + k) & (kXcds - 1);
+        int lo, mc;
+        if (map == kMapBlocks) {
+          lo = x * tiles_m / kXcds;
+          mc = (x + 1) * tiles_m / kXcds - lo;
+        } else {
+          lo = x;
+          mc = x < tiles_m ? (tiles_m - x + kXcds - 1) / kXcds : 0;
+        }
+        const uint32_t size = (uint32_t)(mc * tiles_n);
+        uint32_t *q = &s.ctrl->xq[x * 16];
+        if (size == 0 || ld_relaxed(q) >= size) continue;
+        const uint32_t i = add_relaxed(q, 1u);
+        if (i < size) {
+          const int mi = (int)(i % (uint32_t)mc);
+          r = (map == kMapBlocks ? lo + mi : x + kXcds * mi) * tiles_n + (int)(i / (uint32_t)mc);
+        }
+      }
+    }
+    *lds_word = (uint32_t)r;
+  }
+  __syncthreads();
+  return (int)uniform(*lds_word);
+}
+
 // Every workgroup calls this once, last.  The final workgroup of the launch
 // resets the launch-scoped counters for the next call on this handle; after
 // an abort it also clears the arrival counters, which may be partial.
@@ -206,6 +260,7 @@ __device__ __forceinline__ void finish_launch(const Sync &s) {
       st_relaxed(&c->reduce_ctr, 0u);
       st_relaxed(&c->route_ctr, 0u);
       st_relaxed(&c->route_done, 0u);
+      for (int x = 0; x < 8; ++x) st_relaxed(&c->xq[x * 16], 0u);
       if (ld_relaxed(&c->abort_epoch) == s.epoch) {
         for (uint32_t i = 0; i < s.n_flags; ++i) st_relaxed(cnt_ptr(s, i), 0u);
       }
@@ -271,6 +326,87 @@ __device__ __forceinline__ void wg_copy16(void *__restrict__ dst, const void *__
   for (; i < n; i += nt) d[i] = __builtin_nontemporal_load(&s[i]);
 }
 
+// Copy a rows x row_bytes block (row_bytes a multiple of 16) between two
+// matrices of row pitch pitch_bytes with the whole workgroup, 16-byte
+// vectors.  Thread i moves the vectors at positions i, i + nt, i + 2 nt, ...
+// of the block (nt threads, upr vectors per row).  When the rows are dense
+// or nt is a multiple of upr, those vectors lie a fixed stride apart: the
+// thread's offset stays in one register and the stride steps go in the
+// buffer instructions' scalar offset.  Full batches of U move with the
+// loads of batch b + 1 issued before the stores of batch b, so a thread
+// always has loads in flight and never waits for its own stores.  Other
+// shapes take a plain loop.  The block spans less than 2 GiB.
+#ifndef MK_COPY_U
+#define MK_COPY_U 4
+#endif
+template <int U = MK_COPY_U>
+__device__ __forceinline__ void wg_copy2d(void *__restrict__ dst, const void *__restrict__ src,
+                                          int rows, int row_bytes, size_t pitch_bytes) {
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int upr = row_bytes >> 4;
+  const int n = rows * upr;
+  const bool dense = (size_t)row_bytes == pitch_bytes;
+  const uint32_t span = (uint32_t)((size_t)(rows - 1) * pitch_bytes + row_bytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, span), rd = make_rsrc(dst, span);
+  if (!dense && nt % upr != 0) {
+    for (int p = tid; p < n; p += nt) {
+      const uint32_t o = (uint32_t)((size_t)(p / upr) * pitch_bytes + (size_t)(p % upr) * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0), rd, o, 0, 0);
+    }
+    return;
+  }
+  const uint32_t stride = (uint32_t)(dense ? (size_t)nt * 16 : (size_t)(nt / upr) * pitch_bytes);
+  const uint32_t o0 = (uint32_t)(dense ? (size_t)tid * 16
+                                       : (size_t)(tid / upr) * pitch_bytes + (size_t)(tid % upr) * 16);
+  const int batches = (n / nt) / U;  // full batches every thread has
+  u32x4_t v0[U], v1[U];
+  auto load = [&](u32x4_t (&v)[U], int b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, o0, (b * U + u) * stride, 0);
+  };
+  auto store = [&](const u32x4_t (&v)[U], int b) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, o0, (b * U + u) * stride, 0);
+  };
+  if (batches > 0) {
+    load(v0, 0);
+    int b = 0;
+    for (;;) {
+      if (b + 1 >= batches) { store(v0, b); break; }
+      load(v1, b + 1);
+      store(v0, b);
+      ++b;
+      if (b + 1 >= batches) { store(v1, b); break; }
+      load(v0, b + 1);
+      store(v1, b);
+      ++b;
+    }
+  }
+  // the rest: fewer than U + 1 vectors per thread
+  for (int p = tid + batches * U * nt, j = batches * U; p < n; p += nt, ++j) {
+    const uint32_t so = j * stride;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(rs, o0, so, 0), rd, o0, so, 0);
+  }
+}
+
+// The same copy as an out-of-line call: a kernel that also runs the GEMM
+// loop keeps the copy's registers out of the loop's allocation.  Arguments
+// of a call arrive in vector registers; they are uniform, and reading them
+// through readfirstlane says so (the buffer descriptors need scalars).
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
+}
+__device__ __attribute__((noinline)) void wg_copy2d_call(void *dst, const void *src, int rows,
+                                                         int row_bytes, size_t pitch_bytes) {
+  const uint64_t pb = reinterpret_cast<uint64_t>(uniform_ptr(reinterpret_cast<const void *>(pitch_bytes)));
+  wg_copy2d(const_cast<void *>(uniform_ptr(dst)), uniform_ptr(src), __builtin_amdgcn_readfirstlane(rows),
+            __builtin_amdgcn_readfirstlane(row_bytes), (size_t)pb);
+}
+
 // ---------------------------------------------------------------- GEMM tile engine
 //
 // C_tile[BM x BN] = A[m0:m0+BM, :] @ Bt[n0:n0+BN, :]^T with fp32 accumulation.
@@ -306,7 +442,8 @@ struct TileCfg {
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int FLAG_SLOT = 2 * STAGE_BYTES;  // 256 bytes: a flag word fetched by DMA
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES + 256;
   static constexpr int LOADS_A = BM / (8 * WAVES);  // buffer loads per wave per stage
   static constexpr int LOADS_B = BN / (8 * WAVES);
   static constexpr int LOADS = LOADS_A + LOADS_B;
@@ -338,6 +475,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // explicitly with wait_vmcnt.
 __device__ __forceinline__ void dma16(i32x4_t vdesc, uint32_t m0_base, uint32_t voff) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(vdesc), "{m0}"(m0_base)
+               : "memory");
+}
+
+// One 4-byte-per-lane global->LDS DMA (lane l's word lands at m0_base + 4 l).
+__device__ __forceinline__ void dma4(i32x4_t vdesc, uint32_t m0_base, uint32_t voff) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(vdesc), "{m0}"(m0_base)
                : "memory");
@@ -529,6 +674,17 @@ __device__ __forceinline__ void dma_row_group(i32x4_t vdesc, uint32_t lds_rows, 
   dma16(vdesc, __builtin_amdgcn_readfirstlane(lds_rows), off);
 }
 
+// Gate of a tile whose A rows arrive during the K loop in K-slabs of
+// `stages` stages, slab s being published by flag flag0 + s (an epoch-valued
+// flag of `sync`).  Slab 0 has been waited for before the tile starts; the
+// K loop checks each later slab before it fetches the slab's first A stage.
+// stages == 0: nothing to check.
+struct SlabGate {
+  const Sync *sync;
+  uint32_t flag0;
+  int stages;
+};
+
 // K loop of the 8-wave 256x256 tile as two groups that take turns
 // ("ping-pong").  Waves w and w + 4 share a SIMD; waves 0..3 (tile rows
 // 0..127) form group 0, waves 4..7 (rows 128..255) group 1.  Every wave
@@ -567,17 +723,15 @@ __device__ __forceinline__ void dma_row_group(i32x4_t vdesc, uint32_t lds_rows, 
 template <int BM, int BN>
 __device__ __forceinline__ void gemm_tile_pingpong(
     char *smem, i32x4_t va, int lda_bytes, i32x4_t vb, int ldb_bytes, int K,
-    f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN]) {
+    f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN], const SlabGate &gate) {
   using C = TileCfg<BM, BN>;
   static_assert(BM == 256 && BN == 256 && C::WAVES == 8 && C::WAVES_N == 4,
                 "two groups of four waves, one group per half of the A rows");
   constexpr int G = 4;                      // waves per group
   constexpr int R = 4;                      // row groups per wave and operand
   constexpr int MFMAS = 4 * C::FM * C::FN;  // per stage (32)
-  constexpr int TAIL = 0;                   // MFMAs issued after the closing barrier
   constexpr int DMA_EVERY = 8;              // MFMAs between refill instructions
-  static_assert(TAIL >= 0 && TAIL < MFMAS && DMA_EVERY * (R - 1) < MFMAS - TAIL,
-                "refills are issued before the wait");
+  static_assert(DMA_EVERY * (R - 1) < MFMAS, "refills are issued before the wait");
   static_assert(BM / 8 == 2 * G * R && BN / 8 == 2 * G * R, "row groups per wave");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -605,6 +759,20 @@ __device__ __forceinline__ void gemm_tile_pingpong(
                   (own ? lds_own : lds_oth) + (stage & 1) * C::STAGE_BYTES + d * 1024,
                   lane_off[d & 1], lane_c8[d & 1], ld, stage * kBK, K, rg + d);
   };
+  // slab gate: wave 0 fetches the flag of the slab starting at stage u into
+  // an LDS slot in MEMORY(u-3) (completed by its wait at the end of
+  // COMPUTE(u-3)) and reads it in MEMORY(u-2), before the barrier after
+  // which A rows of stage u are first fetched (group 0, COMPUTE(u-2)); if
+  // the flag is not yet set there it waits for it.  Slabs span at least
+  // four stages, so the slot is never refilled before it is read.
+  const int S = gate.stages;  // 0: no gate
+  const bool gated = S > 0 && wave == 0;
+  i32x4_t fdesc{};
+  uint32_t epoch = 0;
+  if (gated) {
+    fdesc = make_vdesc(gate.sync->flags, gate.sync->n_flags * kFlagStride * 4u);
+    epoch = gate.sync->epoch;
+  }
   // prologue, in the order the loop's waits expect: own 0, other 0, own 1
 #pragma unroll
   for (int d = 0; d < R; ++d) fetch(true, 0, d);
@@ -623,43 +791,52 @@ __device__ __forceinline__ void gemm_tile_pingpong(
     for (int ks = 0; ks < 4; ++ks) load_frags<BM, BN>(f[ks], st, ks, wm, wn, lane);
 #pragma unroll
     for (int d = 0; d < R; ++d) fetch(false, t + 1, d);
+    if (gated) {
+      if ((t + 2) % S == 0 && t + 2 < nk) {
+        const uint32_t seen = uniform(*reinterpret_cast<volatile uint32_t *>(smem + C::FLAG_SLOT));
+        if (seen != epoch && lane == 0) {
+          const uint32_t slab = (uint32_t)((t + 2) / S);
+          // on timeout or abort the error is recorded; the tile completes with
+          // undefined values and the caller stops at its next wait
+          (void)spin_until_eq(*gate.sync, flag_ptr(*gate.sync, gate.flag0 + slab), epoch,
+                              0x51000000u | (gate.flag0 + slab));
+        }
+      }
+      if ((t + 3) % S == 0 && t + 3 < nk)
+        dma4(fdesc, __builtin_amdgcn_readfirstlane(lds_addr(smem + C::FLAG_SLOT)),
+             (gate.flag0 + (uint32_t)((t + 3) / S)) * kFlagStride * 4u);
+    }
     if (g0)
       __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     else  // B rows 128..255 of stage t+1
       __builtin_amdgcn_s_waitcnt(R | (7 << 4) | (0 << 8));               // vmcnt(4) lgkmcnt(0)
     phase_barrier();
     // COMPUTE(t): MFMAs from registers; the own operand of stage t+2
-    // between the first ones.  The wave meets the closing barrier TAIL
-    // MFMAs early and issues those after it, so the matrix core stays busy
-    // while the barrier resolves and the partner wave starts its COMPUTE
-    // (the MFMAs touch no LDS, so the barrier's guarantees are unchanged).
+    // between them
 #pragma unroll
     for (int m = 0; m < MFMAS; ++m) {
-      if (TAIL > 0 && m == MFMAS - TAIL) {
-        wait_vmcnt<R>();  // G0: B rows 0..127 and A rows 0..127 of t+1; G1: A rows 128..255 of t+1
-        phase_barrier();
-      }
       const int ks = m / (C::FM * C::FN), i = (m / C::FN) % C::FM, j = m % C::FN;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks].b[j], f[ks].a[i], acc[i][j], 0, 0, 0);
       if (m % DMA_EVERY == 0 && m / DMA_EVERY < R) fetch(true, t + 2, m / DMA_EVERY);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (TAIL == 0) {
-      wait_vmcnt<R>();
-      phase_barrier();
-    }
+    wait_vmcnt<R>();  // G0: B rows 0..127 and A rows 0..127 of t+1; G1: A rows 128..255 of t+1
+    phase_barrier();
   }
   if (g0) phase_barrier();            // pairs with group 1's last barrier
   wait_vmcnt<0>();                    // the zero fills past the last stage
   wg_barrier();  // every wave is done reading; the caller may refill either stage
 }
 
+// A tile's K loop.  gate applies to the 8-wave tile only; a caller using
+// the 4-wave tile waits for all of its A rows before calling.
 template <int BM, int BN>
 __device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes, i32x4_t vb,
                                           int ldb_bytes, int K,
-                                          f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN]) {
+                                          f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN],
+                                          const SlabGate &gate = SlabGate{nullptr, 0u, 0}) {
   if constexpr (TileCfg<BM, BN>::WAVES == 8)
-    gemm_tile_pingpong<BM, BN>(smem, va, lda_bytes, vb, ldb_bytes, K, acc);
+    gemm_tile_pingpong<BM, BN>(smem, va, lda_bytes, vb, ldb_bytes, K, acc, gate);
   else
     gemm_tile_interleaved<BM, BN>(smem, va, lda_bytes, vb, ldb_bytes, K, acc);
 }
@@ -697,7 +874,7 @@ __device__ __forceinline__ void staged_epilogue(
     const f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN], char *smem, F &&f) {
   using C = TileCfg<BM, BN>;
   constexpr int PITCH = BN * 4 + 16;
-  static_assert(kEpiRows * PITCH <= C::LDS_BYTES, "epilogue block must fit the LDS stages");
+  static_assert(kEpiRows * PITCH <= 2 * C::STAGE_BYTES, "epilogue block must fit the LDS stages");
   static_assert(BM % kEpiRows == 0 && kEpiRows % 32 == 0, "epilogue blocks of whole MFMA rows");
   constexpr int CHUNKS = kEpiRows * (BN / 4);
   static_assert(CHUNKS % C::THREADS == 0, "chunks split evenly over threads");

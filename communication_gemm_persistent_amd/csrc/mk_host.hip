@@ -31,6 +31,10 @@ struct mk_ctx {
   int timeout_ms = 2000;
   uint64_t timeout_ticks = 0;
   int force_tile = 0;  // MK_TILE env: 128 or 256 forces the tile edge
+  bool no_slabs = true;   // MK_NO_SLABS=0 env: cut AllGather land blocks into K-slabs
+  int tile_map = 0;  // MK_TILE_MAP env: 0 global m-major order (default), 1 XCD blocks, 2 XCD strided
+  int item_kib = 256;  // MK_ITEM_KIB env: target size of one AllGather land item
+  int help_every = 2;  // MK_HELP_EVERY env: 1 in this many compute workgroups helps land
   mk::Ctrl *ctrl = nullptr;
   uint32_t *flags = nullptr;
   uint32_t *cnt = nullptr;
@@ -234,6 +238,10 @@ mk_status mk_create(mk_handle *out, const mk_config *cfg) {
     khz = 100000;
   h->timeout_ticks = (uint64_t)khz * (uint64_t)h->timeout_ms;
   if (const char *t = std::getenv("MK_TILE")) h->force_tile = std::atoi(t);
+  if (const char *t = std::getenv("MK_NO_SLABS")) h->no_slabs = std::atoi(t) != 0;
+  if (const char *t = std::getenv("MK_TILE_MAP")) h->tile_map = std::min(2, std::max(0, std::atoi(t)));
+  if (const char *t = std::getenv("MK_ITEM_KIB")) h->item_kib = std::min(4096, std::max(4, std::atoi(t)));
+  if (const char *t = std::getenv("MK_HELP_EVERY")) h->help_every = std::max(1, std::atoi(t));
   for (int i = 0; i < MK_OP_COUNT; ++i) h->roles[i] = mk_roles{-1, -1, -1};
   if (const char *r = std::getenv("MK_ROLES")) {
     int l = -1, c = -1, d = -1;
@@ -359,13 +367,28 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   p.tiles_n = cdiv(n, bm);
   p.n_tiles = p.tiles_m * p.tiles_n;
   p.mb0 = (rank * m_s) / bm;
-  // landing geometry: one flag per lb_rows rows of a shard, items of ~256 KiB
+  p.tile_map = h->tile_map;
+  // landing geometry: one flag per lb_rows rows of a shard and K-slab,
+  // items of ~256 KiB.  Shards are cut into K-slabs (about 8, of at least
+  // 256 columns) when every slab of every row starts on a 128-byte line, so
+  // that tiles can start once their first slab has landed; otherwise one
+  // slab spans K.
+  const bool base_aligned = reinterpret_cast<uintptr_t>(p.ag) % 128 == 0;
+  p.n_slabs = 1;
+  p.slab_k = k;
+  if (!pre && base_aligned && k % 64 == 0 && k >= 2048 && !h->no_slabs) {
+    p.slab_k = std::max(256, (int)((cdiv(k, 8) + 63) / 64 * 64));
+    p.n_slabs = cdiv(k, p.slab_k);
+  }
+  p.slab_stages = p.n_slabs > 1 ? p.slab_k / 64 : 0;
   p.lb_rows = bm;
-  while ((long)world * cdiv(m_s, p.lb_rows) > mk::kMaxFlags) p.lb_rows *= 2;
+  while ((long)world * cdiv(m_s, p.lb_rows) * p.n_slabs > mk::kMaxFlags) p.lb_rows *= 2;
   p.blocks_per_chunk = cdiv(m_s, p.lb_rows);
-  p.item_rows = std::max(1, std::min(p.lb_rows, (256 * 1024) / (k * 2)));
+  p.item_rows = std::max(1, std::min(p.lb_rows, (h->item_kib * 1024) / (p.slab_k * 2)));
   p.items_per_block = cdiv(p.lb_rows, p.item_rows);
-  p.n_items = world * p.blocks_per_chunk * p.items_per_block;
+  const int items_per_chunk = p.blocks_per_chunk * p.n_slabs * p.items_per_block;
+  p.n_items = world * items_per_chunk;
+  p.n_peer_items = (world - 1) * items_per_chunk;
   p.prelanded = pre ? 1 : 0;
 
   const int gmax = max_grid(h, MK_OP_AG_GEMM, bm);
@@ -378,12 +401,28 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   const bool dynamic = (flags & MK_F_STATIC_ROLES) == 0;
   p.land_joins_compute = (dynamic && compute > 0) ? 1 : 0;
   p.help_land = (dynamic && !pre) ? 1 : 0;
+  p.help_every = h->help_every;
   // land blocks on 128-byte boundaries of a_gathered allow the light acquire
-  const bool aligned = (reinterpret_cast<uintptr_t>(p.ag) % 128 == 0) &&
-                       ((size_t)p.lb_rows * k * 2) % 128 == 0 && ((size_t)m_s * k * 2) % 128 == 0;
+  const bool aligned = base_aligned && ((size_t)p.lb_rows * k * 2) % 128 == 0 &&
+                       ((size_t)m_s * k * 2) % 128 == 0;
   p.light_acquire = aligned ? 1 : 0;
+  // in-loop slab checks rely on the light acquire, and on land workgroups
+  // that finish the queue without ever waiting on a tile (a tile inside its
+  // K loop cannot help land)
+  if (!aligned || land == 0) p.slab_stages = 0;
+  // peers whose chunk has tiles in the first round of tiles (in the global
+  // order the local chunk's tiles run first; every workgroup ends up
+  // running tiles)
+  {
+    const long tiles_per_chunk = (long)cdiv(m_s, bm) * p.tiles_n;
+    const long room = (long)(land + compute) - tiles_per_chunk;
+    const long first = room <= 0 ? 1 : (room + tiles_per_chunk - 1) / tiles_per_chunk;
+    p.first_peers = (int)std::max(0L, std::min((long)(world - 1), first));
+    // an XCD map starts tiles of every chunk at once
+    if (p.tile_map != mk::kMapGlobal) p.first_peers = world - 1;
+  }
   const int grid = std::max(1, land + compute);
-  p.sync = make_sync(h, (uint32_t)(world * p.blocks_per_chunk));
+  p.sync = make_sync(h, (uint32_t)(world * p.blocks_per_chunk * p.n_slabs));
   hipError_t e = mk::launch_ag(p, bm, grid, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(h, e, "launching the AllGather+GEMM kernel");
   record(h, MK_OP_AG_GEMM, land, compute, 0, grid);
@@ -433,6 +472,7 @@ mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const m
   p.tiles_n = cdiv(n, bm);
   p.n_tiles = p.tiles_m * p.tiles_n;
   p.mb0 = (rank * p.ms) / bm;
+  p.tile_map = h->tile_map;
   const int gmax = max_grid(h, MK_OP_GEMM_RS, bm);
   int land = 0, compute = 0;
   choose_roles(h, MK_OP_GEMM_RS, gmax, 0, p.n_tiles, &land, &compute);
@@ -491,6 +531,7 @@ mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const m
   p.tiles_m = cdiv(m, bm);
   p.tiles_n = cdiv(n, bm);
   p.n_tiles = p.tiles_m * p.tiles_n;
+  p.tile_map = h->tile_map;
   const int gmax = max_grid(h, MK_OP_GEMM_AR, bm);
   int land = 0, compute = 0;
   choose_roles(h, MK_OP_GEMM_AR, gmax, 0, p.n_tiles, &land, &compute);

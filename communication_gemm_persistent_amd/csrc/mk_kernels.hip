@@ -18,24 +18,46 @@ namespace mk {
 
 // ---------------------------------------------------------------- AllGather + GEMM
 
-// Land item `it`: landing order is peers rank+1, rank+2, ... then the local
-// shard last.  Every thread copies its share, waits for its stores, and
+__device__ __forceinline__ uint32_t ag_flag(const AgParams &p, int q, int j, int s) {
+  return (uint32_t)((q * p.blocks_per_chunk + j) * p.n_slabs + s);
+}
+
+// Land item `it` (numbering in AgParams).  Peers land in the order rank+1,
+// rank+2, ...; every thread copies its share, waits for its stores, and
 // thread 0 records the arrival after the barrier.
 __device__ __forceinline__ void ag_land_item(const AgParams &p, uint32_t it) {
-  const size_t row_bytes = (size_t)p.k * 2;
-  const uint32_t per_chunk = (uint32_t)(p.blocks_per_chunk * p.items_per_block);
-  const int pos = (int)(it / per_chunk);
-  const uint32_t rem = it % per_chunk;
-  const int j = (int)(rem / p.items_per_block), ii = (int)(rem % p.items_per_block);
-  const int q = (p.rank + 1 + pos) % p.world;
+  const uint32_t per_block = (uint32_t)p.items_per_block;
+  const uint32_t per_chunk_slab = (uint32_t)p.blocks_per_chunk * per_block;
+  int q, s;
+  uint32_t rem;
+  if (it < (uint32_t)p.n_peer_items) {
+    // group of peers [pos0, pos0 + np) in landing order, slab-major
+    const uint32_t n_first = (uint32_t)p.first_peers * per_chunk_slab * p.n_slabs;
+    const bool first = it < n_first;
+    const int pos0 = first ? 0 : p.first_peers;
+    const uint32_t np = (uint32_t)(first ? p.first_peers : p.world - 1 - p.first_peers);
+    const uint32_t ig = first ? it : it - n_first;
+    const uint32_t per_slab = np * per_chunk_slab;
+    s = (int)(ig / per_slab);
+    rem = ig % per_slab;
+    q = (p.rank + 1 + pos0 + (int)(rem / per_chunk_slab)) % p.world;
+    rem %= per_chunk_slab;
+  } else {
+    const uint32_t il = it - (uint32_t)p.n_peer_items;
+    s = (int)(il / per_chunk_slab);
+    rem = il % per_chunk_slab;
+    q = p.rank;
+  }
+  const int j = (int)(rem / per_block), ii = (int)(rem % per_block);
   const int r0 = j * p.lb_rows + ii * p.item_rows;
   const int r1 = min(r0 + p.item_rows, min((j + 1) * p.lb_rows, p.m_s));
+  const int c0 = s * p.slab_k, c1 = min(c0 + p.slab_k, p.k);
   if (r1 > r0)
-    wg_copy16(p.ag + ((size_t)q * p.m_s + r0) * p.k, p.shard[q] + (size_t)r0 * p.k,
-              (size_t)(r1 - r0) * row_bytes);
+    wg_copy2d_call(p.ag + ((size_t)q * p.m_s + r0) * p.k + c0, p.shard[q] + (size_t)r0 * p.k + c0,
+                   r1 - r0, (c1 - c0) * 2, (size_t)p.k * 2);
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) arrive(p.sync, (uint32_t)(q * p.blocks_per_chunk + j), (uint32_t)p.items_per_block);
+  if (threadIdx.x == 0) arrive(p.sync, ag_flag(p, q, j, s), per_block);
 }
 
 __device__ __forceinline__ void ag_land(const AgParams &p, uint32_t *s_word) {
@@ -46,77 +68,94 @@ __device__ __forceinline__ void ag_land(const AgParams &p, uint32_t *s_word) {
   }
 }
 
-// Thread 0: are all land blocks overlapping gathered rows [m0, m1) ready?
-__device__ __forceinline__ bool ag_rows_ready(const AgParams &p, int m0, int m1) {
+// Thread 0: are slabs [s0, s1) of all land blocks overlapping gathered rows
+// [m0, m1) ready?
+__device__ __forceinline__ bool ag_rows_ready(const AgParams &p, int m0, int m1, int s0, int s1) {
   int r = m0;
   while (r < m1) {
     const int q = r / p.m_s, lr = r - q * p.m_s;
     const int j = lr / p.lb_rows;
-    if (ld_relaxed(flag_ptr(p.sync, (uint32_t)(q * p.blocks_per_chunk + j))) != p.sync.epoch)
-      return false;
+    for (int s = s0; s < s1; ++s)
+      if (ld_relaxed(flag_ptr(p.sync, ag_flag(p, q, j, s))) != p.sync.epoch) return false;
     r = q * p.m_s + min((j + 1) * p.lb_rows, p.m_s);
   }
   return true;
 }
 
-// Thread 0: wait for every land block overlapping gathered rows [m0, m1).
-__device__ __forceinline__ bool ag_wait_rows(const AgParams &p, int m0, int m1) {
+// Thread 0: wait for slabs [s0, s1) of every land block overlapping
+// gathered rows [m0, m1).
+__device__ __forceinline__ bool ag_wait_rows(const AgParams &p, int m0, int m1, int s0, int s1) {
   int r = m0;
   while (r < m1) {
     const int q = r / p.m_s, lr = r - q * p.m_s;
     const int j = lr / p.lb_rows;
-    const uint32_t f = (uint32_t)(q * p.blocks_per_chunk + j);
-    if (!spin_until_eq(p.sync, flag_ptr(p.sync, f), p.sync.epoch, (uint32_t)((q << 16) | j)))
-      return false;
+    for (int s = s0; s < s1; ++s)
+      if (!spin_until_eq(p.sync, flag_ptr(p.sync, ag_flag(p, q, j, s)), p.sync.epoch,
+                         (uint32_t)((q << 16) | (j << 8) | s)))
+        return false;
     r = q * p.m_s + min((j + 1) * p.lb_rows, p.m_s);
   }
   return true;
 }
 
-// Make gathered rows [m0, m1) available to the workgroup.  While they are
-// missing, the workgroup lands the next unlanded items itself (landing order
-// matches tile order, so these are the rows needed soonest); once nothing is
-// left to land it waits.  Returns false on timeout / abort.
-__device__ __forceinline__ bool ag_acquire_rows(const AgParams &p, int m0, int m1, uint32_t *s_word) {
+// Make slabs [s0, s1) of gathered rows [m0, m1) available to the workgroup.
+// While they are missing, the workgroup lands the next unlanded items
+// itself (slab-major landing order matches what tiles need first); once
+// nothing is left to land it waits.  Returns false on timeout / abort.
+__device__ __forceinline__ bool ag_acquire_rows(const AgParams &p, int m0, int m1, int s0, int s1,
+                                                bool helper, uint32_t *s_word) {
   for (;;) {
     bool ready = false;
-    if (threadIdx.x == 0) ready = ag_rows_ready(p, m0, m1);
+    if (threadIdx.x == 0) ready = ag_rows_ready(p, m0, m1, s0, s1);
     if (wg_broadcast(ready, s_word)) break;
-    if (!p.help_land) break;
+    if (!helper) break;
     const uint32_t it = next_index(&p.sync.ctrl->land_ctr, s_word);
     if (it >= (uint32_t)p.n_items) break;
     ag_land_item(p, it);
   }
   bool ok0 = true;
-  if (threadIdx.x == 0) ok0 = ag_wait_rows(p, m0, m1);
+  if (threadIdx.x == 0) ok0 = ag_wait_rows(p, m0, m1, s0, s1);
   return wg_sync_ok(ok0, s_word, !p.light_acquire);
 }
 
-template <int BM, int BN>
-__device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32_t *s_word) {
+template <int BM, int BN, bool PRE>
+__device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32_t *s_word,
+                                           uint32_t ticket) {
+  // compute workgroups that land items while their rows are missing
+  const bool helper = p.help_land && ticket % (uint32_t)p.help_every == 0;
   using C = TileCfg<BM, BN>;
+  const int xcd = xcd_id();
   const int M = p.world * p.m_s;
   const int loc0 = p.rank * p.m_s, loc1 = loc0 + p.m_s;
   const int ldb = p.k * 2;
   for (;;) {
-    const uint32_t t = next_index(&p.sync.ctrl->tile_ctr, s_word);
-    if (t >= (uint32_t)p.n_tiles) break;
-    const int mi = (int)t / p.tiles_n, nb = (int)t % p.tiles_n;
+    const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, p.tile_map, s_word);
+    if (t < 0) break;
+    const int mi = t / p.tiles_n, nb = t % p.tiles_n;
     const int mb = (mi + p.mb0) % p.tiles_m;   // local rows first, then peers in landing order
     const int m0 = mb * BM, n0 = nb * BN;
     const int m1 = min(m0 + BM, M);
     const uint16_t *abase;
-    if (!p.prelanded && m0 >= loc0 && m1 <= loc1) {
+    SlabGate gate{&p.sync, 0u, 0};
+    if (!PRE && m0 >= loc0 && m1 <= loc1) {
       abase = p.shard[p.rank] + (size_t)(m0 - loc0) * p.k;
     } else {
       abase = p.ag + (size_t)m0 * p.k;
-      if (!p.prelanded && !ag_acquire_rows(p, m0, m1, s_word)) break;
+      if (!PRE) {
+        // rows inside one land block: the 8-wave K loop checks slabs 1.. as
+        // it reaches them; otherwise every slab is waited for here
+        const int q0 = m0 / p.m_s, j0 = (m0 - q0 * p.m_s) / p.lb_rows;
+        const int q1 = (m1 - 1) / p.m_s, j1 = (m1 - 1 - q1 * p.m_s) / p.lb_rows;
+        const bool in_loop = C::WAVES == 8 && p.slab_stages > 0 && q0 == q1 && j0 == j1;
+        if (!ag_acquire_rows(p, m0, m1, 0, in_loop ? 1 : p.n_slabs, helper, s_word)) break;
+        if (in_loop) gate = SlabGate{&p.sync, ag_flag(p, q0, j0, 0), p.slab_stages};
+      }
     }
     const int valid_n = min(BN, p.n - n0);
     const i32x4_t ra = make_vdesc(abase, (uint32_t)((m1 - m0) * ldb));
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * ldb));
     f32x16_t acc[C::FM][C::FN];
-    gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc);
+    gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc, gate);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -148,12 +187,12 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void ag_gemm_kernel(
   if (MODE == kAgLandOnly) {
     if (ticket < (uint32_t)p.n_land) ag_land(p, &s_word);
   } else if (MODE == kAgGemmOnly) {
-    if (ticket < (uint32_t)p.n_compute) ag_compute<BM, BN>(p, smem, &s_word);
+    if (ticket < (uint32_t)p.n_compute) ag_compute<BM, BN, true>(p, smem, &s_word, ticket);
   } else if (ticket < (uint32_t)p.n_land) {
     ag_land(p, &s_word);
-    if (p.land_joins_compute) ag_compute<BM, BN>(p, smem, &s_word);
+    if (p.land_joins_compute) ag_compute<BM, BN, false>(p, smem, &s_word, ticket);
   } else if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
-    ag_compute<BM, BN>(p, smem, &s_word);
+    ag_compute<BM, BN, false>(p, smem, &s_word, ticket);
     // with dynamic roles nobody may have been assigned the items no tile
     // waits for (the local shard's copy is landed last): drain the queue
     if (p.help_land) ag_land(p, &s_word);
@@ -166,11 +205,12 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void ag_gemm_kernel(
 template <int BM, int BN>
 __device__ __forceinline__ void rs_compute(const RsParams &p, char *smem, uint32_t *s_word) {
   using C = TileCfg<BM, BN>;
+  const int xcd = xcd_id();
   const int lda = p.k * 2;
   for (;;) {
-    const uint32_t t = next_index(&p.sync.ctrl->tile_ctr, s_word);
-    if (t >= (uint32_t)p.n_tiles) break;
-    const int mi = (int)t / p.tiles_n, nb = (int)t % p.tiles_n;
+    const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, p.tile_map, s_word);
+    if (t < 0) break;
+    const int mi = t / p.tiles_n, nb = t % p.tiles_n;
     const int mb = (mi + p.mb0) % p.tiles_m;   // own slice first: its epilogue is the heaviest
     const int m0 = mb * BM, n0 = nb * BN;
     const int m1 = min(m0 + BM, p.m);
@@ -218,11 +258,12 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_rs_kernel(
 template <int BM, int BN>
 __device__ __forceinline__ void ar_compute(const ArParams &p, char *smem, uint32_t *s_word) {
   using C = TileCfg<BM, BN>;
+  const int xcd = xcd_id();
   const int lda = p.k * 2;
   for (;;) {
-    const uint32_t t = next_index(&p.sync.ctrl->tile_ctr, s_word);
-    if (t >= (uint32_t)p.n_tiles) break;
-    const int mb = (int)t / p.tiles_n, nb = (int)t % p.tiles_n;
+    const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, p.tile_map, s_word);
+    if (t < 0) break;
+    const int mb = t / p.tiles_n, nb = t % p.tiles_n;
     const int m0 = mb * BM, n0 = nb * BN;
     const int m1 = min(m0 + BM, p.m);
     const int valid_n = min(BN, p.n - n0);

@@ -9,8 +9,13 @@
 namespace mk {
 
 // AllGather + GEMM.  Landing unit: a "land block" of lb_rows rows of one
-// shard (one ready flag each), copied as items_per_block items of item_rows
-// rows.  Flag of block j of shard q: q * blocks_per_chunk + j.
+// shard and one K-slab of slab_k columns (one ready flag each), copied as
+// items_per_block items of item_rows rows.  Flag of block j of shard q,
+// slab s: (q * blocks_per_chunk + j) * n_slabs + s.  Items are numbered
+// peers first, in two groups: the first_peers peers (in landing order
+// rank+1, rank+2, ...) whose tiles run in the first round of tiles, then the
+// others; each group slab-major (every peer's slab 0, then slab 1, ...).
+// The local shard's items come last.
 struct AgParams {
   Sync sync;
   const uint16_t *shard[MK_MAX_WORLD];
@@ -19,11 +24,15 @@ struct AgParams {
   uint16_t *ag;
   int world, rank, m_s, n, k;
   int n_land, n_compute;
-  int tiles_m, tiles_n, n_tiles, mb0;
-  int lb_rows, blocks_per_chunk, item_rows, items_per_block, n_items;
+  int tiles_m, tiles_n, n_tiles, mb0, tile_map;
+  int lb_rows, blocks_per_chunk, item_rows, items_per_block, n_items, n_peer_items;
+  int first_peers;
+  int n_slabs, slab_k;
+  int slab_stages;         // slab_k / 64 when tiles may start before their later slabs land, else 0
   int prelanded;
   int land_joins_compute;  // land workgroups run tiles once nothing is left to land
   int help_land;           // compute workgroups land items while their rows are missing
+  int help_every;          // ... only every help_every-th compute workgroup (by ticket)
   int light_acquire;       // land blocks are cache-line aligned (see wg_sync_ok)
 };
 
@@ -37,7 +46,7 @@ struct RsParams {
   uint16_t *outbox[MK_MAX_WORLD];
   int world, rank, m, n, k, ms;
   int n_compute;
-  int tiles_m, tiles_n, n_tiles, mb0;
+  int tiles_m, tiles_n, n_tiles, mb0, tile_map;
 };
 
 // GEMM + AllReduce.
@@ -50,7 +59,7 @@ struct ArParams {
   uint16_t *bcast[MK_MAX_WORLD];
   int world, rank, n_bcast, m, n, k;
   int n_compute;
-  int tiles_m, tiles_n, n_tiles;
+  int tiles_m, tiles_n, n_tiles, tile_map;
 };
 
 // MoE dispatch + grouped GEMM.  Route items are blocks of kRouteTokens

@@ -163,3 +163,78 @@ def test_ag_gemm_new_data_in_the_same_buffers(handle, shape):
         ref = O.ag_gemm(d["shards"], d["b"])
         O.assert_bits_equal(bits(ag), ref["a_gathered"], f"a_gathered, call {call}")
         O.assert_bits_equal(bits(c), ref["c"], f"C, call {call}")
+
+
+# K >= 2048 with K a multiple of 64 cuts the shards into K-slabs that land
+# separately: tiles start after their first slab and check later ones in the
+# K loop.  Shapes cover 8 full slabs, a partial last slab (K = 2112: 6 slabs
+# of 320 and one of 192), and tiles spanning two land blocks (m_s = 300).
+def _handle_with_env(mk, **env):
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update({k: str(v) for k, v in env.items()})
+    try:
+        return mk.Handle(0, spin_timeout_ms=10000)
+    finally:
+        for k, v in old.items():
+            if v is None:
+                del os.environ[k]
+            else:
+                os.environ[k] = v
+
+
+@pytest.fixture(scope="module")
+def handle256(mk):
+    """Handle on the 8-wave 256x256 tile with K-slab landing, whose K loop
+    checks later slabs, and the per-XCD strided tile order."""
+    h = _handle_with_env(mk, MK_TILE="256", MK_NO_SLABS="0", MK_TILE_MAP="2")
+    yield h
+    h.close()
+
+
+@pytest.mark.parametrize("shape", [(4, 1, 256, 512, 4096), (3, 2, 512, 264, 2112),
+                                   (2, 0, 300, 520, 2048)])
+@pytest.mark.parametrize("variant", [I.FLOAT, I.INTEGER])
+@pytest.mark.parametrize("tile", ["256", "default"])
+def test_ag_gemm_k_slabs(handle, handle256, shape, variant, tile):
+    W, rank, m_s, n, k = shape
+    print(f"ag k-slabs W={W} rank={rank} m_s={m_s} n={n} k={k} variant={variant} tile={tile}",
+          flush=True)
+    d = I.gen_ag(W, m_s, n, k, variant, config=260 + W)
+    h = handle256 if tile == "256" else handle
+    for where in ("hbm", "host"):
+        c, ag = run_ag(h, d, rank=rank, where=where)
+        check_full(d, c, ag, exact=variant == I.INTEGER)
+
+
+@pytest.mark.parametrize("roles", [(1, 1), (1, 40), (4, 3), (32, 224)])
+@pytest.mark.parametrize("static", [False, True])
+def test_ag_gemm_k_slabs_roles(handle256, mk, roles, static):
+    """Few land workgroups (tiles then wait for later slabs inside the K loop)
+    and static roles give the same bits."""
+    print(f"ag k-slab roles={roles} static={static}", flush=True)
+    d = I.gen_ag(4, 512, 512, 4096, I.INTEGER, config=270)
+    ref = O.ag_gemm(d["shards"], d["b"])
+    handle256.set_roles(mk.OP_AG_GEMM, n_land=roles[0], n_compute=roles[1])
+    try:
+        c, ag = run_ag(handle256, d, rank=3, flags=mk.F_STATIC_ROLES if static else 0)
+    finally:
+        handle256.set_roles(mk.OP_AG_GEMM)
+    O.assert_bits_equal(ag, ref["a_gathered"], "a_gathered")
+    O.assert_bits_equal(c, ref["c"], f"C roles={roles} static={static}")
+
+
+@pytest.mark.parametrize("knobs", [dict(MK_TILE_MAP="1"), dict(MK_TILE_MAP="2", MK_HELP_EVERY="1"),
+                                   dict(MK_NO_SLABS="0", MK_ITEM_KIB="32", MK_HELP_EVERY="3")])
+def test_ag_gemm_schedule_knobs(mk, knobs):
+    """Tile orders, slab landing, item sizes and helper counts change only the
+    schedule, never the bits."""
+    print(f"ag knobs {knobs}", flush=True)
+    h = _handle_with_env(mk, **knobs)
+    try:
+        for shape in [(4, 2, 512, 520, 4096), (8, 5, 256, 776, 2048)]:
+            W, rank, m_s, n, k = shape
+            d = I.gen_ag(W, m_s, n, k, I.INTEGER, config=280 + W)
+            c, ag = run_ag(h, d, rank=rank)
+            check_full(d, c, ag, exact=True)
+    finally:
+        h.close()
