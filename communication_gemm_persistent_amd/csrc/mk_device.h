@@ -431,24 +431,32 @@ __device__ __attribute__((noinline)) void wg_copy2d_call(void *dst, const void *
 
 template <int BM, int BN>
 struct TileCfg {
-  // 256x256 tiles run 8 waves (2 per SIMD, a 2 x 4 grid of 128x64 blocks)
-  // so one wave's LDS-read waits are covered by the other wave's MFMAs;
-  // smaller tiles run 4 waves in a 2 x 2 grid.
-  static constexpr int WAVES_M = 2;
-  static constexpr int WAVES_N = (BM >= 256 && BN >= 256) ? 4 : 2;
+  // 256x256 tiles run 8 waves (2 per SIMD, a 2 x 4 grid of 128x64 blocks of
+  // 32x32x16 MFMAs); smaller tiles run 4 waves in a 2 x 2 grid.  256x224
+  // tiles (an N of 7 x 512 splits into 2^k x 224 columns) run 8 waves in a
+  // 4 x 2 grid of 64x112 blocks of 16x16x32 MFMAs; their B stage keeps 256
+  // rows of LDS, the last 32 filled with zeros.
+  static constexpr bool N224 = (BM == 256 && BN == 224);
+  static constexpr int MFMA = N224 ? 16 : 32;                 // MFMA output edge
+  static constexpr int SUBSTEPS = N224 ? 2 : 4;               // MFMA K steps per 64-wide stage
+  static constexpr int GROUPS = N224 ? 1 : 4;                 // 4-column groups per accumulator
+  using Acc = std::conditional_t<N224, f32x4_t, f32x16_t>;
+  static constexpr int WAVES_M = N224 ? 4 : 2;
+  static constexpr int WAVES_N = N224 ? 2 : ((BM >= 256 && BN >= 256) ? 4 : 2);
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int FM = WM / MFMA, FN = WN / MFMA;
+  static constexpr int BN_LDS = N224 ? 256 : BN;              // B rows held per stage
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN_LDS * 128;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int FLAG_SLOT = 2 * STAGE_BYTES;  // 256 bytes: a flag word fetched by DMA
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES + 256;
   static constexpr int LOADS_A = BM / (8 * WAVES);  // buffer loads per wave per stage
-  static constexpr int LOADS_B = BN / (8 * WAVES);
+  static constexpr int LOADS_B = BN_LDS / (8 * WAVES);
   static constexpr int LOADS = LOADS_A + LOADS_B;
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave blocks are built from 32x32 MFMAs");
-  static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "stage rows split over waves");
+  static_assert(WM % MFMA == 0 && WN % MFMA == 0, "wave blocks are built from whole MFMAs");
+  static_assert(BM % (8 * WAVES) == 0 && BN_LDS % (8 * WAVES) == 0, "stage rows split over waves");
 };
 
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
@@ -522,8 +530,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One K-substep (16 elements) of fragments for a wave: FM A rows-blocks and
-// FN B^T row-blocks, one 16-byte LDS read each.
+// One K-substep of fragments for a wave (16 K values for 32x32 MFMAs, 32
+// for 16x16): FM A row-blocks and FN B^T row-blocks, one 16-byte LDS read
+// each.  Lane l reads row l % MFMA of its block and 8 consecutive K values
+// starting at 8 (l / MFMA) of the substep.
 template <int BM, int BN>
 struct Frags {
   bf16x8_t a[TileCfg<BM, BN>::FM];
@@ -534,29 +544,43 @@ template <int BM, int BN>
 __device__ __forceinline__ void load_frags(Frags<BM, BN> &f, const char *stage, int ks, int wm,
                                            int wn, int lane) {
   using C = TileCfg<BM, BN>;
-  const int r32 = lane & 31;
-  const int c = ks * 2 + (lane >> 5);
+  constexpr int E = C::MFMA;
+  const int r = lane & (E - 1);
+  const int c = ks * (64 / 8 / C::SUBSTEPS) + lane / E;  // logical 16-byte chunk of the 128-byte row
+  // every block starts on a multiple of 16 rows, so the swizzle term of
+  // row (block start + r) is (r >> 1) & 7 = (lane >> 1) & 7
   const int coff = ((c ^ ((lane >> 1) & 7)) << 4);
-  const char *pa = stage + (wm * C::WM + r32) * 128 + coff;
-  const char *pb = stage + C::A_BYTES + (wn * C::WN + r32) * 128 + coff;
+  const char *pa = stage + (wm * C::WM + r) * 128 + coff;
+  const char *pb = stage + C::A_BYTES + (wn * C::WN + r) * 128 + coff;
   // issue order = first use in mma_frags (i outer, j inner): a[0] and every
   // b[j] are needed by the first FN MFMAs, a[i] only at MFMA i*FN
   f.a[0] = *reinterpret_cast<const bf16x8_t *>(pa);
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t *>(pb + j * 32 * 128);
+  for (int j = 0; j < C::FN; ++j) f.b[j] = *reinterpret_cast<const bf16x8_t *>(pb + j * E * 128);
 #pragma unroll
-  for (int i = 1; i < C::FM; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t *>(pa + i * 32 * 128);
+  for (int i = 1; i < C::FM; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t *>(pa + i * E * 128);
+}
+
+// acc += B^T-block x A-block^T: the accumulator holds C^T blocks (see above).
+template <int BM, int BN>
+__device__ __forceinline__ typename TileCfg<BM, BN>::Acc mma(const bf16x8_t &b, const bf16x8_t &a,
+                                                             const typename TileCfg<BM, BN>::Acc &acc) {
+  if constexpr (TileCfg<BM, BN>::MFMA == 16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
 }
 
 template <int BM, int BN>
-__device__ __forceinline__ void mma_frags(const Frags<BM, BN> &f,
-                                          f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN]) {
+using AccTile = typename TileCfg<BM, BN>::Acc[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN];
+
+template <int BM, int BN>
+__device__ __forceinline__ void mma_frags(const Frags<BM, BN> &f, AccTile<BM, BN> &acc) {
   using C = TileCfg<BM, BN>;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = mma<BM, BN>(f.b[j], f.a[i], acc[i][j]);
 }
 
 // Interleave the next substep's LDS reads with this substep's MFMAs: one
@@ -589,9 +613,9 @@ __device__ __forceinline__ void interleave_reads_and_mfmas() {
 // to land.
 template <int BM, int BN>
 __device__ __forceinline__ void gemm_tile_interleaved(
-    char *smem, i32x4_t va, int lda_bytes, i32x4_t vb, int ldb_bytes, int K,
-    f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN]) {
+    char *smem, i32x4_t va, int lda_bytes, i32x4_t vb, int ldb_bytes, int K, AccTile<BM, BN> &acc) {
   using C = TileCfg<BM, BN>;
+  static_assert(C::MFMA == 32, "substep pipeline of the 32x32 MFMA tiles");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -722,17 +746,16 @@ struct SlabGate {
 // every iteration; they are drained at the end.
 template <int BM, int BN>
 __device__ __forceinline__ void gemm_tile_pingpong(
-    char *smem, i32x4_t va, int lda_bytes, i32x4_t vb, int ldb_bytes, int K,
-    f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN], const SlabGate &gate) {
+    char *smem, i32x4_t va, int lda_bytes, i32x4_t vb, int ldb_bytes, int K, AccTile<BM, BN> &acc,
+    const SlabGate &gate) {
   using C = TileCfg<BM, BN>;
-  static_assert(BM == 256 && BN == 256 && C::WAVES == 8 && C::WAVES_N == 4,
+  constexpr int G = 4;                                // waves per group
+  static_assert(BM == 256 && C::WAVES == 2 * G && (G / C::WAVES_N) * C::WM == BM / 2,
                 "two groups of four waves, one group per half of the A rows");
-  constexpr int G = 4;                      // waves per group
-  constexpr int R = 4;                      // row groups per wave and operand
-  constexpr int MFMAS = 4 * C::FM * C::FN;  // per stage (32)
-  constexpr int DMA_EVERY = 8;              // MFMAs between refill instructions
-  static_assert(DMA_EVERY * (R - 1) < MFMAS, "refills are issued before the wait");
-  static_assert(BM / 8 == 2 * G * R && BN / 8 == 2 * G * R, "row groups per wave");
+  constexpr int R = 4;                                // row groups per wave and operand
+  constexpr int MFMAS = C::SUBSTEPS * C::FM * C::FN;  // per stage (32 or 56)
+  constexpr int DMA_EVERY = MFMAS / R;                // MFMAs between refill instructions
+  static_assert(BM / 8 == 2 * G * R && C::BN_LDS / 8 == 2 * G * R, "row groups per wave");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -741,7 +764,7 @@ __device__ __forceinline__ void gemm_tile_pingpong(
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::Acc{};
 
   const uint32_t base = lds_addr(smem);
   const int nk = (K + kBK - 1) / kBK;
@@ -783,12 +806,12 @@ __device__ __forceinline__ void gemm_tile_pingpong(
   wait_vmcnt<R>();                    // stage 0 landed
   phase_barrier();
   if (!g0) phase_barrier();           // group 1 starts one phase late
-  Frags<BM, BN> f[4];
+  Frags<BM, BN> f[C::SUBSTEPS];
   for (int t = 0; t < nk; ++t) {
     // MEMORY(t): fragments of stage t, then the other operand of stage t+1
     const char *st = smem + (t & 1) * C::STAGE_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) load_frags<BM, BN>(f[ks], st, ks, wm, wn, lane);
+    for (int ks = 0; ks < C::SUBSTEPS; ++ks) load_frags<BM, BN>(f[ks], st, ks, wm, wn, lane);
 #pragma unroll
     for (int d = 0; d < R; ++d) fetch(false, t + 1, d);
     if (gated) {
@@ -816,7 +839,7 @@ __device__ __forceinline__ void gemm_tile_pingpong(
 #pragma unroll
     for (int m = 0; m < MFMAS; ++m) {
       const int ks = m / (C::FM * C::FN), i = (m / C::FN) % C::FM, j = m % C::FN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks].b[j], f[ks].a[i], acc[i][j], 0, 0, 0);
+      acc[i][j] = mma<BM, BN>(f[ks].b[j], f[ks].a[i], acc[i][j]);
       if (m % DMA_EVERY == 0 && m / DMA_EVERY < R) fetch(true, t + 2, m / DMA_EVERY);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -832,8 +855,7 @@ __device__ __forceinline__ void gemm_tile_pingpong(
 // the 4-wave tile waits for all of its A rows before calling.
 template <int BM, int BN>
 __device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes, i32x4_t vb,
-                                          int ldb_bytes, int K,
-                                          f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN],
+                                          int ldb_bytes, int K, AccTile<BM, BN> &acc,
                                           const SlabGate &gate = SlabGate{nullptr, 0u, 0}) {
   if constexpr (TileCfg<BM, BN>::WAVES == 8)
     gemm_tile_pingpong<BM, BN>(smem, va, lda_bytes, vb, ldb_bytes, K, acc, gate);
@@ -851,13 +873,20 @@ struct AccPos {
 template <int BM, int BN>
 __device__ __forceinline__ AccPos<BM, BN> acc_pos(int i, int j, int g) {
   using C = TileCfg<BM, BN>;
+  constexpr int E = C::MFMA;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   AccPos<BM, BN> p;
-  p.row = wm * C::WM + i * 32 + (lane & 31);
-  p.col = wn * C::WN + j * 32 + g * 8 + (lane >> 5) * 4;
+  p.row = wm * C::WM + i * E + (lane & (E - 1));
+  p.col = wn * C::WN + j * E + g * 8 + (lane / E) * 4;
   return p;
+}
+
+// The 4 values of accumulator group g (the columns acc_pos gives).
+template <class A>
+__device__ __forceinline__ f32x4_t acc_group(const A &v, int g) {
+  return f32x4_t{v[g * 4 + 0], v[g * 4 + 1], v[g * 4 + 2], v[g * 4 + 3]};
 }
 
 // Epilogue through LDS.  The accumulator tile passes through LDS in blocks
@@ -870,9 +899,9 @@ __device__ __forceinline__ AccPos<BM, BN> acc_pos(int i, int j, int g) {
 constexpr int kEpiRows = 64;
 
 template <int BM, int BN, class F>
-__device__ __forceinline__ void staged_epilogue(
-    const f32x16_t (&acc)[TileCfg<BM, BN>::FM][TileCfg<BM, BN>::FN], char *smem, F &&f) {
+__device__ __forceinline__ void staged_epilogue(const AccTile<BM, BN> &acc, char *smem, F &&f) {
   using C = TileCfg<BM, BN>;
+  static_assert(C::MFMA == 32, "accumulator layout of the 32x32 MFMA tiles");
   constexpr int PITCH = BN * 4 + 16;
   static_assert(kEpiRows * PITCH <= 2 * C::STAGE_BYTES, "epilogue block must fit the LDS stages");
   static_assert(BM % kEpiRows == 0 && kEpiRows % 32 == 0, "epilogue blocks of whole MFMA rows");

@@ -17,11 +17,11 @@
 #include "mk_params.h"
 
 namespace mk {
-hipError_t launch_ag(const AgParams &p, int bm, int grid, hipStream_t s);
+hipError_t launch_ag(const AgParams &p, int bm, int bn, int grid, hipStream_t s);
 hipError_t launch_rs(const RsParams &p, int bm, int grid, hipStream_t s);
 hipError_t launch_ar(const ArParams &p, int bm, int grid, hipStream_t s);
 hipError_t launch_moe(const MoeParams &p, int bm, int grid, hipStream_t s);
-hipError_t occupancy(int op, int bm, int *blocks_per_cu);
+hipError_t occupancy(int op, int bm, int bn, int *blocks_per_cu);
 hipError_t occupancy_moe(int bm, int *blocks_per_cu);
 }  // namespace mk
 
@@ -34,7 +34,8 @@ struct mk_ctx {
   bool no_slabs = true;   // MK_NO_SLABS=0 env: cut AllGather land blocks into K-slabs
   int tile_map = 0;  // MK_TILE_MAP env: 0 global m-major order (default), 1 XCD blocks, 2 XCD strided
   int item_kib = 256;  // MK_ITEM_KIB env: target size of one AllGather land item
-  int help_every = 2;  // MK_HELP_EVERY env: 1 in this many compute workgroups helps land
+  int help_every = 0;  // MK_HELP_EVERY env: 1 in this many compute workgroups helps land (0: automatic)
+  int help_eager = -1;  // MK_HELP_EAGER env: helpers land until the queue is empty (-1: automatic)
   mk::Ctrl *ctrl = nullptr;
   uint32_t *flags = nullptr;
   uint32_t *cnt = nullptr;
@@ -43,7 +44,7 @@ struct mk_ctx {
   mk_roles last[MK_OP_COUNT];
   int last_grid[MK_OP_COUNT] = {0, 0, 0, 0};
   bool launched[MK_OP_COUNT] = {false, false, false, false};
-  int occ[MK_OP_COUNT][2] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};  // blocks per CU: [bm=256, bm=128]
+  int occ[MK_OP_COUNT][3] = {};  // blocks per CU: [256x256, 128x128, 256x224]
   void *ws = nullptr;
   size_t ws_bytes = 0;
   std::string err;
@@ -122,11 +123,12 @@ mk::Sync make_sync(mk_ctx *h, uint32_t n_flags) {
 }
 
 // Workgroups resident at once for a kernel instantiation.
-int max_grid(mk_ctx *h, int op, int bm) {
-  int &o = h->occ[op][bm == 256 ? 0 : 1];
+int max_grid(mk_ctx *h, int op, int bm, int bn = 0) {
+  if (bn == 0) bn = bm;
+  int &o = h->occ[op][bm != 256 ? 1 : bn == 224 ? 2 : 0];
   if (o == 0) {
     int b = 0;
-    hipError_t e = op == MK_OP_MOE ? mk::occupancy_moe(bm, &b) : mk::occupancy(op, bm, &b);
+    hipError_t e = op == MK_OP_MOE ? mk::occupancy_moe(bm, &b) : mk::occupancy(op, bm, bn, &b);
     if (e != hipSuccess || b < 1) {
       (void)hipGetLastError();
       b = 1;
@@ -137,8 +139,22 @@ int max_grid(mk_ctx *h, int op, int bm) {
 }
 
 int pick_tile(mk_ctx *h, long tiles256) {
-  if (h->force_tile == 128 || h->force_tile == 256) return h->force_tile;
+  if (h->force_tile == 128 || h->force_tile == 256 || h->force_tile == 224)
+    return h->force_tile == 224 ? 256 : h->force_tile;
   return tiles256 * 2 >= h->cu_count ? 256 : 128;
+}
+
+// Column edge of the 256-row AllGather tiles: 224 when its rounds of
+// resident tiles cost less (an N of 7 x 512 = 3584 gives 512 tiles of
+// 256x224 = two full rounds on 256 CUs instead of 448 of 256x256 = 1.75).
+int pick_tile_n(mk_ctx *h, int tiles_m, int n, int gmax) {
+  if (h->force_tile == 224) return 224;
+  if (h->force_tile != 0) return 256;
+  auto cost = [&](int bn) {
+    const long tiles = (long)tiles_m * ((n + bn - 1) / bn);
+    return ((tiles + gmax - 1) / gmax) * bn;
+  };
+  return cost(224) < cost(256) ? 224 : 256;
 }
 
 // Apply the user's role settings to the defaults.  `want_land` / `want_reduce`
@@ -242,6 +258,7 @@ mk_status mk_create(mk_handle *out, const mk_config *cfg) {
   if (const char *t = std::getenv("MK_TILE_MAP")) h->tile_map = std::min(2, std::max(0, std::atoi(t)));
   if (const char *t = std::getenv("MK_ITEM_KIB")) h->item_kib = std::min(4096, std::max(4, std::atoi(t)));
   if (const char *t = std::getenv("MK_HELP_EVERY")) h->help_every = std::max(1, std::atoi(t));
+  if (const char *t = std::getenv("MK_HELP_EAGER")) h->help_eager = std::atoi(t) != 0 ? 1 : 0;
   for (int i = 0; i < MK_OP_COUNT; ++i) h->roles[i] = mk_roles{-1, -1, -1};
   if (const char *r = std::getenv("MK_ROLES")) {
     int l = -1, c = -1, d = -1;
@@ -358,13 +375,14 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
 
   const int M = world * m_s;
   const int bm = pick_tile(h, (long)cdiv(M, 256) * cdiv(n, 256));
+  const int bn = bm == 256 ? pick_tile_n(h, cdiv(M, 256), n, max_grid(h, MK_OP_AG_GEMM, 256, 256)) : bm;
   p.world = world;
   p.rank = rank;
   p.m_s = m_s;
   p.n = n;
   p.k = k;
   p.tiles_m = cdiv(M, bm);
-  p.tiles_n = cdiv(n, bm);
+  p.tiles_n = cdiv(n, bn);
   p.n_tiles = p.tiles_m * p.tiles_n;
   p.mb0 = (rank * m_s) / bm;
   p.tile_map = h->tile_map;
@@ -391,7 +409,7 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   p.n_peer_items = (world - 1) * items_per_chunk;
   p.prelanded = pre ? 1 : 0;
 
-  const int gmax = max_grid(h, MK_OP_AG_GEMM, bm);
+  const int gmax = max_grid(h, MK_OP_AG_GEMM, bm, bn);
   int land = 0, compute = 0;
   const int want_land = pre ? 0 : std::max(1, std::min(std::min(p.n_items, gmax / 8), 32));
   choose_roles(h, MK_OP_AG_GEMM, gmax, want_land, p.n_tiles, &land, &compute);
@@ -401,7 +419,17 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   const bool dynamic = (flags & MK_F_STATIC_ROLES) == 0;
   p.land_joins_compute = (dynamic && compute > 0) ? 1 : 0;
   p.help_land = (dynamic && !pre) ? 1 : 0;
-  p.help_every = h->help_every;
+  // Landing costs workgroup time.  When the tiles leave part of the last
+  // round idle, the land workgroups fit there (they run one tile fewer) and
+  // every second waiting workgroup helps with the first chunks; when the
+  // tiles fill whole rounds, every waiting workgroup lands until the queue
+  // is empty, so all landing is done at the start and no tile waits later.
+  {
+    const int grid_all = std::max(1, land + compute);
+    const bool fills = p.n_tiles % grid_all == 0 || grid_all - p.n_tiles % grid_all < land;
+    p.help_eager = h->help_eager >= 0 ? h->help_eager : (fills ? 1 : 0);
+    p.help_every = h->help_every > 0 ? h->help_every : (p.help_eager ? 1 : 2);
+  }
   // land blocks on 128-byte boundaries of a_gathered allow the light acquire
   const bool aligned = base_aligned && ((size_t)p.lb_rows * k * 2) % 128 == 0 &&
                        ((size_t)m_s * k * 2) % 128 == 0;
@@ -423,7 +451,7 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   }
   const int grid = std::max(1, land + compute);
   p.sync = make_sync(h, (uint32_t)(world * p.blocks_per_chunk * p.n_slabs));
-  hipError_t e = mk::launch_ag(p, bm, grid, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = mk::launch_ag(p, bm, bn, grid, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(h, e, "launching the AllGather+GEMM kernel");
   record(h, MK_OP_AG_GEMM, land, compute, 0, grid);
   return MK_OK;

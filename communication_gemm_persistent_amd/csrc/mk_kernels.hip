@@ -112,6 +112,10 @@ __device__ __forceinline__ bool ag_acquire_rows(const AgParams &p, int m0, int m
     const uint32_t it = next_index(&p.sync.ctrl->land_ctr, s_word);
     if (it >= (uint32_t)p.n_items) break;
     ag_land_item(p, it);
+    if (p.help_eager) {  // keep landing while anything is left
+      ag_land(p, s_word);
+      break;
+    }
   }
   bool ok0 = true;
   if (threadIdx.x == 0) ok0 = ag_wait_rows(p, m0, m1, s0, s1);
@@ -154,20 +158,19 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
     const int valid_n = min(BN, p.n - n0);
     const i32x4_t ra = make_vdesc(abase, (uint32_t)((m1 - m0) * ldb));
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * ldb));
-    f32x16_t acc[C::FM][C::FN];
+    AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc, gate);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < C::GROUPS; ++g) {
           const AccPos<BM, BN> ps = acc_pos<BM, BN>(i, j, g);
           const int row = m0 + ps.row, col = n0 + ps.col;
           if (row < m1 && col < p.n) {
-            const f32x16_t &v = acc[i][j];
-            *reinterpret_cast<uint2 *>(p.c + (size_t)row * p.n + col) =
-                pack_bf16x4(v[g * 4 + 0], v[g * 4 + 1], v[g * 4 + 2], v[g * 4 + 3]);
+            const f32x4_t v = acc_group(acc[i][j], g);
+            *reinterpret_cast<uint2 *>(p.c + (size_t)row * p.n + col) = pack_bf16x4(v[0], v[1], v[2], v[3]);
           }
         }
   }
@@ -217,7 +220,7 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, char *smem, uint32
     const int valid_n = min(BN, p.n - n0);
     const i32x4_t ra = make_vdesc(p.a + (size_t)m0 * p.k, (uint32_t)((m1 - m0) * lda));
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * lda));
-    f32x16_t acc[C::FM][C::FN];
+    AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
     const int cols = min(BN, p.n - n0);
     auto epi = [&](int r, int cc, const f32x4_t &v) {
@@ -269,7 +272,7 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, char *smem, uint32
     const int valid_n = min(BN, p.n - n0);
     const i32x4_t ra = make_vdesc(p.a + (size_t)m0 * p.k, (uint32_t)((m1 - m0) * lda));
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * lda));
-    f32x16_t acc[C::FM][C::FN];
+    AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
     const int cols = min(BN, p.n - n0);
     auto epi = [&](int r, int cc, const f32x4_t &v) {
@@ -322,7 +325,8 @@ static hipError_t launch_ag_tile(const AgParams &p, int grid, hipStream_t s) {
   return launch(ag_gemm_kernel<BM, BN, kAgFused>, T, grid, s, p);
 }
 
-hipError_t launch_ag(const AgParams &p, int bm, int grid, hipStream_t s) {
+hipError_t launch_ag(const AgParams &p, int bm, int bn, int grid, hipStream_t s) {
+  if (bm == 256 && bn == 224) return launch_ag_tile<256, 224>(p, grid, s);
   if (bm == 256) return launch_ag_tile<256, 256>(p, grid, s);
   return launch_ag_tile<128, 128>(p, grid, s);
 }
@@ -336,12 +340,13 @@ hipError_t launch_ar(const ArParams &p, int bm, int grid, hipStream_t s) {
 }
 
 // Resident workgroups per CU of each instantiation (queried once per handle).
-hipError_t occupancy(int op, int bm, int *blocks_per_cu) {
+hipError_t occupancy(int op, int bm, int bn, int *blocks_per_cu) {
   const void *f = nullptr;
   switch (op) {
     case MK_OP_AG_GEMM:
-      f = bm == 256 ? (const void *)ag_gemm_kernel<256, 256, kAgFused>
-                    : (const void *)ag_gemm_kernel<128, 128, kAgFused>;
+      f = bm != 256 ? (const void *)ag_gemm_kernel<128, 128, kAgFused>
+          : bn == 224 ? (const void *)ag_gemm_kernel<256, 224, kAgFused>
+                      : (const void *)ag_gemm_kernel<256, 256, kAgFused>;
       break;
     case MK_OP_GEMM_RS:
       f = bm == 256 ? (const void *)gemm_rs_kernel<256, 256> : (const void *)gemm_rs_kernel<128, 128>;
@@ -354,6 +359,7 @@ hipError_t occupancy(int op, int bm, int *blocks_per_cu) {
   }
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f,
                                                       bm == 256 ? Big::THREADS : Small::THREADS, 0);
+  static_assert(TileCfg<256, 224>::THREADS == Big::THREADS, "256-row tiles run 8 waves");
 }
 
 }  // namespace mk

@@ -271,7 +271,7 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
     const int valid_n = min(BN, p.N - n0);
     const i32x4_t ra = make_vdesc(p.x_slots + (size_t)slot0 * p.H, (uint32_t)((slot1 - slot0) * ld));
     const i32x4_t rb = make_vdesc(p.wt + ((size_t)e * p.N + n0) * p.H, (uint32_t)(valid_n * ld));
-    f32x16_t acc[C::FM][C::FN];
+    AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, ld, rb, ld, p.H, acc);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {

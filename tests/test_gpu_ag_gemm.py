@@ -61,7 +61,7 @@ def test_ag_gemm_ragged(handle, shape, variant):
     check_full(d, c, ag, exact=variant == I.INTEGER)
 
 
-@pytest.mark.parametrize("tile", ["256", "128"])
+@pytest.mark.parametrize("tile", ["256", "128", "224"])
 def test_ag_gemm_each_tile_shape(mk, tile):
     os.environ["MK_TILE"] = tile
     try:
@@ -182,11 +182,11 @@ def _handle_with_env(mk, **env):
                 os.environ[k] = v
 
 
-@pytest.fixture(scope="module")
-def handle256(mk):
-    """Handle on the 8-wave 256x256 tile with K-slab landing, whose K loop
-    checks later slabs, and the per-XCD strided tile order."""
-    h = _handle_with_env(mk, MK_TILE="256", MK_NO_SLABS="0", MK_TILE_MAP="2")
+@pytest.fixture(scope="module", params=["256", "224"])
+def handle256(mk, request):
+    """Handle on an 8-wave tile (256x256 or 256x224) with K-slab landing,
+    whose K loop checks later slabs, and the per-XCD strided tile order."""
+    h = _handle_with_env(mk, MK_TILE=request.param, MK_NO_SLABS="0", MK_TILE_MAP="2")
     yield h
     h.close()
 
@@ -224,7 +224,9 @@ def test_ag_gemm_k_slabs_roles(handle256, mk, roles, static):
 
 
 @pytest.mark.parametrize("knobs", [dict(MK_TILE_MAP="1"), dict(MK_TILE_MAP="2", MK_HELP_EVERY="1"),
-                                   dict(MK_NO_SLABS="0", MK_ITEM_KIB="32", MK_HELP_EVERY="3")])
+                                   dict(MK_NO_SLABS="0", MK_ITEM_KIB="32", MK_HELP_EVERY="3"),
+                                   dict(MK_HELP_EAGER="1", MK_TILE="224"),
+                                   dict(MK_HELP_EAGER="0", MK_HELP_EVERY="1", MK_ROLES="0")])
 def test_ag_gemm_schedule_knobs(mk, knobs):
     """Tile orders, slab landing, item sizes and helper counts change only the
     schedule, never the bits."""
