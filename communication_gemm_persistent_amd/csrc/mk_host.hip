@@ -32,7 +32,7 @@ struct mk_ctx {
   uint64_t timeout_ticks = 0;
   int force_tile = 0;  // MK_TILE env: 128 or 256 forces the tile edge
   bool no_slabs = true;   // MK_NO_SLABS=0 env: cut AllGather land blocks into K-slabs
-  int tile_map = 0;  // MK_TILE_MAP env: 0 global m-major order (default), 1 XCD blocks, 2 XCD strided
+  int tile_map = -1;  // MK_TILE_MAP env: 0 global m-major order, 1 XCD blocks, 2 XCD strided (-1: per op)
   int item_kib = 256;  // MK_ITEM_KIB env: target size of one AllGather land item
   int help_every = 0;  // MK_HELP_EVERY env: 1 in this many compute workgroups helps land (0: automatic)
   int help_eager = -1;  // MK_HELP_EAGER env: helpers land until the queue is empty (-1: automatic)
@@ -385,7 +385,9 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   p.tiles_n = cdiv(n, bn);
   p.n_tiles = p.tiles_m * p.tiles_n;
   p.mb0 = (rank * m_s) / bm;
-  p.tile_map = h->tile_map;
+  // AllGather tiles share A and B slabs best per XCD; the reduce epilogues
+  // balance better in the global order (own slice first)
+  p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapStrided;
   // landing geometry: one flag per lb_rows rows of a shard and K-slab,
   // items of ~256 KiB.  Shards are cut into K-slabs (about 8, of at least
   // 256 columns) when every slab of every row starts on a 128-byte line, so
@@ -500,7 +502,7 @@ mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const m
   p.tiles_n = cdiv(n, bm);
   p.n_tiles = p.tiles_m * p.tiles_n;
   p.mb0 = (rank * p.ms) / bm;
-  p.tile_map = h->tile_map;
+  p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapGlobal;
   const int gmax = max_grid(h, MK_OP_GEMM_RS, bm);
   int land = 0, compute = 0;
   choose_roles(h, MK_OP_GEMM_RS, gmax, 0, p.n_tiles, &land, &compute);
@@ -559,7 +561,7 @@ mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const m
   p.tiles_m = cdiv(m, bm);
   p.tiles_n = cdiv(n, bm);
   p.n_tiles = p.tiles_m * p.tiles_n;
-  p.tile_map = h->tile_map;
+  p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapGlobal;
   const int gmax = max_grid(h, MK_OP_GEMM_AR, bm);
   int land = 0, compute = 0;
   choose_roles(h, MK_OP_GEMM_AR, gmax, 0, p.n_tiles, &land, &compute);

@@ -1,4 +1,6 @@
 """GPU parity of GEMM+ReduceScatter and GEMM+AllReduce against the CPU oracle."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -178,3 +180,34 @@ def test_gemm_ar_w8_full_size_sampled(handle, variant):
         O.assert_bits_equal(c[rows], ref, "rows (integer inputs)")
     else:
         O.assert_close_bf16(c[rows], ref, "rows")
+
+
+@pytest.mark.parametrize("tile_map", ["1", "2"])
+def test_rs_ar_tile_orders(mk, tile_map):
+    """The per-XCD tile orders hand out every tile exactly once (RS and AR at
+    shapes with ragged tile grids)."""
+    old = os.environ.get("MK_TILE_MAP")
+    os.environ["MK_TILE_MAP"] = tile_map
+    try:
+        h = mk.Handle(0, spin_timeout_ms=10000)
+    finally:
+        if old is None:
+            del os.environ["MK_TILE_MAP"]
+        else:
+            os.environ["MK_TILE_MAP"] = old
+    try:
+        for shape in [(8, 3, 2560, 776, 264), (3, 1, 1500, 520, 72)]:
+            W, rank, m, n, k = shape
+            print(f"rs tile_map={tile_map} {shape}", flush=True)
+            d = I.gen_rs(W, m, n, k, rank=rank, variant=I.INTEGER, config=330 + W)
+            c_own, outbox = run_rs(h, d, rank)
+            check_rs(d, rank, c_own, outbox, exact=True)
+            print(f"ar tile_map={tile_map} {shape}", flush=True)
+            d = I.gen_ar(W, m, n, k, rank=rank, variant=I.INTEGER, config=340 + W)
+            c, bc = run_ar(h, d, rank, 2)
+            ref = O.gemm_ar(d["a"], d["b"], d["peers"], rank=rank, n_bcast=2)
+            O.assert_bits_equal(c, ref["c"], "c")
+            for i, b in enumerate(bc):
+                O.assert_bits_equal(b, c, f"bcast[{i}] vs c")
+    finally:
+        h.close()
