@@ -36,6 +36,7 @@ struct mk_ctx {
   int item_kib = 256;  // MK_ITEM_KIB env: target size of one AllGather land item
   int help_every = 0;  // MK_HELP_EVERY env: 1 in this many compute workgroups helps land (0: automatic)
   int help_eager = -1;  // MK_HELP_EAGER env: helpers land until the queue is empty (-1: automatic)
+  int land_split = 1;  // MK_LAND_SPLIT env: land first-round chunks at the start, the rest between tiles
   mk::Ctrl *ctrl = nullptr;
   uint32_t *flags = nullptr;
   uint32_t *cnt = nullptr;
@@ -259,6 +260,7 @@ mk_status mk_create(mk_handle *out, const mk_config *cfg) {
   if (const char *t = std::getenv("MK_ITEM_KIB")) h->item_kib = std::min(4096, std::max(4, std::atoi(t)));
   if (const char *t = std::getenv("MK_HELP_EVERY")) h->help_every = std::max(1, std::atoi(t));
   if (const char *t = std::getenv("MK_HELP_EAGER")) h->help_eager = std::atoi(t) != 0 ? 1 : 0;
+  if (const char *t = std::getenv("MK_LAND_SPLIT")) h->land_split = std::atoi(t) != 0 ? 1 : 0;
   for (int i = 0; i < MK_OP_COUNT; ++i) h->roles[i] = mk_roles{-1, -1, -1};
   if (const char *r = std::getenv("MK_ROLES")) {
     int l = -1, c = -1, d = -1;
@@ -412,26 +414,27 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   p.prelanded = pre ? 1 : 0;
 
   const int gmax = max_grid(h, MK_OP_AG_GEMM, bm, bn);
+  const bool dynamic = (flags & MK_F_STATIC_ROLES) == 0;
+  // Landing costs workgroup time.  When the tiles leave part of the last
+  // round of resident workgroups idle, land workgroups fit there (they run
+  // one tile fewer) and every second waiting workgroup helps with the first
+  // chunks.  When the tiles fill whole rounds, either every waiting
+  // workgroup lands until the queue is empty (all landing at the start), or
+  // (split) the chunks of first-round tiles land at the start and every
+  // workgroup lands its share of the rest after each tile, just before the
+  // tiles that need it; the split needs the global tile order, whose first
+  // round covers the fewest chunks.
+  const int want_land0 = pre ? 0 : std::max(1, std::min(std::min(p.n_items, gmax / 8), 32));
+  const bool fills = p.n_tiles % gmax == 0 || gmax - p.n_tiles % gmax < want_land0;
+  const bool split = !pre && dynamic && fills && h->land_split > 0 && h->roles[MK_OP_AG_GEMM].n_land < 0;
+  if (split && h->tile_map < 0) p.tile_map = mk::kMapGlobal;
   int land = 0, compute = 0;
-  const int want_land = pre ? 0 : std::max(1, std::min(std::min(p.n_items, gmax / 8), 32));
-  choose_roles(h, MK_OP_AG_GEMM, gmax, want_land, p.n_tiles, &land, &compute);
+  choose_roles(h, MK_OP_AG_GEMM, gmax, split ? 0 : want_land0, p.n_tiles, &land, &compute);
   if (pre) land = 0;
   p.n_land = land;
   p.n_compute = compute;
-  const bool dynamic = (flags & MK_F_STATIC_ROLES) == 0;
   p.land_joins_compute = (dynamic && compute > 0) ? 1 : 0;
   p.help_land = (dynamic && !pre) ? 1 : 0;
-  // Landing costs workgroup time.  When the tiles leave part of the last
-  // round idle, the land workgroups fit there (they run one tile fewer) and
-  // every second waiting workgroup helps with the first chunks; when the
-  // tiles fill whole rounds, every waiting workgroup lands until the queue
-  // is empty, so all landing is done at the start and no tile waits later.
-  {
-    const int grid_all = std::max(1, land + compute);
-    const bool fills = p.n_tiles % grid_all == 0 || grid_all - p.n_tiles % grid_all < land;
-    p.help_eager = h->help_eager >= 0 ? h->help_eager : (fills ? 1 : 0);
-    p.help_every = h->help_every > 0 ? h->help_every : (p.help_eager ? 1 : 2);
-  }
   // land blocks on 128-byte boundaries of a_gathered allow the light acquire
   const bool aligned = base_aligned && ((size_t)p.lb_rows * k * 2) % 128 == 0 &&
                        ((size_t)m_s * k * 2) % 128 == 0;
@@ -443,13 +446,25 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   // peers whose chunk has tiles in the first round of tiles (in the global
   // order the local chunk's tiles run first; every workgroup ends up
   // running tiles)
+  const int grid_all = std::max(1, land + compute);
   {
     const long tiles_per_chunk = (long)cdiv(m_s, bm) * p.tiles_n;
-    const long room = (long)(land + compute) - tiles_per_chunk;
+    const long room = (long)grid_all - tiles_per_chunk;
     const long first = room <= 0 ? 1 : (room + tiles_per_chunk - 1) / tiles_per_chunk;
     p.first_peers = (int)std::max(0L, std::min((long)(world - 1), first));
     // an XCD map starts tiles of every chunk at once
     if (p.tile_map != mk::kMapGlobal) p.first_peers = world - 1;
+  }
+  if (split) {
+    p.help_eager = 1;
+    p.eager_items = p.first_peers * items_per_chunk;
+    p.land_between = (p.n_peer_items - p.eager_items + grid_all - 1) / grid_all;
+    p.help_every = 1;
+  } else {
+    p.help_eager = h->help_eager >= 0 ? h->help_eager : (fills ? 1 : 0);
+    p.eager_items = p.n_items;
+    p.land_between = 0;
+    p.help_every = h->help_every > 0 ? h->help_every : (p.help_eager ? 1 : 2);
   }
   const int grid = std::max(1, land + compute);
   p.sync = make_sync(h, (uint32_t)(world * p.blocks_per_chunk * p.n_slabs));

@@ -105,6 +105,8 @@ __device__ __forceinline__ bool ag_wait_rows(const AgParams &p, int m0, int m1, 
 __device__ __forceinline__ bool ag_acquire_rows(const AgParams &p, int m0, int m1, int s0, int s1,
                                                 bool helper, uint32_t *s_word) {
   for (;;) {
+    // the barrier closes the previous item's single-thread arrival (see uniform())
+    __syncthreads();
     bool ready = false;
     if (threadIdx.x == 0) ready = ag_rows_ready(p, m0, m1, s0, s1);
     if (wg_broadcast(ready, s_word)) break;
@@ -112,8 +114,16 @@ __device__ __forceinline__ bool ag_acquire_rows(const AgParams &p, int m0, int m
     const uint32_t it = next_index(&p.sync.ctrl->land_ctr, s_word);
     if (it >= (uint32_t)p.n_items) break;
     ag_land_item(p, it);
-    if (p.help_eager) {  // keep landing while anything is left
-      ag_land(p, s_word);
+    if (p.help_eager) {  // keep landing while items below eager_items are unclaimed
+      for (;;) {
+        __syncthreads();
+        bool more = false;
+        if (threadIdx.x == 0) more = ld_relaxed(&p.sync.ctrl->land_ctr) < (uint32_t)p.eager_items;
+        if (!wg_broadcast(more, s_word)) break;
+        const uint32_t jt = next_index(&p.sync.ctrl->land_ctr, s_word);
+        if (jt >= (uint32_t)p.n_items) break;
+        ag_land_item(p, jt);
+      }
       break;
     }
   }
@@ -173,6 +183,14 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
             *reinterpret_cast<uint2 *>(p.c + (size_t)row * p.n + col) = pack_bf16x4(v[0], v[1], v[2], v[3]);
           }
         }
+    // this workgroup's share of the items later tiles need
+    if constexpr (!PRE) {
+      for (int i = 0; i < p.land_between; ++i) {
+        const uint32_t it = next_index(&p.sync.ctrl->land_ctr, s_word);
+        if (it >= (uint32_t)p.n_items) break;
+        ag_land_item(p, it);
+      }
+    }
   }
 }
 

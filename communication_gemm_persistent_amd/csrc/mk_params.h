@@ -33,7 +33,9 @@ struct AgParams {
   int land_joins_compute;  // land workgroups run tiles once nothing is left to land
   int help_land;           // compute workgroups land items while their rows are missing
   int help_every;          // ... only every help_every-th compute workgroup (by ticket)
-  int help_eager;          // a helping workgroup lands until the queue is empty, not only until its rows are ready
+  int help_eager;          // a helping workgroup lands every item below eager_items, not only until its rows are ready
+  int eager_items;
+  int land_between;        // items every compute workgroup lands after each tile
   int light_acquire;       // land blocks are cache-line aligned (see wg_sync_ok)
 };
 

@@ -225,8 +225,9 @@ def test_ag_gemm_k_slabs_roles(handle256, mk, roles, static):
 
 @pytest.mark.parametrize("knobs", [dict(MK_TILE_MAP="1"), dict(MK_TILE_MAP="2", MK_HELP_EVERY="1"),
                                    dict(MK_NO_SLABS="0", MK_ITEM_KIB="32", MK_HELP_EVERY="3"),
-                                   dict(MK_HELP_EAGER="1", MK_TILE="224"),
-                                   dict(MK_HELP_EAGER="0", MK_HELP_EVERY="1", MK_ROLES="0")])
+                                   dict(MK_HELP_EAGER="1", MK_TILE="224", MK_LAND_SPLIT="0"),
+                                   dict(MK_HELP_EAGER="0", MK_HELP_EVERY="1", MK_ROLES="0"),
+                                   dict(MK_LAND_SPLIT="1", MK_TILE="224", MK_ITEM_KIB="64")])
 def test_ag_gemm_schedule_knobs(mk, knobs):
     """Tile orders, slab landing, item sizes and helper counts change only the
     schedule, never the bits."""
