@@ -186,13 +186,18 @@ def gen_ar(world: int, m: int, n: int, k: int, rank: int = 0, variant: int = FLO
 
 
 def gen_moe(S: int, T: int, H: int, N: int, E: int, E_loc: int, variant: int = FLOAT,
-            config: int = 4, x_scale: float = 1.0, w_scale: float = 0.02) -> Dict[str, object]:
+            config: int = 4, x_scale: float = 1.0, w_scale: float = 0.02, top_k: int = 2,
+            y_scale: float = 0.05) -> Dict[str, object]:
     """MoE inputs: 0..S-1 = tokens x_s [T,H] bf16, S..2S-1 = logits_s [T,E] fp32,
-    2S = expert weights W [E_loc, H, N] bf16 (logical [K, N] per expert)."""
+    2S = expert weights W [E_loc, H, N] bf16 (logical [K, N] per expert),
+    2S+1 = y_peer [T, top_k=2, N] bf16: the gated expert rows the peers return
+    for this rank's tokens in the combine (standard deviation y_scale, about
+    that of gate * x @ W at these scales)."""
     xs = [draw_bf16(variant, config, s, (T, H), "normal", x_scale) for s in range(S)]
     logits = [draw_logits(variant, config, S + s, (T, E)) for s in range(S)]
     w = draw_bf16(variant, config, 2 * S, (E_loc, H, N), "normal", w_scale)
-    return dict(x=xs, logits=logits, w=w)
+    y_peer = draw_bf16(variant, config, 2 * S + 1, (T, top_k, N), "normal", y_scale)
+    return dict(x=xs, logits=logits, w=w, y_peer=y_peer)
 
 
 def gen_workload(name: str, variant: int = FLOAT) -> Dict[str, object]:

@@ -37,6 +37,10 @@ Readings of points the pages leave open (each also listed in the design notes):
       token is dropped.
 * r9  the expert output is y[slot] = bf16(gate * (x @ W_e)); an ungated variant
       (gate applied later, in the combine) gives bf16(x @ W_e).
+* r10 (combine; the pages describe the dispatch only) each output row of this
+      rank's experts returns to its source at (token, k), k being the
+      expert's place in the token's top-k list; a source's combined row is
+      the bf16 of the sum over k of its returned rows (gates already applied).
 
 Parity is pinned (tests marked "not gpu"): bf16 rounding by exhaustive and
 brute-force nearest-value search; the GEMM by exact rational brute force on
@@ -44,7 +48,8 @@ tiny shapes and by identity / unit-vector special cases; the gather order by
 B = I; ReduceScatter by a W-rank emulation whose slices must tile the full
 sum; AllReduce by its equivalence to ReduceScatter followed by a gather; MoE
 routing by a brute-force sort and the dispatch permutation by its inverse;
-and hand-worked examples under tests/golden.
+the MoE combine by its return permutation and exact-gate examples; and
+hand-worked examples under tests/golden.
 """
 from __future__ import annotations
 
@@ -326,3 +331,56 @@ def moe_dispatch_gemm(x: Sequence[np.ndarray], logits: Sequence[np.ndarray], w: 
     out = dict(route, **d)
     out.update(x_slots=x_slots, y=y, n_slots=n_slots)
     return out
+
+
+# --------------------------------------------------------------------------
+# MoE combine (completes the MoE layer after dispatch + grouped GEMM)
+# --------------------------------------------------------------------------
+
+
+def moe_return_positions(slot_token: np.ndarray, idx: np.ndarray, expert_offsets: np.ndarray,
+                         T: int, top_k: int, E_loc: int, rank: int) -> np.ndarray:
+    """For every slot of this rank, the position s*T*top_k + t*top_k + k its
+    output row returns to: source s = slot_token // T, token t, and k the
+    place of the slot's expert in the token's top-k list (reading r10)."""
+    n = len(slot_token)
+    exp_of = slot_expert(expert_offsets, n)
+    pos = np.zeros(n, dtype=np.int64)
+    for slot in range(n):
+        st = int(slot_token[slot])
+        g = rank * E_loc + int(exp_of[slot])
+        ks = np.nonzero(np.asarray(idx[st]) == g)[0]
+        assert ks.size == 1, "a slot's expert appears once in its token's top-k list"
+        pos[slot] = st * top_k + int(ks[0])
+    return pos
+
+
+def moe_combine(x: Sequence[np.ndarray], logits: Sequence[np.ndarray], w: np.ndarray,
+                top_k: int, y_peer: np.ndarray, rank: int = 0) -> Dict[str, np.ndarray]:
+    """[P1] MoE layer of one rank: dispatch + grouped GEMM (moe_dispatch_gemm),
+    then the combine of reading r10.
+
+    Every output row y[slot] of this rank's experts returns to its source s at
+    position (t, k), k being the slot's expert's place in token t's top-k list:
+    ret[s] is [T, top_k, N] bf16 with ret_mask[s] [T, top_k] marking the rows
+    this rank writes (its own experts' pairs).  For this rank's own tokens,
+    out[t] = bf16(sum over k of v_k), v_k = y[slot] when expert k of token t is
+    local and y_peer[t, k] (the row its owner returned) otherwise; the gate is
+    already in the rows, the sum runs over k in float64 and rounds once.
+    """
+    S = len(x)
+    T = x[0].shape[0]
+    E_loc, N = w.shape[0], w.shape[2]
+    d = moe_dispatch_gemm(x, logits, w, top_k, rank)
+    pos = moe_return_positions(d["slot_token"], d["idx"], d["expert_offsets"], T, top_k, E_loc, rank)
+    ret = np.zeros((S, T, top_k, N), dtype=np.uint16)
+    ret_mask = np.zeros((S, T, top_k), dtype=bool)
+    flat = ret.reshape(S * T * top_k, N)
+    flat[pos] = d["y"]
+    ret_mask.reshape(-1)[pos] = True
+    yp = np.asarray(y_peer, dtype=np.uint16).reshape(T, top_k, N)
+    rows = np.where(ret_mask[rank][:, :, None], ret[rank], yp)
+    out = f64_to_bf16(bf16_to_f64(rows).sum(axis=1))
+    res = dict(d)
+    res.update(ret=ret, ret_mask=ret_mask, out=out, return_pos=pos)
+    return res

@@ -79,6 +79,35 @@ def _dispatch_token_major(idx, gate, S, T, E_loc, rank=0):
     return dict(d, slot_token=d["slot_token"][o], slot_gate=d["slot_gate"][o])
 
 
+_orig_return_pos = M.moe_return_positions
+
+
+def _return_pos_k_reversed(slot_token, idx, expert_offsets, T, top_k, E_loc, rank):
+    pos = _orig_return_pos(slot_token, idx, expert_offsets, T, top_k, E_loc, rank)
+    return (pos // top_k) * top_k + (top_k - 1 - pos % top_k)
+
+
+def _combine_variant(regate=False, drop_peer=False, peer_everywhere=False):
+    def combine(x, logits, w, top_k, y_peer, rank=0):
+        r = dict(_orig_combine(x, logits, w, top_k, y_peer, rank))
+        T, N = x[0].shape[0], w.shape[2]
+        mask = r["ret_mask"][rank][:, :, None]
+        yp = np.asarray(y_peer, dtype=np.uint16).reshape(T, top_k, N)
+        if drop_peer:
+            yp = np.zeros_like(yp)
+        rows = M.bf16_to_f64(yp if peer_everywhere else np.where(mask, r["ret"][rank], yp))
+        if regate:
+            rows = rows * r["gate"][rank * T:(rank + 1) * T][:, :, None]
+        r["out"] = M.f64_to_bf16(rows.sum(axis=1))
+        return r
+    combine.__name__ = ("_combine_regates" if regate else "_combine_drops_peer_rows" if drop_peer
+                        else "_combine_peer_rows_everywhere")
+    return combine
+
+
+_orig_combine = M.moe_combine
+
+
 MUTANTS = [
     ("f64_to_bf16", _truncating_bf16, [P.test_bf16_hand_patterns]),
     ("gemm", _gemm_transposed_b, [lambda: P.test_gemm_exact_bruteforce((5, 6, 6))]),
@@ -88,6 +117,13 @@ MUTANTS = [
     ("moe_route", _route_ties_to_higher_id, [P.test_moe_golden_hand_example]),
     ("moe_route", _route_renormalised, [P.test_moe_gates_are_softmax]),
     ("moe_dispatch", _dispatch_token_major, [P.test_moe_golden_hand_example]),
+    ("moe_return_positions", _return_pos_k_reversed,
+     [P.test_moe_combine_hand_worked, P.test_moe_combine_return_is_a_permutation_of_the_slots]),
+    ("moe_combine", _combine_variant(regate=True), [P.test_moe_combine_hand_worked]),
+    ("moe_combine", _combine_variant(drop_peer=True),
+     [P.test_moe_combine_hand_worked, P.test_moe_combine_all_experts_remote_is_a_plain_sum]),
+    ("moe_combine", _combine_variant(peer_everywhere=True),
+     [P.test_moe_combine_hand_worked, P.test_moe_combine_top1_all_local_is_y_in_token_order]),
 ]
 
 

@@ -440,3 +440,75 @@ def test_generator_distributions():
     assert abs(x.std() - 0.02) < 0.001 and abs(x.mean()) < 0.001
     u = O.bf16_to_f64(I.draw_bf16(0, 2, 1, (512, 512), "uniform", 1.0))
     assert u.min() >= -1 and u.max() <= 1 and abs(u.std() - 1 / math.sqrt(3)) < 0.01
+
+
+# ---------------------------------------------------------------- MoE combine
+
+def _combine_hand():
+    g = json.load(open(os.path.join(GOLDEN, "moe_combine_hand.json")))
+    bf = lambda a: O.f64_to_bf16(np.asarray(a, dtype=np.float64))
+    x = [bf(v) for v in g["x"]]
+    logits = [np.asarray(v, dtype=np.float32) for v in g["logits"]]
+    w = bf(g["w"])
+    return g, O.moe_combine(x, logits, w, g["top_k"], bf(g["y_peer"]), rank=g["rank"])
+
+
+def test_moe_combine_hand_worked():
+    g, r = _combine_hand()
+    np.testing.assert_array_equal(r["idx"], np.asarray(g["topk_idx"]))
+    np.testing.assert_array_equal(r["slot_token"], np.asarray(g["slot_token"]))
+    np.testing.assert_array_equal(O.bf16_to_f64(r["y"]), np.asarray(g["y"]))
+    np.testing.assert_array_equal(r["return_pos"], np.asarray(g["return_pos"]))
+    np.testing.assert_array_equal(r["ret_mask"][1], np.asarray(g["ret_mask_source1"]))
+    np.testing.assert_array_equal(O.bf16_to_f64(r["ret"][1]), np.asarray(g["ret_source1"]))
+    np.testing.assert_array_equal(O.bf16_to_f64(r["out"]), np.asarray(g["out"]))
+
+
+def test_moe_combine_return_is_a_permutation_of_the_slots():
+    """Every slot returns to exactly one (source, token, k) whose top-k entry
+    is the slot's expert; no two slots share a position."""
+    S, T, H, N, E, E_loc, k, rank = 3, 40, 16, 8, 6, 2, 2, 1
+    rng = np.random.default_rng(7)
+    x = [O.f64_to_bf16(rng.standard_normal((T, H))) for _ in range(S)]
+    logits = [rng.standard_normal((T, E)).astype(np.float32) for _ in range(S)]
+    w = O.f64_to_bf16(0.1 * rng.standard_normal((E_loc, H, N)))
+    yp = O.f64_to_bf16(rng.standard_normal((T, k, N)))
+    r = O.moe_combine(x, logits, w, k, yp, rank=rank)
+    pos = r["return_pos"]
+    assert len(set(pos.tolist())) == len(pos)
+    flat_idx = r["idx"].reshape(-1)
+    exp_of = O.slot_expert(r["expert_offsets"], len(pos))
+    np.testing.assert_array_equal(flat_idx[pos], rank * E_loc + exp_of)
+    np.testing.assert_array_equal(pos // k, r["slot_token"])
+    # the mask marks exactly the (t, k) pairs of local experts
+    local = (r["idx"] >= rank * E_loc) & (r["idx"] < (rank + 1) * E_loc)
+    np.testing.assert_array_equal(r["ret_mask"].reshape(S * T, k), local)
+
+
+def test_moe_combine_all_experts_remote_is_a_plain_sum():
+    """No token picks a local expert: the combine sums the returned rows."""
+    S, T, H, N, E, E_loc, k = 2, 8, 4, 4, 4, 2, 2
+    rng = np.random.default_rng(3)
+    logits = [rng.standard_normal((T, E)).astype(np.float32) for _ in range(S)]
+    for l in logits:
+        l[:, :E_loc] -= 1000.0  # experts 0..E_loc-1 (rank 0's) are never chosen
+    x = [O.f64_to_bf16(rng.standard_normal((T, H))) for _ in range(S)]
+    w = O.f64_to_bf16(rng.standard_normal((E_loc, H, N)))
+    yp = O.f64_to_bf16(np.arange(T * k * N, dtype=np.float64).reshape(T, k, N) * 0.5 - 7.0)
+    r = O.moe_combine(x, logits, w, k, yp, rank=0)
+    assert r["n_slots"] == 0 and not r["ret_mask"].any()
+    expect = (np.arange(T * k * N, dtype=np.float64).reshape(T, k, N) * 0.5 - 7.0).sum(axis=1)
+    np.testing.assert_array_equal(O.bf16_to_f64(r["out"]), expect)
+
+
+def test_moe_combine_top1_all_local_is_y_in_token_order():
+    """top_k = 1 and every expert local: out[t] is y of t's slot, unchanged."""
+    S, T, H, N, E = 1, 24, 8, 8, 3
+    rng = np.random.default_rng(5)
+    x = [O.f64_to_bf16(rng.standard_normal((T, H)))]
+    logits = [rng.standard_normal((T, E)).astype(np.float32)]
+    w = O.f64_to_bf16(rng.standard_normal((E, H, N)))
+    r = O.moe_combine(x, logits, w, 1, np.zeros((T, 1, N), dtype=np.uint16), rank=0)
+    inv = np.empty(T, dtype=np.int64)
+    inv[r["slot_token"]] = np.arange(T)
+    np.testing.assert_array_equal(r["out"], r["y"][inv])
