@@ -174,7 +174,10 @@ def main() -> int:
     log("[bench] GEMM alone / transfer alone")
     t_gemm = float(np.median(time_calls(lambda: h.ag_gemm(shards, bt, c, ag, rank=0,
                                                           flags=mk.F_PRELANDED), reps, 3)))
-    h.set_roles(mk.OP_AG_GEMM, n_land=roles_fused[0], n_compute=0)
+    # the same landing with no compute: the fused launch's land workgroups, or
+    # its whole grid when every workgroup lands between tiles (land = 0)
+    n_land_alone = roles_fused[0] if roles_fused[0] > 0 else grid_fused
+    h.set_roles(mk.OP_AG_GEMM, n_land=n_land_alone, n_compute=0)
     t_xfer = float(np.median(time_calls(fused, reps, 3)))
     h.set_roles(mk.OP_AG_GEMM)
     t_fused_med = float(np.median(kern_ms))
@@ -196,7 +199,7 @@ def main() -> int:
             h.ag_gemm(shards_host, bt, c, ag, rank=0)
 
         t_fused_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
-        h.set_roles(mk.OP_AG_GEMM, n_land=roles_fused[0], n_compute=0)
+        h.set_roles(mk.OP_AG_GEMM, n_land=n_land_alone, n_compute=0)
         t_xfer_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
         h.set_roles(mk.OP_AG_GEMM)
         del shards_host
@@ -231,7 +234,7 @@ def main() -> int:
                      "kernel_source_hash": src_hash},
         "overlap": {
             "t_fused_ms": round(t_fused_med, 4), "t_gemm_alone_ms": round(t_gemm, 4),
-            "t_transfer_alone_ms": round(t_xfer, 4),
+            "t_transfer_alone_ms": round(t_xfer, 4), "transfer_alone_land_wgs": n_land_alone,
             "efficiency": round(max(t_gemm, t_xfer) / t_fused_med, 4),
             "gemm_alone_over_fused": round(t_gemm / t_fused_med, 4),
             "gemm_alone_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 2),
@@ -282,8 +285,10 @@ def profile_run(which, h, I, mk, to_dev, dev):
     if which == "gemm_alone":
         h.ag_gemm(shards, bt, c, ag, rank=0)      # gathers A once
         flags = mk.F_PRELANDED
-    if which == "transfer_alone":
-        h.set_roles(mk.OP_AG_GEMM, n_land=32, n_compute=0)
+    if which == "transfer_alone":                 # as the timed transfer-alone leg
+        h.ag_gemm(shards, bt, c, ag, rank=0)
+        (n_land, _, _), grid = h.last_launch(mk.OP_AG_GEMM)
+        h.set_roles(mk.OP_AG_GEMM, n_land=n_land if n_land > 0 else grid, n_compute=0)
     for _ in range(7):
         h.ag_gemm(shards, bt, c, ag, rank=0, flags=flags)
     h.sync()
@@ -363,7 +368,28 @@ def other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev):
     byts = S * T * E * 4 + 2 * n_slots * H * 2 + n_slots * H * 2 + E_loc * H * N * 2 + n_slots * N * 2
     out[name] = {"ms": round(t, 4), "n_slots": n_slots, "tflops": round(fl / (t * 1e-3) / 1e12, 2),
                  "GBps": round(byts / (t * 1e-3) / 1e9, 1), "roles": h.last_launch(mk.OP_MOE)[0]}
-    del x, lg, wt, y, idx, gate, st, eo, co, xs, d
+
+    # the same layer with the return of every remote token's rows and the combine
+    log(f"[bench] {name} + combine")
+    yp = to_dev(np.ascontiguousarray(d["y_peer"]).reshape(T * top_k, N))
+    ret = [None] + [torch.empty((T * top_k, N), dtype=torch.bfloat16, device=dev)
+                    for _ in range(S - 1)]
+    o = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+
+    def moe_combine():
+        h.moe_dispatch_gemm_combine(x, lg, wt, E, top_k, y, idx, gate, st, eo, co, xs, yp, ret, o,
+                                    rank=0)
+
+    tc = float(np.median(time_calls(moe_combine, 20, 3)))
+    own = int((st[:n_slots] < T).sum().item())  # slots of this rank's own tokens stay local
+    # extra over the dispatch: returned rows written, then the combine reads
+    # top_k rows per own token (from y or y_peer) and writes out
+    byts_c = byts + (n_slots - own) * N * 2 + T * top_k * N * 2 + T * N * 2
+    out[name + "+combine"] = {
+        "ms": round(tc, 4), "tflops": round(fl / (tc * 1e-3) / 1e12, 2),
+        "GBps": round(byts_c / (tc * 1e-3) / 1e9, 1), "combine_extra_ms": round(tc - t, 4),
+        "roles": h.last_launch(mk.OP_MOE)[0]}
+    del x, lg, wt, y, idx, gate, st, eo, co, xs, d, yp, ret, o
     torch.cuda.empty_cache()
     return out
 

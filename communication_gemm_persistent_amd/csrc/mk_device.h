@@ -50,6 +50,8 @@ struct Ctrl {
   uint32_t route_done;  uint32_t _p8[15];
   uint32_t scan_ready;  uint32_t _p9[15];
   uint32_t xq[8 * 16];  // per-XCD tile queue counters, one 64-byte line each
+  uint32_t tiles_done;  uint32_t _p10[15];
+  uint32_t combine_ctr; uint32_t _p11[15];
 };
 
 // Per-launch synchronisation state passed to every kernel.
@@ -261,6 +263,8 @@ __device__ __forceinline__ void finish_launch(const Sync &s) {
       st_relaxed(&c->route_ctr, 0u);
       st_relaxed(&c->route_done, 0u);
       for (int x = 0; x < 8; ++x) st_relaxed(&c->xq[x * 16], 0u);
+      st_relaxed(&c->tiles_done, 0u);
+      st_relaxed(&c->combine_ctr, 0u);
       if (ld_relaxed(&c->abort_epoch) == s.epoch) {
         for (uint32_t i = 0; i < s.n_flags; ++i) st_relaxed(cnt_ptr(s, i), 0u);
       }

@@ -591,13 +591,15 @@ mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const m
 
 // ---------------------------------------------------------------- MoE dispatch + grouped GEMM
 
-mk_status mk_moe_dispatch_gemm(mk_handle h, mk_stream stream, int n_src, int rank,
-                               const mk_bf16 *const *x_src, const float *const *logits_src,
-                               const mk_bf16 *wt, int T, int H, int N, int E, int E_loc,
-                               int top_k, mk_bf16 *y, int32_t *topk_idx, float *topk_gate,
-                               int32_t *slot_token, int32_t *expert_offsets,
-                               int32_t *chunk_offsets, mk_bf16 *x_slots, int cap,
-                               unsigned flags) {
+// Shared by mk_moe_dispatch_gemm and mk_moe_dispatch_gemm_combine; the
+// combine arguments are NULL for the former.
+static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
+                            const mk_bf16 *const *x_src, const float *const *logits_src,
+                            const mk_bf16 *wt, int T, int H, int N, int E, int E_loc, int top_k,
+                            mk_bf16 *y, int32_t *topk_idx, float *topk_gate, int32_t *slot_token,
+                            int32_t *expert_offsets, int32_t *chunk_offsets, mk_bf16 *x_slots,
+                            int cap, bool combine, const mk_bf16 *y_peer, mk_bf16 *const *ret,
+                            mk_bf16 *out, unsigned flags) {
   if (!h) return MK_ERR_INVALID;
   h->err.clear();
   if (n_src < 1 || n_src > MK_MAX_WORLD) return fail(h, MK_ERR_INVALID, "n_src out of range");
@@ -641,6 +643,23 @@ mk_status mk_moe_dispatch_gemm(mk_handle h, mk_stream stream, int n_src, int ran
   p.chunk_offsets = static_cast<int32_t *>(const_cast<void *>(dp));
   if ((st = resolve(h, x_slots, false, &dp, "x_slots")) != MK_OK) return st;
   p.x_slots = static_cast<uint16_t *>(const_cast<void *>(dp));
+  if (combine) {
+    if (flags & MK_F_NO_GATE) return fail(h, MK_ERR_INVALID, "the combine sums gated rows: MK_F_NO_GATE");
+    if (rank >= n_src) return fail(h, MK_ERR_INVALID, "the combine sums this rank's own tokens: rank >= n_src");
+    if (n_src > 1 && !ret) return fail(h, MK_ERR_INVALID, "ret is NULL");
+    if ((st = resolve(h, y_peer, true, &dp, "y_peer")) != MK_OK) return st;
+    p.y_peer = static_cast<const uint16_t *>(dp);
+    if ((st = resolve(h, out, true, &dp, "out")) != MK_OK) return st;
+    p.out = static_cast<uint16_t *>(const_cast<void *>(dp));
+    for (int s = 0; s < n_src; ++s) {
+      if (s == rank) continue;
+      char what[32];
+      std::snprintf(what, sizeof(what), "ret[%d]", s);
+      if ((st = resolve(h, ret[s], true, &dp, what)) != MK_OK) return st;
+      p.ret[s] = static_cast<uint16_t *>(const_cast<void *>(dp));
+    }
+    p.combine = 1;
+  }
 
   p.S = n_src;
   p.T = T;
@@ -662,13 +681,13 @@ mk_status mk_moe_dispatch_gemm(mk_handle h, mk_stream stream, int n_src, int ran
   p.tiles_n = cdiv(N, bm);
   const long max_row_tiles = cdiv(cap, bm) + E_loc;
 
-  // workspace: item_cnt, item_base, tok_rank, slot_gate, tile list
+  // workspace: item_cnt, item_base, tok_rank, slot_gate, slot_ret, tile list
   const size_t sz_items = (size_t)p.n_items * E_loc * sizeof(int32_t);
   const size_t sz_rank = (size_t)n_src * T * top_k * sizeof(int32_t);
   const size_t sz_gate = (size_t)cap * sizeof(float);
   const size_t sz_tiles = (size_t)(max_row_tiles + 2) * sizeof(int32_t);
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  const size_t total = al(sz_items) * 2 + al(sz_rank) + al(sz_gate) + al(sz_tiles);
+  const size_t total = al(sz_items) * 2 + al(sz_rank) + al(sz_gate) * 2 + al(sz_tiles);
   if ((st = ensure_ws(h, total)) != MK_OK) return st;
   char *w = static_cast<char *>(h->ws);
   p.item_cnt = reinterpret_cast<int32_t *>(w);
@@ -679,6 +698,8 @@ mk_status mk_moe_dispatch_gemm(mk_handle h, mk_stream stream, int n_src, int ran
   w += al(sz_rank);
   p.slot_gate = reinterpret_cast<float *>(w);
   w += al(sz_gate);
+  p.slot_ret = reinterpret_cast<int32_t *>(w);
+  w += al(sz_gate);
   p.tile_base = reinterpret_cast<int32_t *>(w);
 
   const int gmax = max_grid(h, MK_OP_MOE, bm);
@@ -687,7 +708,12 @@ mk_status mk_moe_dispatch_gemm(mk_handle h, mk_stream stream, int n_src, int ran
   land = std::max(1, std::min(land, 4 * gmax));  // landing cannot be switched off: compute depends on it
   int compute = r.n_compute >= 0 ? std::min(r.n_compute, 4 * gmax)
                                  : (int)std::max(1L, std::min(max_row_tiles * p.tiles_n, (long)gmax - land));
-  compute = std::max(0, compute);
+  if (combine) {
+    // Land workgroups wait for the last tile before they combine, so every
+    // workgroup must be resident at once or they could hold every slot.
+    land = std::min(land, std::max(1, gmax - 1));
+    compute = std::max(1, std::min(compute, gmax - land));
+  }
   p.n_land = land;
   p.n_compute = compute;
   const int grid = land + compute;
@@ -696,6 +722,31 @@ mk_status mk_moe_dispatch_gemm(mk_handle h, mk_stream stream, int n_src, int ran
   if (e != hipSuccess) return hip_fail(h, e, "launching the MoE dispatch kernel");
   record(h, MK_OP_MOE, land, compute, 0, grid);
   return MK_OK;
+}
+
+mk_status mk_moe_dispatch_gemm(mk_handle h, mk_stream stream, int n_src, int rank,
+                               const mk_bf16 *const *x_src, const float *const *logits_src,
+                               const mk_bf16 *wt, int T, int H, int N, int E, int E_loc,
+                               int top_k, mk_bf16 *y, int32_t *topk_idx, float *topk_gate,
+                               int32_t *slot_token, int32_t *expert_offsets,
+                               int32_t *chunk_offsets, mk_bf16 *x_slots, int cap,
+                               unsigned flags) {
+  return moe_launch(h, stream, n_src, rank, x_src, logits_src, wt, T, H, N, E, E_loc, top_k, y,
+                    topk_idx, topk_gate, slot_token, expert_offsets, chunk_offsets, x_slots, cap,
+                    false, nullptr, nullptr, nullptr, flags);
+}
+
+mk_status mk_moe_dispatch_gemm_combine(mk_handle h, mk_stream stream, int n_src, int rank,
+                                       const mk_bf16 *const *x_src, const float *const *logits_src,
+                                       const mk_bf16 *wt, int T, int H, int N, int E, int E_loc,
+                                       int top_k, mk_bf16 *y, int32_t *topk_idx, float *topk_gate,
+                                       int32_t *slot_token, int32_t *expert_offsets,
+                                       int32_t *chunk_offsets, mk_bf16 *x_slots, int cap,
+                                       const mk_bf16 *y_peer, mk_bf16 *const *ret, mk_bf16 *out,
+                                       unsigned flags) {
+  return moe_launch(h, stream, n_src, rank, x_src, logits_src, wt, T, H, N, E, E_loc, top_k, y,
+                    topk_idx, topk_gate, slot_token, expert_offsets, chunk_offsets, x_slots, cap,
+                    true, y_peer, ret, out, flags);
 }
 
 }  // extern "C"

@@ -17,6 +17,11 @@
 //   compute (compute workgroups) grouped-GEMM tiles over the expert slots; a
 //                              tile waits for the flags of the route items whose
 //                              tokens fill its rows; y = bf16(gate * acc)
+//   combine (every workgroup, when requested) each finished row also returns
+//                              to its source (ret[s] at (token, k)); once every
+//                              tile is done, this rank's tokens sum their k rows
+//                              (local experts from y, remote ones from what
+//                              their owners returned) into out
 // A route item is kRouteTokens consecutive tokens of one source rank.
 #include "mk_params.h"
 
@@ -200,6 +205,7 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, MoeS
         }
         p.slot_token[slot] = s * p.T + t;
         p.slot_gate[slot] = p.topk_gate[o + j];
+        if (p.combine) p.slot_ret[slot] = (int32_t)((size_t)(s * p.T + t) * p.top_k + j);
         const int k = atomicAdd(&sh.n_list, 1);
         sh.list_tok[k] = (slot << 8) | (int)threadIdx.x;
       }
@@ -279,18 +285,113 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
       const int slot = slot0 + p0.row;
       if (slot >= slot1) continue;
       const float gt = p.no_gate ? 1.f : p.slot_gate[slot];
+      // the row's return position in its source's combine buffer (none for this rank's tokens)
+      uint16_t *ret_row = nullptr;
+      if (p.combine) {
+        const size_t rp = (size_t)p.slot_ret[slot];
+        const size_t per_src = (size_t)p.T * p.top_k;
+        const int src = (int)(rp / per_src);
+        if (src != p.rank) ret_row = p.ret[src] + (rp - (size_t)src * per_src) * p.N;
+      }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < C::GROUPS; ++g) {
           const int col = n0 + acc_pos<BM, BN>(i, j, g).col;
           if (col >= p.N) continue;
-          const f32x16_t &v = acc[i][j];
-          float x0 = v[g * 4 + 0], x1 = v[g * 4 + 1], x2 = v[g * 4 + 2], x3 = v[g * 4 + 3];
+          const f32x4_t v = acc_group(acc[i][j], g);
+          float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
           if (!p.no_gate) { x0 *= gt; x1 *= gt; x2 *= gt; x3 *= gt; }
-          *reinterpret_cast<uint2 *>(p.y + (size_t)slot * p.N + col) = pack_bf16x4(x0, x1, x2, x3);
+          const uint2 o = pack_bf16x4(x0, x1, x2, x3);
+          *reinterpret_cast<uint2 *>(p.y + (size_t)slot * p.N + col) = o;
+          if (ret_row) *reinterpret_cast<uint2 *>(ret_row + col) = o;
         }
     }
+    if (p.combine) {  // count the finished tile for the combine (release of its rows)
+      wait_stores();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        fence_release();
+        add_relaxed(&p.sync.ctrl->tiles_done, 1u);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+
+constexpr int kCombineTokens = 16;  // tokens per combine item
+static_assert(kCombineTokens * 8 <= TileCfg<128, 128>::THREADS, "one thread per (token, k) row");
+static_assert(kCombineTokens * 8 * sizeof(void *) <= TileCfg<128, 128>::LDS_BYTES, "row table fits");
+
+// Combine tokens [c*16, c*16+16) of the local source: out[t] = bf16(sum over
+// k of row k), row k from y when the token's k-th expert is local and from
+// y_peer otherwise.  The rows' addresses go to LDS first (rows[t][k]); then
+// every thread takes 8 columns of a token and issues its top_k loads together.
+__device__ __forceinline__ void moe_combine_item(const MoeParams &p, int c, char *smem) {
+  const uint16_t **rows = reinterpret_cast<const uint16_t **>(smem);
+  const int t0 = c * kCombineTokens, nt = min(kCombineTokens, p.T - t0);
+  const int K = p.top_k;
+  const int i = (int)threadIdx.x;
+  if (i < nt * K) {
+    const int t = t0 + i / K, k = i % K;
+    const size_t o = ((size_t)p.rank * p.T + t) * K + k;
+    const int e = p.topk_idx[o] - p.rank * p.E_loc;
+    if (e >= 0 && e < p.E_loc) {
+      const int item = p.rank * p.items_per_src + t / kRouteTokens;
+      const int slot = p.item_base[(size_t)item * p.E_loc + e] + p.tok_rank[o];
+      rows[i] = p.y + (size_t)slot * p.N;
+    } else {
+      rows[i] = p.y_peer + ((size_t)t * K + k) * p.N;
+    }
+  }
+  __syncthreads();
+  const int vpr = p.N / 8;  // 16-byte vectors per row
+  for (int idx = i; idx < nt * vpr; idx += blockDim.x) {
+    const int tl = idx / vpr, cv = idx - tl * vpr;
+    u32x4_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < K) v[k] = *reinterpret_cast<const u32x4_t *>(rows[tl * K + k] + cv * 8);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k >= K) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += __uint_as_float(v[k][q] << 16);
+        acc[2 * q + 1] += __uint_as_float(v[k][q] & 0xFFFF0000u);
+      }
+    }
+    uint4 r;
+    const uint2 lo = pack_bf16x4(acc[0], acc[1], acc[2], acc[3]);
+    const uint2 hi = pack_bf16x4(acc[4], acc[5], acc[6], acc[7]);
+    r.x = lo.x; r.y = lo.y; r.z = hi.x; r.w = hi.y;
+    *reinterpret_cast<uint4 *>(p.out + (size_t)(t0 + tl) * p.N + cv * 8) = r;
+  }
+  __syncthreads();  // rows[] is rewritten by the next item
+}
+
+// Every workgroup, after its other roles: wait until every tile is done,
+// then combine token chunks of the local source until none are left.  The
+// GEMM staging area is free by then and holds the row addresses.
+__device__ __forceinline__ void moe_combine(const MoeParams &p, MoeShared &sh, char *smem) {
+  Ctrl *ctrl = p.sync.ctrl;
+  const uint32_t n_items = (uint32_t)((p.T + kCombineTokens - 1) / kCombineTokens);
+  bool waited = false;
+  for (;;) {
+    const uint32_t c = next_index(&ctrl->combine_ctr, &sh.word);
+    if (c >= n_items) break;
+    if (!waited) {
+      bool ok0 = true;
+      if (threadIdx.x == 0) {
+        const uint32_t n_tiles = (uint32_t)p.tile_base[0] * (uint32_t)p.tiles_n;
+        ok0 = spin_until_ge(p.sync, &ctrl->tiles_done, n_tiles, 0xFFFF0003u);
+      }
+      if (!wg_sync_ok(ok0, &sh.word)) break;  // full acquire: rows of every tile are visible
+      waited = true;
+    }
+    moe_combine_item(p, (int)c, smem);
   }
 }
 
@@ -346,6 +447,7 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeP
     } else if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
       moe_compute<BM, BN>(p, smem, sh);
     }
+    if (p.combine && ticket < (uint32_t)(p.n_land + p.n_compute)) moe_combine(p, sh, smem);
   }
   finish_launch(p.sync);
 }

@@ -88,6 +88,14 @@ struct MoeParams {
   int32_t *tok_rank;    // [S*T, top_k] rank of the token within (item, e); -1 if not local
   float *slot_gate;     // [cap]
   int32_t *tile_base;   // [E_loc + 1] first GEMM tile of each expert
+  int32_t *slot_ret;    // [cap] return position (s*T + t)*top_k + k of every slot (combine)
+  // combine (when `combine`): rows of this rank's experts return to ret[s]
+  // ([T, top_k, N] per source s != rank); this rank's tokens sum their rows
+  // from y (local experts) and y_peer ([T, top_k, N], remote experts) into out
+  const uint16_t *y_peer;
+  uint16_t *ret[MK_MAX_WORLD];
+  uint16_t *out;
+  int combine;
   int S, T, H, N, E, E_loc, top_k, rank, cap;
   int items_per_src, n_items;
   int n_land, n_compute;

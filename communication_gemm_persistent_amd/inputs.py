@@ -212,7 +212,7 @@ def gen_workload(name: str, variant: int = FLOAT) -> Dict[str, object]:
         return gen_ar(p["world"], p["m"], p["n"], p["k"], p["rank"], variant, wl.config_id)
     if wl.op == "moe":
         return gen_moe(p["S"], p["T"], p["H"], p["N"], p["E"], p["E_loc"], variant,
-                       wl.config_id)
+                       wl.config_id, top_k=p["top_k"])
     raise ValueError(wl.op)
 
 

@@ -39,7 +39,7 @@ MAX_WORLD = 16
 # Names declared in include/mk.h (the CPU tests check the library exports them).
 EXPORTS = ("mk_create", "mk_destroy", "mk_set_roles", "mk_get_roles", "mk_last_launch",
            "mk_sync", "mk_status_string", "mk_last_error", "mk_ag_gemm", "mk_gemm_rs",
-           "mk_gemm_ar", "mk_moe_dispatch_gemm")
+           "mk_gemm_ar", "mk_moe_dispatch_gemm", "mk_moe_dispatch_gemm_combine")
 
 
 class MkError(RuntimeError):
@@ -91,6 +91,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_gemm_ar.argtypes = [_vp, _vp, _i, _i, _vp, _vp, _pp, _vp, _pp, _i, _i, _i, _i, _u]
     lib.mk_moe_dispatch_gemm.argtypes = [_vp, _vp, _i, _i, _pp, _pp, _vp, _i, _i, _i, _i, _i, _i,
                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _u]
+    lib.mk_moe_dispatch_gemm_combine.argtypes = [
+        _vp, _vp, _i, _i, _pp, _pp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+        _i, _vp, _pp, _vp, _u]
     for name in EXPORTS:
         if name not in ("mk_status_string", "mk_last_error"):
             getattr(lib, name).restype = _i
@@ -251,3 +254,38 @@ class Handle:
             _ptr(chunk_offsets, "chunk_offsets", i32, (E_loc, S + 1)),
             _ptr(x_slots, "x_slots", _BF16, (cap, H)), cap, flags)
         self._check(st, "mk_moe_dispatch_gemm", self.h)
+
+    def moe_dispatch_gemm_combine(self, x: Sequence[torch.Tensor], logits: Sequence[torch.Tensor],
+                                  wt: torch.Tensor, E: int, top_k: int, y: torch.Tensor,
+                                  topk_idx: torch.Tensor, topk_gate: torch.Tensor,
+                                  slot_token: torch.Tensor, expert_offsets: torch.Tensor,
+                                  chunk_offsets: torch.Tensor, x_slots: torch.Tensor,
+                                  y_peer: torch.Tensor, ret: Sequence[Optional[torch.Tensor]],
+                                  out: torch.Tensor, rank: int = 0, flags: int = 0,
+                                  stream=None) -> None:
+        """Dispatch + grouped GEMM as moe_dispatch_gemm, plus the return of
+        every remote token's rows into ret[s] ([T * top_k, N]) and the combine
+        of this rank's tokens into out ([T, N])."""
+        S = len(x)
+        T, H = x[0].shape
+        E_loc, N, _ = wt.shape
+        cap = y.shape[0]
+        if len(ret) != S:
+            raise ValueError(f"ret has {len(ret)} entries, expected {S}")
+        xp = [_ptr(xx, f"x[{s}]", _BF16, (T, H)) for s, xx in enumerate(x)]
+        lp = [_ptr(ll, f"logits[{s}]", (torch.float32,), (T, E)) for s, ll in enumerate(logits)]
+        rp = [0 if s == rank else _ptr(r, f"ret[{s}]", _BF16, (T * top_k, N))
+              for s, r in enumerate(ret)]
+        i32 = (torch.int32,)
+        st = self.lib.mk_moe_dispatch_gemm_combine(
+            self.h, _vp(_stream(stream, self.device)), S, rank, _ptr_array(xp), _ptr_array(lp),
+            _ptr(wt, "wt", _BF16, (E_loc, N, H)), T, H, N, E, E_loc, top_k,
+            _ptr(y, "y", _BF16, (cap, N)), _ptr(topk_idx, "topk_idx", i32, (S * T, top_k)),
+            _ptr(topk_gate, "topk_gate", (torch.float32,), (S * T, top_k)),
+            _ptr(slot_token, "slot_token", i32, (cap,)),
+            _ptr(expert_offsets, "expert_offsets", i32, (E_loc + 1,)),
+            _ptr(chunk_offsets, "chunk_offsets", i32, (E_loc, S + 1)),
+            _ptr(x_slots, "x_slots", _BF16, (cap, H)), cap,
+            _ptr(y_peer, "y_peer", _BF16, (T * top_k, N)), _ptr_array(rp),
+            _ptr(out, "out", _BF16, (T, N)), flags)
+        self._check(st, "mk_moe_dispatch_gemm_combine", self.h)

@@ -215,6 +215,39 @@ mk_status mk_moe_dispatch_gemm(mk_handle h, mk_stream stream, int n_src, int ran
                                int32_t *chunk_offsets, mk_bf16 *x_slots, int cap,
                                unsigned flags);
 
+/*
+ * MoE dispatch + grouped GEMM + combine  [P1, row "MoE-Versand + GEMM"; the
+ * return trip is this library's reading, the pages name only the dispatch]:
+ *   everything mk_moe_dispatch_gemm does (same arguments, same outputs), and
+ *   in the same launch:
+ *   - return: every finished row y[slot] whose token came from a source
+ *     s != rank is also written to ret[s] at row (t * top_k + k), k being the
+ *     place of the slot's expert in token t's top-k list (bit-identical to
+ *     y[slot]); other rows of ret[s] are left untouched;
+ *   - combine: once every tile is done, for this rank's own tokens
+ *     out[t] = bf16(sum over k of v_k) with fp32 sums, v_k = y[slot] when
+ *     expert k of token t is local and y_peer[t * top_k + k] otherwise.
+ *
+ *   y_peer  [T * top_k, N] bf16: the rows the owners of this rank's remote
+ *           experts returned (rows of local experts are not read)
+ *   ret     host array of S pointers; ret[s] (s != rank) is source s's
+ *           return buffer, [T * top_k, N] bf16; entry [rank] ignored; may be
+ *           NULL when S == 1
+ *   out     output [T, N] bf16
+ *   rank < n_src (source `rank` holds this rank's own tokens).
+ *   MK_F_NO_GATE is rejected (MK_ERR_INVALID): the combine sums gated rows.
+ *   The grid is capped at what is resident at once, since every workgroup
+ *   waits for the last tile before it combines.
+ */
+mk_status mk_moe_dispatch_gemm_combine(mk_handle h, mk_stream stream, int n_src, int rank,
+                                       const mk_bf16 *const *x_src, const float *const *logits_src,
+                                       const mk_bf16 *wt, int T, int H, int N, int E, int E_loc,
+                                       int top_k, mk_bf16 *y, int32_t *topk_idx, float *topk_gate,
+                                       int32_t *slot_token, int32_t *expert_offsets,
+                                       int32_t *chunk_offsets, mk_bf16 *x_slots, int cap,
+                                       const mk_bf16 *y_peer, mk_bf16 *const *ret, mk_bf16 *out,
+                                       unsigned flags);
+
 #ifdef __cplusplus
 }
 #endif

@@ -356,7 +356,8 @@ def moe_return_positions(slot_token: np.ndarray, idx: np.ndarray, expert_offsets
 
 
 def moe_combine(x: Sequence[np.ndarray], logits: Sequence[np.ndarray], w: np.ndarray,
-                top_k: int, y_peer: np.ndarray, rank: int = 0) -> Dict[str, np.ndarray]:
+                top_k: int, y_peer: np.ndarray, rank: int = 0,
+                tokens: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """[P1] MoE layer of one rank: dispatch + grouped GEMM (moe_dispatch_gemm),
     then the combine of reading r10.
 
@@ -367,10 +368,17 @@ def moe_combine(x: Sequence[np.ndarray], logits: Sequence[np.ndarray], w: np.nda
     out[t] = bf16(sum over k of v_k), v_k = y[slot] when expert k of token t is
     local and y_peer[t, k] (the row its owner returned) otherwise; the gate is
     already in the rows, the sum runs over k in float64 and rounds once.
+
+    With `tokens` (a sample of this rank's token indices, for large sizes) only
+    those tokens are combined: out is [len(tokens), N], y holds the rows of the
+    slots they use (their indices in "slots"), and ret / ret_mask are not built.
     """
     S = len(x)
     T = x[0].shape[0]
     E_loc, N = w.shape[0], w.shape[2]
+    assert 0 <= rank < S, "this rank's own tokens are source `rank`"
+    if tokens is not None:
+        return _moe_combine_sampled(x, logits, w, top_k, y_peer, rank, np.asarray(tokens))
     d = moe_dispatch_gemm(x, logits, w, top_k, rank)
     pos = moe_return_positions(d["slot_token"], d["idx"], d["expert_offsets"], T, top_k, E_loc, rank)
     ret = np.zeros((S, T, top_k, N), dtype=np.uint16)
@@ -383,4 +391,30 @@ def moe_combine(x: Sequence[np.ndarray], logits: Sequence[np.ndarray], w: np.nda
     out = f64_to_bf16(bf16_to_f64(rows).sum(axis=1))
     res = dict(d)
     res.update(ret=ret, ret_mask=ret_mask, out=out, return_pos=pos)
+    return res
+
+
+def _moe_combine_sampled(x, logits, w, top_k, y_peer, rank, tokens):
+    """moe_combine restricted to some of this rank's tokens: the same steps,
+    with the expert GEMM run only on the slots those tokens use."""
+    T = x[0].shape[0]
+    E_loc, N = w.shape[0], w.shape[2]
+    d0 = moe_dispatch_gemm(x, logits, w, top_k, rank, slots=np.zeros(0, dtype=np.int64))
+    pos = moe_return_positions(d0["slot_token"], d0["idx"], d0["expert_offsets"], T, top_k,
+                               E_loc, rank)
+    want = set(int(rank * T + t) for t in tokens)
+    slots = np.array([i for i, st in enumerate(d0["slot_token"]) if int(st) in want],
+                     dtype=np.int64)
+    d = moe_dispatch_gemm(x, logits, w, top_k, rank, slots=slots)
+    yp = np.asarray(y_peer, dtype=np.uint16).reshape(T, top_k, N)
+    rows = yp[tokens].copy()                      # [n, top_k, N]
+    where = {int(pos[sl]): i for i, sl in enumerate(slots)}
+    for r, t in enumerate(tokens):
+        for k in range(top_k):
+            i = where.get(int((rank * T + t) * top_k + k))
+            if i is not None:
+                rows[r, k] = d["y"][i]
+    out = f64_to_bf16(bf16_to_f64(rows).sum(axis=1))
+    res = dict(d)
+    res.update(out=out, return_pos=pos, slots=slots)
     return res

@@ -512,3 +512,23 @@ def test_moe_combine_top1_all_local_is_y_in_token_order():
     inv = np.empty(T, dtype=np.int64)
     inv[r["slot_token"]] = np.arange(T)
     np.testing.assert_array_equal(r["out"], r["y"][inv])
+
+
+def test_moe_combine_sampled_tokens_match_the_full_combine():
+    """The sampled form (used at large sizes) gives the full form's rows for
+    the sampled tokens and multiplies only the slots they use."""
+    S, T, H, N, E, E_loc, k, rank = 3, 50, 16, 8, 8, 3, 3, 1
+    rng = np.random.default_rng(11)
+    x = [O.f64_to_bf16(rng.standard_normal((T, H))) for _ in range(S)]
+    logits = [rng.standard_normal((T, E)).astype(np.float32) for _ in range(S)]
+    w = O.f64_to_bf16(0.2 * rng.standard_normal((E_loc, H, N)))
+    yp = O.f64_to_bf16(rng.standard_normal((T, k, N)))
+    full = O.moe_combine(x, logits, w, k, yp, rank=rank)
+    toks = np.array([0, 3, 17, 31, 49])
+    part = O.moe_combine(x, logits, w, k, yp, rank=rank, tokens=toks)
+    assert 0 < len(part["slots"]) < full["n_slots"]
+    np.testing.assert_array_equal(part["out"], full["out"][toks])
+    np.testing.assert_array_equal(part["y"], full["y"][part["slots"]])
+    np.testing.assert_array_equal(part["return_pos"], full["return_pos"])
+    used = np.isin(full["slot_token"], rank * T + toks)
+    np.testing.assert_array_equal(part["slots"], np.nonzero(used)[0])
