@@ -200,25 +200,62 @@ __device__ __forceinline__ int xcd_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (kXcds - 1);
 }
 
-// Next tile of a tiles_m x tiles_n grid, as mi * tiles_n + nb, or -1 when
-// none is left (all threads get the value).  map selects the order:
+// Tile order of a tiles_m x tiles_n grid.  map selects it:
 //   kMapGlobal  one queue, m-major (every n-block of m-block 0, then 1, ...)
 //   kMapBlocks  XCD x owns m-blocks [x tiles_m / 8, (x+1) tiles_m / 8)
 //   kMapStrided XCD x owns m-blocks x, x + 8, x + 16, ...
+//   kMapRounds  the m-blocks form groups of group_m (one round of the grid in
+//               the global order, so round r still covers the same rows);
+//               each group is cut into split_m x (8 / split_m) sub-blocks and
+//               XCD x owns sub-block (x % split_m, x / split_m) of every
+//               group, the groups in order
 // With an XCD map, every owned m-block of n-block 0 comes first, then of
 // n-block 1, ..., so the tiles one XCD runs at a time share a few A and B
 // slabs in its L2 (the stride also spreads neighbouring m-blocks, which may
 // cost alike, over the XCDs); a workgroup drains its own XCD's queue first,
 // then the others in turn.
-constexpr int kMapGlobal = 0, kMapBlocks = 1, kMapStrided = 2;
-__device__ __forceinline__ int next_tile(const Sync &s, int tiles_m, int tiles_n, int xcd, int map,
-                                         uint32_t *lds_word) {
+constexpr int kMapGlobal = 0, kMapBlocks = 1, kMapStrided = 2, kMapRounds = 3;
+struct TileOrder {
+  int map;
+  int group_m;  // kMapRounds: m-blocks per group (>= 1)
+  int split_m;  // kMapRounds: 1, 2, 4 or 8
+};
+
+// Next tile as mi * tiles_n + nb, or -1 when none is left (all threads get
+// the value).
+__device__ __forceinline__ int next_tile(const Sync &s, int tiles_m, int tiles_n, int xcd,
+                                         TileOrder ord, uint32_t *lds_word) {
+  const int map = ord.map;
   __syncthreads();
   if (threadIdx.x == 0) {
     int r = -1;
     if (map == kMapGlobal) {
       const uint32_t i = add_relaxed(&s.ctrl->xq[0], 1u);
       if (i < (uint32_t)(tiles_m * tiles_n)) r = (int)i;
+    } else if (map == kMapRounds) {
+      const int G = ord.group_m, am = ord.split_m, bx = kXcds / am;
+      const int nfull = tiles_m / G, gl = tiles_m - nfull * G;  // gl: rows of the last, partial group
+      for (int k = 0; k < kXcds && r < 0; ++k) {
+        const int x = (xcd + k) & (kXcds - 1);
+        const int xa = x % am, xb = x / am;
+        const int n_lo = xb * tiles_n / bx, nc = (xb + 1) * tiles_n / bx - n_lo;
+        const int m_lo = xa * G / am, mc = (xa + 1) * G / am - m_lo;
+        const int ml_lo = xa * gl / am, mlc = (xa + 1) * gl / am - ml_lo;
+        const uint32_t cf = (uint32_t)(mc * nc);
+        const uint32_t size = (uint32_t)nfull * cf + (uint32_t)(mlc * nc);
+        uint32_t *q = &s.ctrl->xq[x * 16];
+        if (size == 0 || ld_relaxed(q) >= size) continue;
+        const uint32_t i = add_relaxed(q, 1u);
+        if (i < size) {
+          int g, j, mcc, mlo;
+          if (i < (uint32_t)nfull * cf) {
+            g = (int)(i / cf); j = (int)(i % cf); mcc = mc; mlo = m_lo;
+          } else {
+            g = nfull; j = (int)(i - (uint32_t)nfull * cf); mcc = mlc; mlo = ml_lo;
+          }
+          r = (g * G + mlo + j % mcc) * tiles_n + n_lo + j / mcc;
+        }
+      }
     } else {
       for (int k = 0; k < kXcds && r < 0; ++k) {
         const int x = (xcd + k) & (kXcds - 1);

@@ -32,7 +32,7 @@ struct mk_ctx {
   uint64_t timeout_ticks = 0;
   int force_tile = 0;  // MK_TILE env: 128 or 256 forces the tile edge
   bool no_slabs = true;   // MK_NO_SLABS=0 env: cut AllGather land blocks into K-slabs
-  int tile_map = -1;  // MK_TILE_MAP env: 0 global m-major order, 1 XCD blocks, 2 XCD strided (-1: per op)
+  int tile_map = -1;  // MK_TILE_MAP env: 0 global m-major order, 1 XCD blocks, 2 XCD strided, 3 XCD rounds (-1: per op)
   int item_kib = 256;  // MK_ITEM_KIB env: target size of one AllGather land item
   int help_every = 0;  // MK_HELP_EVERY env: 1 in this many compute workgroups helps land (0: automatic)
   int help_eager = -1;  // MK_HELP_EAGER env: helpers land until the queue is empty (-1: automatic)
@@ -158,6 +158,27 @@ int pick_tile_n(mk_ctx *h, int tiles_m, int n, int gmax) {
   return cost(224) < cost(256) ? 224 : 256;
 }
 
+// Group and sub-block shape of the kMapRounds order: a group is the m-blocks
+// one round of `grid` workgroups covers; the 8 XCDs split it into
+// split_m x (8 / split_m) sub-blocks, picked to minimise the A + B rows that
+// one XCD's tiles of a round read per K step.
+void rounds_order(int tiles_m, int tiles_n, int grid, int bm, int bn, int *group_m, int *split_m) {
+  const int G = std::max(1, std::min(tiles_m, grid / std::max(1, tiles_n)));
+  int best = 1;
+  long best_cost = -1;
+  for (int am = 1; am <= 8; am *= 2) {
+    const int bx = 8 / am;
+    const long cost = (long)cdiv(G, am) * bm + (long)cdiv(tiles_n, bx) * bn +
+                      (am > G || bx > tiles_n ? 1L << 40 : 0);  // an XCD with no tiles
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = am;
+    }
+  }
+  *group_m = G;
+  *split_m = best;
+}
+
 // Apply the user's role settings to the defaults.  `want_land` / `want_reduce`
 // are the defaults; compute fills the rest of the resident grid (capped by
 // the tile count).  Grid = the sum; at least one workgroup.
@@ -256,7 +277,7 @@ mk_status mk_create(mk_handle *out, const mk_config *cfg) {
   h->timeout_ticks = (uint64_t)khz * (uint64_t)h->timeout_ms;
   if (const char *t = std::getenv("MK_TILE")) h->force_tile = std::atoi(t);
   if (const char *t = std::getenv("MK_NO_SLABS")) h->no_slabs = std::atoi(t) != 0;
-  if (const char *t = std::getenv("MK_TILE_MAP")) h->tile_map = std::min(2, std::max(0, std::atoi(t)));
+  if (const char *t = std::getenv("MK_TILE_MAP")) h->tile_map = std::min(3, std::max(0, std::atoi(t)));
   if (const char *t = std::getenv("MK_ITEM_KIB")) h->item_kib = std::min(4096, std::max(4, std::atoi(t)));
   if (const char *t = std::getenv("MK_HELP_EVERY")) h->help_every = std::max(1, std::atoi(t));
   if (const char *t = std::getenv("MK_HELP_EAGER")) h->help_eager = std::atoi(t) != 0 ? 1 : 0;
@@ -427,7 +448,7 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   const int want_land0 = pre ? 0 : std::max(1, std::min(std::min(p.n_items, gmax / 8), 32));
   const bool fills = p.n_tiles % gmax == 0 || gmax - p.n_tiles % gmax < want_land0;
   const bool split = !pre && dynamic && fills && h->land_split > 0 && h->roles[MK_OP_AG_GEMM].n_land < 0;
-  if (split && h->tile_map < 0) p.tile_map = mk::kMapGlobal;
+  if (split && h->tile_map < 0) p.tile_map = mk::kMapRounds;
   int land = 0, compute = 0;
   choose_roles(h, MK_OP_AG_GEMM, gmax, split ? 0 : want_land0, p.n_tiles, &land, &compute);
   if (pre) land = 0;
@@ -452,9 +473,11 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
     const long room = (long)grid_all - tiles_per_chunk;
     const long first = room <= 0 ? 1 : (room + tiles_per_chunk - 1) / tiles_per_chunk;
     p.first_peers = (int)std::max(0L, std::min((long)(world - 1), first));
-    // an XCD map starts tiles of every chunk at once
-    if (p.tile_map != mk::kMapGlobal) p.first_peers = world - 1;
+    // the other XCD maps start tiles of every chunk at once; the rounds map
+    // keeps the global order's rounds
+    if (p.tile_map != mk::kMapGlobal && p.tile_map != mk::kMapRounds) p.first_peers = world - 1;
   }
+  rounds_order(p.tiles_m, p.tiles_n, grid_all, bm, bn, &p.tile_group_m, &p.tile_split_m);
   if (split) {
     p.help_eager = 1;
     p.eager_items = p.first_peers * items_per_chunk;
@@ -517,11 +540,12 @@ mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const m
   p.tiles_n = cdiv(n, bm);
   p.n_tiles = p.tiles_m * p.tiles_n;
   p.mb0 = (rank * p.ms) / bm;
-  p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapGlobal;
+  p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapRounds;
   const int gmax = max_grid(h, MK_OP_GEMM_RS, bm);
   int land = 0, compute = 0;
   choose_roles(h, MK_OP_GEMM_RS, gmax, 0, p.n_tiles, &land, &compute);
   p.n_compute = compute;
+  rounds_order(p.tiles_m, p.tiles_n, std::max(1, compute), bm, bm, &p.tile_group_m, &p.tile_split_m);
   const int grid = std::max(1, compute);
   p.sync = make_sync(h, 0);
   hipError_t e = mk::launch_rs(p, bm, grid, reinterpret_cast<hipStream_t>(stream));
@@ -581,6 +605,7 @@ mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const m
   int land = 0, compute = 0;
   choose_roles(h, MK_OP_GEMM_AR, gmax, 0, p.n_tiles, &land, &compute);
   p.n_compute = compute;
+  rounds_order(p.tiles_m, p.tiles_n, std::max(1, compute), bm, bm, &p.tile_group_m, &p.tile_split_m);
   const int grid = std::max(1, compute);
   p.sync = make_sync(h, 0);
   hipError_t e = mk::launch_ar(p, bm, grid, reinterpret_cast<hipStream_t>(stream));

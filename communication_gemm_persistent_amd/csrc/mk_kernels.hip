@@ -143,7 +143,7 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
   const int loc0 = p.rank * p.m_s, loc1 = loc0 + p.m_s;
   const int ldb = p.k * 2;
   for (;;) {
-    const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, p.tile_map, s_word);
+    const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, TileOrder{p.tile_map, p.tile_group_m, p.tile_split_m}, s_word);
     if (t < 0) break;
     const int mi = t / p.tiles_n, nb = t % p.tiles_n;
     const int mb = (mi + p.mb0) % p.tiles_m;   // local rows first, then peers in landing order
@@ -229,7 +229,7 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, char *smem, uint32
   const int xcd = xcd_id();
   const int lda = p.k * 2;
   for (;;) {
-    const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, p.tile_map, s_word);
+    const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, TileOrder{p.tile_map, p.tile_group_m, p.tile_split_m}, s_word);
     if (t < 0) break;
     const int mi = t / p.tiles_n, nb = t % p.tiles_n;
     const int mb = (mi + p.mb0) % p.tiles_m;   // own slice first: its epilogue is the heaviest
@@ -282,7 +282,7 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, char *smem, uint32
   const int xcd = xcd_id();
   const int lda = p.k * 2;
   for (;;) {
-    const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, p.tile_map, s_word);
+    const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, TileOrder{p.tile_map, p.tile_group_m, p.tile_split_m}, s_word);
     if (t < 0) break;
     const int mb = t / p.tiles_n, nb = t % p.tiles_n;
     const int m0 = mb * BM, n0 = nb * BN;

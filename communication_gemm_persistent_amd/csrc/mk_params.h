@@ -24,7 +24,7 @@ struct AgParams {
   uint16_t *ag;
   int world, rank, m_s, n, k;
   int n_land, n_compute;
-  int tiles_m, tiles_n, n_tiles, mb0, tile_map;
+  int tiles_m, tiles_n, n_tiles, mb0, tile_map, tile_group_m, tile_split_m;
   int lb_rows, blocks_per_chunk, item_rows, items_per_block, n_items, n_peer_items;
   int first_peers;
   int n_slabs, slab_k;
@@ -49,7 +49,7 @@ struct RsParams {
   uint16_t *outbox[MK_MAX_WORLD];
   int world, rank, m, n, k, ms;
   int n_compute;
-  int tiles_m, tiles_n, n_tiles, mb0, tile_map;
+  int tiles_m, tiles_n, n_tiles, mb0, tile_map, tile_group_m, tile_split_m;
 };
 
 // GEMM + AllReduce.
@@ -62,7 +62,7 @@ struct ArParams {
   uint16_t *bcast[MK_MAX_WORLD];
   int world, rank, n_bcast, m, n, k;
   int n_compute;
-  int tiles_m, tiles_n, n_tiles, tile_map;
+  int tiles_m, tiles_n, n_tiles, tile_map, tile_group_m, tile_split_m;
 };
 
 // MoE dispatch + grouped GEMM.  Route items are blocks of kRouteTokens

@@ -227,7 +227,9 @@ def test_ag_gemm_k_slabs_roles(handle256, mk, roles, static):
                                    dict(MK_NO_SLABS="0", MK_ITEM_KIB="32", MK_HELP_EVERY="3"),
                                    dict(MK_HELP_EAGER="1", MK_TILE="224", MK_LAND_SPLIT="0"),
                                    dict(MK_HELP_EAGER="0", MK_HELP_EVERY="1", MK_ROLES="0"),
-                                   dict(MK_LAND_SPLIT="1", MK_TILE="224", MK_ITEM_KIB="64")])
+                                   dict(MK_LAND_SPLIT="1", MK_TILE="224", MK_ITEM_KIB="64"),
+                                   dict(MK_TILE_MAP="3"),
+                                   dict(MK_TILE_MAP="3", MK_NO_SLABS="0", MK_LAND_SPLIT="0")])
 def test_ag_gemm_schedule_knobs(mk, knobs):
     """Tile orders, slab landing, item sizes and helper counts change only the
     schedule, never the bits."""
@@ -238,6 +240,26 @@ def test_ag_gemm_schedule_knobs(mk, knobs):
             W, rank, m_s, n, k = shape
             d = I.gen_ag(W, m_s, n, k, I.INTEGER, config=280 + W)
             c, ag = run_ag(h, d, rank=rank)
+            check_full(d, c, ag, exact=True)
+    finally:
+        h.close()
+
+
+@pytest.mark.parametrize("tile_map", [None, "0", "2"])
+def test_ag_gemm_split_landing_tile_orders(mk, tile_map):
+    """Tile grids that fill whole rounds of the grid take the split landing
+    schedule (no dedicated land workgroups); with the default rounds order,
+    the global order and an XCD-strided order every tile is computed once and
+    the bits match the oracle (exact and ragged shard heights)."""
+    print(f"ag split landing tile_map={tile_map}", flush=True)
+    h = _handle_with_env(mk, **({} if tile_map is None else dict(MK_TILE_MAP=tile_map)))
+    try:
+        for shape in [(4, 1, 1024, 3584, 2048), (8, 3, 1000, 3584, 1024)]:
+            W, rank, m_s, n, k = shape
+            d = I.gen_ag(W, m_s, n, k, I.INTEGER, config=290 + W)
+            c, ag = run_ag(h, d, rank=rank)
+            (n_land, n_compute, _), grid = h.last_launch(mk.OP_AG_GEMM)
+            assert n_land == 0 and n_compute == grid, (n_land, n_compute, grid)
             check_full(d, c, ag, exact=True)
     finally:
         h.close()

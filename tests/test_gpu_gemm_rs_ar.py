@@ -182,7 +182,7 @@ def test_gemm_ar_w8_full_size_sampled(handle, variant):
         O.assert_close_bf16(c[rows], ref, "rows")
 
 
-@pytest.mark.parametrize("tile_map", ["1", "2"])
+@pytest.mark.parametrize("tile_map", ["1", "2", "3"])
 def test_rs_ar_tile_orders(mk, tile_map):
     """The per-XCD tile orders hand out every tile exactly once (RS and AR at
     shapes with ragged tile grids)."""
