@@ -522,8 +522,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // the compiler does not treat every later LDS read as aliasing the DMA (it
 // would wait for the prefetch before each read); completion is waited for
 // explicitly with wait_vmcnt.
+//
+// The compiler's hazard checks do not look at the operands of inline
+// assembly.  An LDS DMA needs 1 wait state after an SALU write of M0, which
+// the asm's s_nop 0 provides.  A vector memory instruction that reads an
+// SGPR written by a VALU instruction (for instance a descriptor reloaded from
+// a spill with v_readlane) needs 5; the library's build is checked for that
+// pattern instead (an s_nop 4 here slows the MFMA stream the DMAs are
+// interleaved with).
 __device__ __forceinline__ void dma16(i32x4_t vdesc, uint32_t m0_base, uint32_t voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(vdesc), "{m0}"(m0_base)
                : "memory");
@@ -531,7 +539,7 @@ __device__ __forceinline__ void dma16(i32x4_t vdesc, uint32_t m0_base, uint32_t 
 
 // One 4-byte-per-lane global->LDS DMA (lane l's word lands at m0_base + 4 l).
 __device__ __forceinline__ void dma4(i32x4_t vdesc, uint32_t m0_base, uint32_t voff) {
-  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(vdesc), "{m0}"(m0_base)
                : "memory");

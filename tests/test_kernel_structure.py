@@ -2,8 +2,10 @@
 
 Every workgroup-wide barrier must execute in control flow that all lanes
 follow together; a barrier inside a loop whose exit is exec-masked deadlocks
-the workgroup.  The check also requires the checker to flag a known-bad
-variant, so a silent checker cannot pass.
+the workgroup.  No global->LDS DMA (inline assembly, outside the compiler's
+hazard checks) may read a descriptor SGPR that a VALU instruction wrote
+fewer than 5 wait states before.  Each checker must also flag known-bad
+input, so a silent checker cannot pass.
 """
 import os
 import shutil
@@ -12,6 +14,7 @@ import subprocess
 import pytest
 
 from tests.asm_barrier_check import check_file
+from tests.asm_hazard_check import check_file as check_hazards
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "communication_gemm_persistent_amd", "csrc")
@@ -51,3 +54,41 @@ def test_checker_flags_merged_single_thread_regions(tmp_path):
     (src / "mk_device.h").write_text(dev)
     assert check_file(_asm(str(src), "mk_kernels.hip", str(tmp_path))), \
         "checker missed the known-bad variant"
+
+
+@pytest.mark.parametrize("name", ["mk_kernels.hip", "mk_moe.hip"])
+def test_no_sgpr_hazard_at_lds_dma(tmp_path, name):
+    bad = check_hazards(_asm(CSRC, name, str(tmp_path)))
+    assert not bad, f"LDS DMAs reading a VALU-written SGPR too early: {bad[:5]}"
+
+
+_HAZARD_ASM = """_Z1kv:
+\tv_readlane_b32 s0, v250, 33
+\tv_readlane_b32 s3, v250, 36
+{between}\tbuffer_load_dwordx4 v32, s[0:3], 0 offen lds
+\ts_endpgm
+.Lfunc_end0:
+"""
+
+
+@pytest.mark.parametrize("between,flagged", [
+    ("", True),                                             # descriptor read right after v_readlane
+    ("\ts_mov_b32 m0, s5\n\ts_add_i32 s6, s6, 1\n", True),  # 2 wait states are not 5
+    ("\ts_nop 4\n", False),                                 # the DMA helpers' own wait states
+    ("\ts_add_i32 s6, s6, 1\n" * 5, False),                  # 5 other instructions
+])
+def test_hazard_checker_on_known_sequences(tmp_path, between, flagged):
+    """The checker itself: a VALU write of a descriptor SGPR fewer than 5 wait
+    states before an LDS DMA is flagged, and only then."""
+    f = tmp_path / "k.s"
+    f.write_text(_HAZARD_ASM.format(between=between))
+    assert bool(check_hazards(str(f))) == flagged
+
+
+def test_hazard_checker_sees_scalar_offsets(tmp_path):
+    """A DMA's scalar offset written by a VALU instruction (v_readfirstlane)
+    right before it is the same hazard as a descriptor."""
+    f = tmp_path / "k.s"
+    f.write_text("_Z1kv:\n\tv_readfirstlane_b32 s7, v3\n"
+                 "\tbuffer_load_dwordx4 v32, s[8:11], s7 offen lds\n\ts_endpgm\n.Lfunc_end0:\n")
+    assert check_hazards(str(f))
