@@ -108,6 +108,8 @@ class Workload:
             if n_slots is None:
                 raise ValueError("MoE work depends on the routed slot count")
             return 2.0 * n_slots * p["H"] * p["N"]
+        if self.op == "ring_attn":  # Q K^T and P V over every rank's keys
+            return 4.0 * p["B"] * p["H"] * p["S_q"] * p["world"] * p["S_kv"] * p["D"]
         raise ValueError(self.op)
 
 
@@ -133,6 +135,11 @@ CONFIGS: Dict[str, Workload] = {
     "moe_s8_t4096_h4096_n1536_e64": Workload(
         "moe_s8_t4096_h4096_n1536_e64", "moe", 4,
         dict(S=8, T=4096, H=4096, N=1536, E=64, E_loc=8, top_k=2, rank=0)),
+    # Ring attention (the pages give no shape): a 32768-token sequence over 8
+    # ranks, 4096 local queries and 4096 keys per block, 32 heads of 128.
+    "ring_attn_w8_h32_s4096_d128": Workload(
+        "ring_attn_w8_h32_s4096_d128", "ring_attn", 5,
+        dict(world=8, rank=0, B=1, H=32, S_q=4096, S_kv=4096, D=128)),
 }
 
 
@@ -200,6 +207,17 @@ def gen_moe(S: int, T: int, H: int, N: int, E: int, E_loc: int, variant: int = F
     return dict(x=xs, logits=logits, w=w, y_peer=y_peer)
 
 
+def gen_ring(W: int, B: int, H: int, S_q: int, S_kv: int, D: int, config: int = 5,
+             scale: float = 1.0) -> Dict[str, object]:
+    """Ring attention inputs: 0 = queries q [B,H,S_q,D] bf16, 1..W = keys of
+    rank r (k_src[r]) [B,H,S_kv,D], W+1..2W = values of rank r; all N(0, scale).
+    Only the float variant exists: softmax weights are never exact."""
+    q = draw_bf16(FLOAT, config, 0, (B, H, S_q, D), "normal", scale)
+    ks = [draw_bf16(FLOAT, config, 1 + r, (B, H, S_kv, D), "normal", scale) for r in range(W)]
+    vs = [draw_bf16(FLOAT, config, 1 + W + r, (B, H, S_kv, D), "normal", scale) for r in range(W)]
+    return dict(q=q, k=ks, v=vs)
+
+
 def gen_workload(name: str, variant: int = FLOAT) -> Dict[str, object]:
     wl = CONFIGS[name]
     p = wl.params
@@ -213,6 +231,8 @@ def gen_workload(name: str, variant: int = FLOAT) -> Dict[str, object]:
     if wl.op == "moe":
         return gen_moe(p["S"], p["T"], p["H"], p["N"], p["E"], p["E_loc"], variant,
                        wl.config_id, top_k=p["top_k"])
+    if wl.op == "ring_attn":
+        return gen_ring(p["world"], p["B"], p["H"], p["S_q"], p["S_kv"], p["D"], wl.config_id)
     raise ValueError(wl.op)
 
 

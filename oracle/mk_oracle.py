@@ -41,6 +41,13 @@ Readings of points the pages leave open (each also listed in the design notes):
       rank's experts returns to its source at (token, k), k being the
       expert's place in the token's top-k list; a source's combined row is
       the bf16 of the sum over k of its returned rows (gates already applied).
+* r11 (ring attention; the pages give one sentence) the local queries attend
+      to the keys and values of every rank's block: full (non-causal)
+      softmax attention over their concatenation, scores scaled by a given
+      factor (1/sqrt(D) by default); block s of the ring is the one that
+      started on rank (rank - s) mod W; the order affects rounding only.
+      Outputs: o = bf16(softmax(Q K^T scale) V) and the log of each row's
+      softmax denominator, lse = max + log(sum exp(s - max)), unrounded.
 
 Parity is pinned (tests marked "not gpu"): bf16 rounding by exhaustive and
 brute-force nearest-value search; the GEMM by exact rational brute force on
@@ -48,8 +55,11 @@ tiny shapes and by identity / unit-vector special cases; the gather order by
 B = I; ReduceScatter by a W-rank emulation whose slices must tile the full
 sum; AllReduce by its equivalence to ReduceScatter followed by a gather; MoE
 routing by a brute-force sort and the dispatch permutation by its inverse;
-the MoE combine by its return permutation and exact-gate examples; and
-hand-worked examples under tests/golden.
+the MoE combine by its return permutation and exact-gate examples; ring
+attention by closed forms (zero queries, equal values, one key), the
+invariance of the result to the ring order and to splitting heads, the
+scale acting as a factor on the queries; and hand-worked examples under
+tests/golden.
 """
 from __future__ import annotations
 
@@ -418,3 +428,53 @@ def _moe_combine_sampled(x, logits, w, top_k, y_peer, rank, tokens):
     res = dict(d)
     res.update(out=out, return_pos=pos, slots=slots)
     return res
+
+
+# --------------------------------------------------------------------------
+# Ring attention
+# --------------------------------------------------------------------------
+
+
+def ring_order(world: int, rank: int) -> List[int]:
+    """[P1] ring attention row: at step s a rank holds the KV block that
+    started on rank (rank - s) mod W, the previous step's block having moved
+    one rank along the ring (reading r11)."""
+    return [(rank - s) % world for s in range(world)]
+
+
+def ring_attention(q: np.ndarray, k_src: Sequence[np.ndarray], v_src: Sequence[np.ndarray],
+                   rank: int = 0, scale: Optional[float] = None,
+                   rows: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """[P1] table "Die fuenf verschmolzenen Kerne", ring attention row:
+    sequence-parallel attention of this rank's queries over every rank's
+    keys and values, the blocks taken in ring order (reading r11).
+
+    q: [B, H, S_q, D] bf16; k_src, v_src: W arrays [B, H, S_kv, D] bf16 (block
+    of rank r).  scale defaults to 1/sqrt(D).  rows (optional) restricts the
+    queries to those row indices (for sampled checks at large sizes).
+    Returns o [B, H, R, D] bf16, o_f64 (unrounded), lse [B, H, R] float64, the
+    ring order, and k_recv / v_recv [W, B, H, S_kv, D]: every block by source
+    rank, as landed.
+    """
+    W = len(k_src)
+    B, H, S_q, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    order = ring_order(W, rank)
+    sel = np.arange(S_q) if rows is None else np.asarray(rows)
+    o = np.zeros((B, H, len(sel), D))
+    lse = np.zeros((B, H, len(sel)))
+    for b in range(B):
+        for h in range(H):
+            k = np.concatenate([bf16_to_f64(np.asarray(k_src[r])[b, h]) for r in order], axis=0)
+            v = np.concatenate([bf16_to_f64(np.asarray(v_src[r])[b, h]) for r in order], axis=0)
+            qq = bf16_to_f64(np.asarray(q)[b, h][sel])
+            s = (qq @ k.T) * float(scale)                 # [R, S_total]
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            den = p.sum(axis=1, keepdims=True)
+            o[b, h] = (p @ v) / den
+            lse[b, h] = (m + np.log(den))[:, 0]
+    return dict(o=f64_to_bf16(o), o_f64=o, lse=lse, order=np.array(order),
+                k_recv=np.stack([np.asarray(x, dtype=np.uint16) for x in k_src]),
+                v_recv=np.stack([np.asarray(x, dtype=np.uint16) for x in v_src]))

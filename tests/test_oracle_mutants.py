@@ -108,6 +108,43 @@ def _combine_variant(regate=False, drop_peer=False, peer_everywhere=False):
 _orig_combine = M.moe_combine
 
 
+
+def _ring_variant(kind):
+    """ring_attention with one plausible mistake: 'noscale' ignores the scale,
+    'qaxis' normalises over the queries, 'local' sees only the rank's own
+    block, 'log2' reports lse in base 2, 'vorder' pairs keys in ring order
+    with values in rank order."""
+    def ring(q, k_src, v_src, rank=0, scale=None, rows=None):
+        W = len(k_src)
+        B, H, S_q, D = q.shape
+        sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+        if kind == "noscale":
+            sc = 1.0
+        order = M.ring_order(W, rank)
+        korder = [rank] if kind == "local" else order
+        vorder = list(range(W)) if kind == "vorder" else korder
+        sel = np.arange(S_q) if rows is None else np.asarray(rows)
+        o = np.zeros((B, H, len(sel), D))
+        lse = np.zeros((B, H, len(sel)))
+        for b in range(B):
+            for h in range(H):
+                k = np.concatenate([M.bf16_to_f64(np.asarray(k_src[r])[b, h]) for r in korder])
+                v = np.concatenate([M.bf16_to_f64(np.asarray(v_src[r])[b, h]) for r in vorder])
+                sq = (M.bf16_to_f64(np.asarray(q)[b, h][sel]) @ k.T) * sc
+                ax = 0 if kind == "qaxis" else 1
+                m = sq.max(axis=ax, keepdims=True)
+                pr = np.exp(sq - m)
+                den = pr.sum(axis=ax, keepdims=True)
+                o[b, h] = (pr / den) @ v
+                l = (m + np.log(den))
+                l = l[:, 0] if ax == 1 else np.broadcast_to(l, sq.shape)[:, 0]
+                lse[b, h] = l / np.log(2.0) if kind == "log2" else l
+        return dict(o=M.f64_to_bf16(o), o_f64=o, lse=lse, order=np.array(order),
+                    k_recv=np.stack(k_src), v_recv=np.stack(v_src))
+    ring.__name__ = f"_ring_{kind}"
+    return ring
+
+
 MUTANTS = [
     ("f64_to_bf16", _truncating_bf16, [P.test_bf16_hand_patterns]),
     ("gemm", _gemm_transposed_b, [lambda: P.test_gemm_exact_bruteforce((5, 6, 6))]),
@@ -124,6 +161,12 @@ MUTANTS = [
      [P.test_moe_combine_hand_worked, P.test_moe_combine_all_experts_remote_is_a_plain_sum]),
     ("moe_combine", _combine_variant(peer_everywhere=True),
      [P.test_moe_combine_hand_worked, P.test_moe_combine_top1_all_local_is_y_in_token_order]),
+    ("ring_attention", _ring_variant("noscale"), [lambda: P.test_ring_attention_hand_worked(0)]),
+    ("ring_attention", _ring_variant("qaxis"), [lambda: P.test_ring_attention_hand_worked(0)]),
+    ("ring_attention", _ring_variant("local"),
+     [lambda: P.test_ring_attention_hand_worked(0), P.test_ring_attention_zero_queries_average_the_values]),
+    ("ring_attention", _ring_variant("log2"), [P.test_ring_attention_single_key_is_its_value]),
+    ("ring_attention", _ring_variant("vorder"), [lambda: P.test_ring_attention_hand_worked(1)]),
 ]
 
 

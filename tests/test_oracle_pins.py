@@ -532,3 +532,110 @@ def test_moe_combine_sampled_tokens_match_the_full_combine():
     np.testing.assert_array_equal(part["return_pos"], full["return_pos"])
     used = np.isin(full["slot_token"], rank * T + toks)
     np.testing.assert_array_equal(part["slots"], np.nonzero(used)[0])
+
+
+# ---------------------------------------------------------------- ring attention
+
+def _bf(a):
+    return O.f64_to_bf16(np.asarray(a, dtype=np.float64))
+
+
+def _ring_hand():
+    g = json.load(open(os.path.join(GOLDEN, "ring_attention_hand.json")))
+    q = _bf(g["q"])
+    ks = [_bf(k) for k in g["k_src"]]
+    vs = [_bf(v) for v in g["v_src"]]
+    return g, q, ks, vs
+
+
+@pytest.mark.parametrize("rank", [0, 1])
+def test_ring_attention_hand_worked(rank):
+    g, q, ks, vs = _ring_hand()
+    r = O.ring_attention(q, ks, vs, rank=rank, scale=g["scale"])
+    np.testing.assert_allclose(r["o_f64"], np.asarray(g["o"]), rtol=1e-12, atol=1e-15)
+    np.testing.assert_array_equal(r["o"], _bf(g["o"]))
+    np.testing.assert_allclose(r["lse"], np.asarray(g["lse"]), rtol=1e-12)
+    np.testing.assert_array_equal(r["order"], g[f"order_rank{rank}"])
+
+
+def _ring_random(seed, W=3, B=2, H=2, S_q=5, S_kv=4, D=8):
+    rng = np.random.default_rng(seed)
+    q = _bf(rng.standard_normal((B, H, S_q, D)))
+    ks = [_bf(rng.standard_normal((B, H, S_kv, D))) for _ in range(W)]
+    vs = [_bf(rng.standard_normal((B, H, S_kv, D))) for _ in range(W)]
+    return q, ks, vs
+
+
+def test_ring_attention_zero_queries_average_the_values():
+    """Q = 0: every score is 0, the weights are uniform over all W * S_kv keys,
+    o is the mean of every value row and lse = log(W * S_kv)."""
+    q, ks, vs = _ring_random(1)
+    q = np.zeros_like(q)
+    r = O.ring_attention(q, ks, vs, rank=2)
+    allv = np.concatenate([O.bf16_to_f64(v) for v in vs], axis=2)      # [B, H, W*S_kv, D]
+    mean = allv.mean(axis=2, keepdims=True)
+    np.testing.assert_allclose(r["o_f64"], np.broadcast_to(mean, r["o_f64"].shape), atol=1e-14)
+    np.testing.assert_allclose(r["lse"], np.log(3 * 4), rtol=1e-14)
+
+
+def test_ring_attention_equal_values_pass_through():
+    """Every value row equal to u: the output is u whatever the scores."""
+    q, ks, vs = _ring_random(2)
+    u = _bf(np.linspace(-2, 3, 8))
+    vs = [np.broadcast_to(u, v.shape).copy() for v in vs]
+    r = O.ring_attention(q, ks, vs, rank=0)
+    np.testing.assert_array_equal(r["o"], np.broadcast_to(u, r["o"].shape))
+
+
+def test_ring_attention_single_key_is_its_value():
+    """One rank, one key: the softmax weight is 1, o = v and lse = scale q.k."""
+    q, ks, vs = _ring_random(3, W=1, S_kv=1)
+    r = O.ring_attention(q, ks, vs, rank=0, scale=0.75)
+    np.testing.assert_array_equal(r["o"], np.broadcast_to(vs[0], r["o"].shape))
+    qk = (O.bf16_to_f64(q) * O.bf16_to_f64(ks[0])).sum(axis=-1)
+    np.testing.assert_allclose(r["lse"], 0.75 * qk, rtol=1e-13, atol=1e-13)
+
+
+def test_ring_attention_order_and_head_split_invariance():
+    """The ring order permutes (key, value) pairs only: every rank order gives
+    the same result; heads and batches are independent problems."""
+    q, ks, vs = _ring_random(4)
+    base = O.ring_attention(q, ks, vs, rank=0)
+    for rank in (1, 2):
+        r = O.ring_attention(q, ks, vs, rank=rank)
+        assert r["order"][0] == rank
+        np.testing.assert_allclose(r["o_f64"], base["o_f64"], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(r["lse"], base["lse"], rtol=1e-13)
+    one = O.ring_attention(q[1:2, 1:2], [k[1:2, 1:2] for k in ks], [v[1:2, 1:2] for v in vs])
+    np.testing.assert_allclose(one["o_f64"][0, 0], base["o_f64"][1, 1], rtol=1e-12, atol=1e-14)
+
+
+def test_ring_attention_scale_acts_on_the_queries():
+    """scale c on Q equals scale 1 on c Q (c a power of two keeps Q exact)."""
+    q, ks, vs = _ring_random(5)
+    a = O.ring_attention(q, ks, vs, rank=1, scale=0.25)
+    q4 = _bf(O.bf16_to_f64(q) * 0.25)
+    b = O.ring_attention(q4, ks, vs, rank=1, scale=1.0)
+    np.testing.assert_allclose(a["o_f64"], b["o_f64"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(a["lse"], b["lse"], rtol=1e-13)
+
+
+def test_ring_attention_rows_subset_matches_full():
+    q, ks, vs = _ring_random(6)
+    full = O.ring_attention(q, ks, vs, rank=1)
+    rows = np.array([0, 3, 4])
+    part = O.ring_attention(q, ks, vs, rank=1, rows=rows)
+    np.testing.assert_array_equal(part["o"], full["o"][:, :, rows])
+    np.testing.assert_allclose(part["lse"], full["lse"][:, :, rows], rtol=1e-15)
+
+
+def test_ring_attention_peaked_scores_select_one_value():
+    """One key scores far above the rest (120 against 0): o is its value to
+    within exp(-120) relative."""
+    q, ks, vs = _ring_random(7, W=2, B=1, H=1, S_q=1, S_kv=3, D=4)
+    q = _bf([[[[8.0, 0, 0, 0]]]])
+    ks = [np.zeros_like(k) for k in ks]
+    ks[1] = ks[1].copy()
+    ks[1][0, 0, 2] = _bf([15.0, 0, 0, 0])
+    r = O.ring_attention(q, ks, vs, rank=0, scale=1.0)
+    np.testing.assert_allclose(r["o_f64"][0, 0, 0], O.bf16_to_f64(vs[1][0, 0, 2]), atol=1e-20)
