@@ -1,0 +1,344 @@
+// Persistent fused ring attention: the ring KV exchange and a
+// FlashAttention-style online-softmax attention in one launch.
+//
+// [P1] German article on mKernel (chatgpz.de), table "Die fuenf
+// verschmolzenen Kerne", ring attention row: sequence-parallel attention in
+// which, at every step, a KV block moves one rank along the ring while the
+// local attention consumes the block received before; compute and the ring
+// transfer run at the same time inside one persistent kernel.
+//
+// Roles (atomic tickets):
+//   land     copies every rank's KV block into this rank's receive buffers in
+//            ring order (at step s the block of rank (rank - s) mod W), a
+//            chunk of keys at a time: K as it is, V transposed (keys
+//            contiguous, the layout the P V product reads); then releases
+//            the chunk's flag.  Land workgroups run tasks when done.
+//   compute  takes (batch*head, 128-query tile) tasks.  For every ring step
+//            and every 64-key tile of that step's block it waits for the
+//            tile's chunk, stages K and V^T in LDS (DMA, double-buffered) and
+//            runs S = Q K^T, the online softmax and O += P V on the matrix
+//            cores; O is divided by the softmax denominator at the end and
+//            stored with each row's log-sum-exp.
+//
+// Every wave owns 32 query rows (two 16-row blocks) and all 128 columns of
+// the head.  S comes out of the 16x16x32 MFMA with each lane holding 4
+// consecutive keys of one query row; the P V product takes P from those
+// registers directly: within every 32-key step, lane group g supplies keys
+// 4g..4g+3 and 16+4g..16+4g+3 as its 8 K slots, and V^T is read from LDS in
+// the same slot order, so the sum over K slots is the sum over keys.
+#include "mk_params.h"
+
+namespace mk {
+
+constexpr int kAttnQ = 128;        // query rows per task
+constexpr int kAttnKT = 64;        // keys per tile
+constexpr int kAttnThreads = 256;  // 4 waves
+// LDS stage: the K tile as two halves [64 keys x 64 d] (8 KB each), then the
+// V^T tile [128 d x 64 keys] (16 KB); 128-byte rows whose 16-byte chunks are
+// XOR-swizzled by (row >> 1) & 7, as in the GEMM tiles.
+constexpr int kAttnKHalf = kAttnKT * 128;
+constexpr int kAttnVOff = 2 * kAttnKHalf;
+constexpr int kAttnStage = kAttnVOff + kAttnD * 128;
+constexpr int kAttnLds = 2 * kAttnStage;
+// land transpose tile: [128 d][64 keys] with a 132-byte pitch
+constexpr int kAttnTPitch = 132;
+static_assert(kAttnD * kAttnTPitch <= kAttnLds, "transpose tile fits the staging area");
+static_assert(kAttnD == 128, "the task layout assumes 128-wide heads");
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- land
+
+// Land item i: ring step s = i / (BH * chunks), source rank (rank - s) mod W,
+// then (batch*head, chunk).  Returns the flag index of the chunk.
+__device__ __forceinline__ uint32_t attn_flag(const AttnParams &p, int src, int bh, int c) {
+  return (uint32_t)((src * p.BH + bh) * p.chunks + c);
+}
+
+__device__ __forceinline__ void attn_land_item(const AttnParams &p, int item, char *smem) {
+  const int per_step = p.BH * p.chunks;
+  const int s = item / per_step, rem = item % per_step;
+  const int src = (p.rank - s + p.world) % p.world;
+  const int bh = rem / p.chunks, c = rem % p.chunks;
+  const int key0 = c * p.chunk_keys, nk = min(p.chunk_keys, p.S_kv - key0);
+  const int tid = threadIdx.x;
+  // K: the chunk's rows are contiguous in both buffers
+  {
+    const u32x4_t *sp = reinterpret_cast<const u32x4_t *>(p.k_src[src] + ((size_t)bh * p.S_kv + key0) * kAttnD);
+    u32x4_t *dp = reinterpret_cast<u32x4_t *>(p.k_recv + (((size_t)src * p.BH + bh) * p.S_kv + key0) * kAttnD);
+    const int n16 = nk * (kAttnD / 8);
+    int i = tid;
+    for (; i + 3 * kAttnThreads < n16; i += 4 * kAttnThreads) {
+      const u32x4_t a0 = sp[i], a1 = sp[i + kAttnThreads], a2 = sp[i + 2 * kAttnThreads],
+                    a3 = sp[i + 3 * kAttnThreads];
+      dp[i] = a0; dp[i + kAttnThreads] = a1; dp[i + 2 * kAttnThreads] = a2; dp[i + 3 * kAttnThreads] = a3;
+    }
+    for (; i < n16; i += kAttnThreads) dp[i] = sp[i];
+  }
+  // V: transposed through LDS, 64 keys at a time
+  const uint16_t *vsrc = p.v_src[src] + (size_t)bh * p.S_kv * kAttnD;
+  uint16_t *vdst = p.vt_recv + ((size_t)src * p.BH + bh) * kAttnD * p.S_kv;
+  for (int k0 = key0; k0 < key0 + nk; k0 += kAttnKT) {
+    // read: 16 lanes per key row (coalesced), 8 d values each
+    for (int i = tid; i < kAttnKT * 16; i += kAttnThreads) {
+      const int key = i >> 4, dc = i & 15;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(vsrc + (size_t)(k0 + key) * kAttnD + dc * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<uint16_t *>(smem + (dc * 8 + 2 * q) * kAttnTPitch + key * 2) = (uint16_t)v[q];
+        *reinterpret_cast<uint16_t *>(smem + (dc * 8 + 2 * q + 1) * kAttnTPitch + key * 2) =
+            (uint16_t)(v[q] >> 16);
+      }
+    }
+    __syncthreads();
+    // write: one 16-byte piece (8 keys) of a V^T row per item
+    for (int i = tid; i < kAttnD * (kAttnKT / 8); i += kAttnThreads) {
+      const int d = i >> 3, kc = i & 7;
+      const uint32_t *l = reinterpret_cast<const uint32_t *>(smem + d * kAttnTPitch + kc * 16);
+      u32x4_t w;
+      w[0] = l[0]; w[1] = l[1]; w[2] = l[2]; w[3] = l[3];
+      *reinterpret_cast<u32x4_t *>(vdst + (size_t)d * p.S_kv + k0 + kc * 8) = w;
+    }
+    __syncthreads();
+  }
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) st_release(flag_ptr(p.sync, attn_flag(p, src, bh, c)), p.sync.epoch);
+}
+
+// ---------------------------------------------------------------- compute
+
+__device__ __forceinline__ float xor_max(float v, int m) {
+  return fmaxf(v, __shfl_xor(v, m, 64));
+}
+__device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
+
+// Two 8-byte LDS reads as one 8-value fragment (K slots 0..3, 4..7).
+__device__ __forceinline__ bf16x8_t lds_pair(const char *a, const char *b) {
+  const bf16x4_t lo = *reinterpret_cast<const bf16x4_t *>(a);
+  const bf16x4_t hi = *reinterpret_cast<const bf16x4_t *>(b);
+  return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ bf16x8_t pack_p(const f32x4_t &a, const f32x4_t &b) {
+  const uint2 lo = pack_bf16x4(a[0], a[1], a[2], a[3]);
+  const uint2 hi = pack_bf16x4(b[0], b[1], b[2], b[3]);
+  u32x4_t w;
+  w[0] = lo.x; w[1] = lo.y; w[2] = hi.x; w[3] = hi.y;
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+__device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, const f32x4_t &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One task: query tile qt of batch*head bh over every block of the ring.
+__device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, char *smem,
+                                          uint32_t *s_word) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int row0 = qt * kAttnQ + wave * 32;  // this wave's first query row
+  const int tpb = p.S_kv / kAttnKT;          // tiles per block
+  const int n_tiles = p.world * tpb;
+  const uint32_t base = lds_addr(smem);
+  const int ldk = kAttnD * 2, ldv = p.S_kv * 2;
+
+  // Q fragments (kept for the whole task): rows r16 of each 16-row block,
+  // d = 32 ks + 8 g .. +7; rows past S_q are zeros
+  bf16x8_t qf[2][4];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int row = row0 + mb * 16 + r16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (row < p.S_q)
+        v = *reinterpret_cast<const u32x4_t *>(p.q + ((size_t)bh * p.S_q + row) * kAttnD + ks * 32 + g * 8);
+      qf[mb][ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  f32x4_t oacc[2][8];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) oacc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrow[2] = {-INFINITY, -INFINITY};  // running row max (log2 domain)
+  float lpart[2] = {0.f, 0.f};             // this lane's part of the row sum
+
+  // DMA lane offsets (8-row groups, 64-wide rows, swizzled as the GEMM tiles)
+  const uint32_t lane_off_k[2] = {(uint32_t)((lane >> 3) * ldk + dma_chunk(lane, 0) * 16),
+                                  (uint32_t)((lane >> 3) * ldk + dma_chunk(lane, 1) * 16)};
+  const uint32_t lane_off_v[2] = {(uint32_t)((lane >> 3) * ldv + dma_chunk(lane, 0) * 16),
+                                  (uint32_t)((lane >> 3) * ldv + dma_chunk(lane, 1) * 16)};
+  const int lane_c8[2] = {dma_chunk(lane, 0) * 8, dma_chunk(lane, 1) * 8};
+  // this wave's DMAs of a tile: K half (wave >> 1), row groups 4 (wave & 1) ..
+  // +3; V^T row groups 4 wave .. +3
+  auto stage_tile = [&](int j, int buf) {
+    const int step = j / tpb, kt = j % tpb;
+    const int src = (p.rank - step + p.world) % p.world;
+    const size_t blk = (size_t)src * p.BH + bh;
+    const i32x4_t vk = make_vdesc(p.k_recv + blk * p.S_kv * kAttnD, (uint32_t)(p.S_kv * ldk));
+    const i32x4_t vv = make_vdesc(p.vt_recv + blk * kAttnD * p.S_kv, (uint32_t)(kAttnD * ldv));
+    const uint32_t st = base + buf * kAttnStage;
+    const int half = wave >> 1;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int gl = 4 * (wave & 1) + d;  // row group within the tile
+      dma_row_group(vk, st + half * kAttnKHalf + gl * 1024, lane_off_k[gl & 1], lane_c8[gl & 1], ldk,
+                    half * 64, kAttnD, kt * (kAttnKT / 8) + gl);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int gl = 4 * wave + d;
+      dma_row_group(vv, st + kAttnVOff + gl * 1024, lane_off_v[gl & 1], lane_c8[gl & 1], ldv,
+                    kt * kAttnKT, p.S_kv, gl);
+    }
+  };
+  // wait for the chunk holding tile j (once per chunk)
+  int have = -1;
+  auto acquire = [&](int j) -> bool {
+    const int step = j / tpb, kt = j % tpb;
+    const int src = (p.rank - step + p.world) % p.world;
+    const int c = kt * kAttnKT / p.chunk_keys;
+    const int id = src * p.chunks + c;
+    if (id == have) return true;
+    have = id;
+    bool ok0 = true;
+    const uint32_t f = attn_flag(p, src, bh, c);
+    if (threadIdx.x == 0) ok0 = spin_until_eq(p.sync, flag_ptr(p.sync, f), p.sync.epoch, f);
+    return wg_sync_ok(ok0, s_word, !p.light_acquire);
+  };
+
+  if (!acquire(0)) return false;
+  stage_tile(0, 0);
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_vmcnt<0>();
+    wg_barrier();  // tile j landed; every wave is done with the other buffer
+    if (j + 1 < n_tiles) {
+      if (!acquire(j + 1)) return false;  // timeout or abort: nothing is in flight here
+      stage_tile(j + 1, (j + 1) & 1);
+    }
+    const char *st = smem + (j & 1) * kAttnStage;
+    // S = Q K^T: sacc[mb][kb] lane (g, r16): query 16 mb + r16, keys 16 kb + 4 g + 0..3
+    f32x4_t sacc[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) sacc[mb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = (ks & 1) * 4 + g;  // logical chunk of the 128-byte row
+      const char *kh = st + (ks >> 1) * kAttnKHalf + ((c ^ ((lane >> 1) & 7)) << 4);
+      bf16x8_t kf[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) kf[kb] = *reinterpret_cast<const bf16x8_t *>(kh + (kb * 16 + r16) * 128);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) sacc[mb][kb] = mfma16(kf[kb], qf[mb][ks], sacc[mb][kb]);
+    }
+    // online softmax (log2 domain)
+    bf16x8_t pf[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sacc[mb][kb][r] *= p.scale_log2;
+          mx = fmaxf(mx, sacc[mb][kb][r]);
+        }
+      mx = xor_max(xor_max(mx, 16), 32);
+      const float mnew = fmaxf(mrow[mb], mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrow[mb] - mnew);
+      mrow[mb] = mnew;
+      float sum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(sacc[mb][kb][r] - mnew);
+          sacc[mb][kb][r] = e;
+          sum += e;
+        }
+      lpart[mb] = lpart[mb] * alpha + sum;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        oacc[mb][db][0] *= alpha; oacc[mb][db][1] *= alpha;
+        oacc[mb][db][2] *= alpha; oacc[mb][db][3] *= alpha;
+      }
+      pf[mb][0] = pack_p(sacc[mb][0], sacc[mb][1]);
+      pf[mb][1] = pack_p(sacc[mb][2], sacc[mb][3]);
+    }
+    // O += P V: V^T row d = 16 db + r16, K slots = keys 32 kk + 4 g .. +3 and
+    // 32 kk + 16 + 4 g .. +3 (8-byte halves of 16-byte chunks 4 kk + g / 2
+    // and 4 kk + 2 + g / 2)
+    const char *vt = st + kAttnVOff;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const char *vrow = vt + (db * 16 + r16) * 128 + (g & 1) * 8;
+      const int swz = (lane >> 1) & 7;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int c1 = 4 * kk + (g >> 1), c2 = 4 * kk + 2 + (g >> 1);
+        const bf16x8_t vf = lds_pair(vrow + ((c1 ^ swz) << 4), vrow + ((c2 ^ swz) << 4));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) oacc[mb][db] = mfma16(vf, pf[mb][kk], oacc[mb][db]);
+      }
+    }
+  }
+  wg_barrier();  // both buffers are free for the next task
+  // finish: row sums over the 4 lane groups, O / l, lse = (m + log2 l) ln 2
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const float l = xor_sum(xor_sum(lpart[mb], 16), 32);
+    const float inv = 1.f / l;
+    const int row = row0 + mb * 16 + r16;
+    if (row < p.S_q) {
+      uint16_t *orow = p.o + ((size_t)bh * p.S_q + row) * kAttnD;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const f32x4_t v = oacc[mb][db];
+        *reinterpret_cast<uint2 *>(orow + db * 16 + 4 * g) = pack_bf16x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      }
+      if (g == 0) p.lse[(size_t)bh * p.S_q + row] = (mrow[mb] + __log2f(l)) * 0.69314718055994530942f;
+    }
+  }
+  return true;
+}
+
+template <int DUMMY>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[kAttnLds];
+  __shared__ uint32_t s_word;
+  const uint32_t ticket = take_ticket(p.sync, &s_word);
+  Ctrl *ctrl = p.sync.ctrl;
+  if (ticket < (uint32_t)p.n_land) {
+    for (;;) {
+      const uint32_t it = next_index(&ctrl->land_ctr, &s_word);
+      if (it >= (uint32_t)p.n_items) break;
+      attn_land_item(p, (int)it, smem);
+    }
+  }
+  if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
+    for (;;) {
+      const uint32_t t = next_index(&ctrl->tile_ctr, &s_word);
+      if (t >= (uint32_t)p.n_tasks) break;
+      if (!attn_task(p, (int)t / p.q_tiles, (int)t % p.q_tiles, smem, &s_word)) break;
+    }
+  }
+  finish_launch(p.sync);
+}
+
+hipError_t launch_attn(const AttnParams &p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((attn_kernel<0>), dim3(grid), dim3(kAttnThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t occupancy_attn(int *blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, attn_kernel<0>, kAttnThreads, 0);
+}
+
+}  // namespace mk

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -23,6 +24,8 @@ hipError_t launch_ar(const ArParams &p, int bm, int grid, hipStream_t s);
 hipError_t launch_moe(const MoeParams &p, int bm, int grid, hipStream_t s);
 hipError_t occupancy(int op, int bm, int bn, int *blocks_per_cu);
 hipError_t occupancy_moe(int bm, int *blocks_per_cu);
+hipError_t launch_attn(const AttnParams &p, int grid, hipStream_t s);
+hipError_t occupancy_attn(int *blocks_per_cu);
 }  // namespace mk
 
 struct mk_ctx {
@@ -129,7 +132,9 @@ int max_grid(mk_ctx *h, int op, int bm, int bn = 0) {
   int &o = h->occ[op][bm != 256 ? 1 : bn == 224 ? 2 : 0];
   if (o == 0) {
     int b = 0;
-    hipError_t e = op == MK_OP_MOE ? mk::occupancy_moe(bm, &b) : mk::occupancy(op, bm, bn, &b);
+    hipError_t e = op == MK_OP_MOE ? mk::occupancy_moe(bm, &b)
+                   : op == MK_OP_RING_ATTN ? mk::occupancy_attn(&b)
+                                           : mk::occupancy(op, bm, bn, &b);
     if (e != hipSuccess || b < 1) {
       (void)hipGetLastError();
       b = 1;
@@ -772,6 +777,84 @@ mk_status mk_moe_dispatch_gemm_combine(mk_handle h, mk_stream stream, int n_src,
   return moe_launch(h, stream, n_src, rank, x_src, logits_src, wt, T, H, N, E, E_loc, top_k, y,
                     topk_idx, topk_gate, slot_token, expert_offsets, chunk_offsets, x_slots, cap,
                     true, y_peer, ret, out, flags);
+}
+
+// ---------------------------------------------------------------- ring attention
+
+mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, const mk_bf16 *q,
+                            const mk_bf16 *const *k_src, const mk_bf16 *const *v_src, int BH,
+                            int S_q, int S_kv, int D, float scale, mk_bf16 *o, float *lse,
+                            mk_bf16 *k_recv, mk_bf16 *vt_recv, unsigned flags) {
+  if (!h) return MK_ERR_INVALID;
+  h->err.clear();
+  if (world < 1 || world > MK_MAX_WORLD || rank < 0 || rank >= world)
+    return fail(h, MK_ERR_INVALID, "bad world / rank");
+  if (flags != 0) return fail(h, MK_ERR_INVALID, "unknown flag bits");
+  if (!k_src || !v_src) return fail(h, MK_ERR_INVALID, "k_src / v_src is NULL");
+  if (BH < 1 || S_q < 1 || S_kv < 1) return fail(h, MK_ERR_INVALID, "bad BH / S_q / S_kv");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(h, MK_ERR_INVALID, "scale must be positive and finite");
+  if (D != mk::kAttnD || S_kv % 64 != 0)
+    return fail(h, MK_ERR_UNSUPPORTED, "ring attention needs D = 128 and S_kv a multiple of 64");
+  if ((long)BH * S_q * D >= (1L << 31) || (long)world * BH * S_kv * D >= (1L << 34))
+    return fail(h, MK_ERR_UNSUPPORTED, "ring attention sizes beyond the supported range");
+  DeviceGuard g(h->device);
+  mk::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  const void *dp;
+  mk_status st;
+  if ((st = resolve(h, q, false, &dp, "q")) != MK_OK) return st;
+  p.q = static_cast<const uint16_t *>(dp);
+  for (int r = 0; r < world; ++r) {
+    char what[32];
+    std::snprintf(what, sizeof(what), "k_src[%d]", r);
+    if ((st = resolve(h, k_src[r], r != rank, &dp, what)) != MK_OK) return st;
+    p.k_src[r] = static_cast<const uint16_t *>(dp);
+    std::snprintf(what, sizeof(what), "v_src[%d]", r);
+    if ((st = resolve(h, v_src[r], r != rank, &dp, what)) != MK_OK) return st;
+    p.v_src[r] = static_cast<const uint16_t *>(dp);
+  }
+  if ((st = resolve(h, o, false, &dp, "o")) != MK_OK) return st;
+  p.o = static_cast<uint16_t *>(const_cast<void *>(dp));
+  if ((st = resolve(h, lse, false, &dp, "lse")) != MK_OK) return st;
+  p.lse = static_cast<float *>(const_cast<void *>(dp));
+  if ((st = resolve(h, k_recv, false, &dp, "k_recv")) != MK_OK) return st;
+  p.k_recv = static_cast<uint16_t *>(const_cast<void *>(dp));
+  if ((st = resolve(h, vt_recv, false, &dp, "vt_recv")) != MK_OK) return st;
+  p.vt_recv = static_cast<uint16_t *>(const_cast<void *>(dp));
+
+  p.world = world;
+  p.rank = rank;
+  p.BH = BH;
+  p.S_q = S_q;
+  p.S_kv = S_kv;
+  p.scale_log2 = scale * 1.44269504088896340736f;
+  // landing chunks: 256 keys (64 KB of K, 64 KB of V), larger while the flags
+  // would not fit
+  p.chunk_keys = 256;
+  while ((long)world * BH * cdiv(S_kv, p.chunk_keys) > mk::kMaxFlags) p.chunk_keys *= 2;
+  p.chunks = cdiv(S_kv, p.chunk_keys);
+  p.n_items = world * BH * p.chunks;
+  p.q_tiles = cdiv(S_q, 128);
+  p.n_tasks = BH * p.q_tiles;
+  if (p.n_tasks >= (1 << 30)) return fail(h, MK_ERR_UNSUPPORTED, "too many attention tasks");
+  // chunks of both receive buffers start and end on 128-byte lines
+  p.light_acquire = ((reinterpret_cast<uintptr_t>(p.k_recv) | reinterpret_cast<uintptr_t>(p.vt_recv)) & 127u) == 0 ? 1 : 0;
+
+  const int gmax = max_grid(h, MK_OP_RING_ATTN, 256);
+  const mk_roles &r = h->roles[MK_OP_RING_ATTN];
+  // every workgroup waits for land workgroups, so all must be resident at once
+  int land = r.n_land >= 0 ? r.n_land : std::min(p.n_items, std::max(1, std::min(32, gmax / 8)));
+  land = std::max(1, std::min(land, gmax));
+  int compute = r.n_compute >= 0 ? r.n_compute : std::min(p.n_tasks, gmax - land);
+  compute = std::max(0, std::min(compute, gmax - land));
+  p.n_land = land;
+  p.n_compute = compute;
+  const int grid = land + compute;
+  p.sync = make_sync(h, (uint32_t)p.n_items);
+  hipError_t e = mk::launch_attn(p, grid, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(h, e, "launching the ring attention kernel");
+  record(h, MK_OP_RING_ATTN, land, compute, 0, grid);
+  return MK_OK;
 }
 
 }  // extern "C"

@@ -65,6 +65,26 @@ struct ArParams {
   int tiles_m, tiles_n, n_tiles, tile_map, tile_group_m, tile_split_m;
 };
 
+// Ring attention.  Receive buffers are indexed by source rank: k_recv
+// [W][BH][S_kv][D], vt_recv [W][BH][D][S_kv] (V transposed).
+constexpr int kAttnD = 128;
+struct AttnParams {
+  Sync sync;
+  const uint16_t *q;                      // [BH][S_q][D]
+  const uint16_t *k_src[MK_MAX_WORLD];    // [BH][S_kv][D] of rank r
+  const uint16_t *v_src[MK_MAX_WORLD];
+  uint16_t *o;                            // [BH][S_q][D]
+  float *lse;                             // [BH][S_q]
+  uint16_t *k_recv;
+  uint16_t *vt_recv;
+  int world, rank, BH, S_q, S_kv;
+  float scale_log2;                       // scale * log2(e)
+  int n_land, n_compute;
+  int chunk_keys, chunks;                 // keys per landing chunk, chunks per block
+  int q_tiles, n_tasks, n_items;
+  int light_acquire;
+};
+
 // MoE dispatch + grouped GEMM.  Route items are blocks of kRouteTokens
 // tokens of one source; an item's flag says all of its local tokens landed.
 constexpr int kRouteTokens = 256;

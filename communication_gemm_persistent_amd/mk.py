@@ -29,6 +29,7 @@ OP_AG_GEMM = 0
 OP_GEMM_RS = 1
 OP_GEMM_AR = 2
 OP_MOE = 3
+OP_RING_ATTN = 4
 
 F_PRELANDED = 0x1
 F_NO_GATE = 0x2
@@ -39,7 +40,8 @@ MAX_WORLD = 16
 # Names declared in include/mk.h (the CPU tests check the library exports them).
 EXPORTS = ("mk_create", "mk_destroy", "mk_set_roles", "mk_get_roles", "mk_last_launch",
            "mk_sync", "mk_status_string", "mk_last_error", "mk_ag_gemm", "mk_gemm_rs",
-           "mk_gemm_ar", "mk_moe_dispatch_gemm", "mk_moe_dispatch_gemm_combine")
+           "mk_gemm_ar", "mk_moe_dispatch_gemm", "mk_moe_dispatch_gemm_combine",
+           "mk_ring_attention")
 
 
 class MkError(RuntimeError):
@@ -91,6 +93,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_gemm_ar.argtypes = [_vp, _vp, _i, _i, _vp, _vp, _pp, _vp, _pp, _i, _i, _i, _i, _u]
     lib.mk_moe_dispatch_gemm.argtypes = [_vp, _vp, _i, _i, _pp, _pp, _vp, _i, _i, _i, _i, _i, _i,
                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _u]
+    lib.mk_ring_attention.argtypes = [_vp, _vp, _i, _i, _vp, _pp, _pp, _i, _i, _i, _i,
+                                      ctypes.c_float, _vp, _vp, _vp, _vp, _u]
     lib.mk_moe_dispatch_gemm_combine.argtypes = [
         _vp, _vp, _i, _i, _pp, _pp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
         _i, _vp, _pp, _vp, _u]
@@ -289,3 +293,28 @@ class Handle:
             _ptr(y_peer, "y_peer", _BF16, (T * top_k, N)), _ptr_array(rp),
             _ptr(out, "out", _BF16, (T, N)), flags)
         self._check(st, "mk_moe_dispatch_gemm_combine", self.h)
+
+    def ring_attention(self, q: torch.Tensor, k_src: Sequence[torch.Tensor],
+                       v_src: Sequence[torch.Tensor], o: torch.Tensor, lse: torch.Tensor,
+                       k_recv: torch.Tensor, vt_recv: torch.Tensor, scale: Optional[float] = None,
+                       rank: int = 0, flags: int = 0, stream=None) -> None:
+        """Ring attention of this rank's queries q [BH, S_q, D] over every rank's
+        keys / values k_src[r], v_src[r] [BH, S_kv, D]: o [BH, S_q, D] bf16,
+        lse [BH, S_q] fp32, k_recv [W, BH, S_kv, D] and vt_recv [W, BH, D, S_kv]
+        (the landed blocks, values transposed).  scale defaults to 1/sqrt(D)."""
+        W = len(k_src)
+        BH, S_q, D = q.shape
+        S_kv = k_src[0].shape[1]
+        if len(v_src) != W:
+            raise ValueError("k_src and v_src differ in length")
+        if scale is None:
+            scale = 1.0 / float(D) ** 0.5
+        kp = [_ptr(k, f"k_src[{r}]", _BF16, (BH, S_kv, D)) for r, k in enumerate(k_src)]
+        vp = [_ptr(v, f"v_src[{r}]", _BF16, (BH, S_kv, D)) for r, v in enumerate(v_src)]
+        st = self.lib.mk_ring_attention(
+            self.h, _vp(_stream(stream, self.device)), W, rank, _ptr(q, "q", _BF16),
+            _ptr_array(kp), _ptr_array(vp), BH, S_q, S_kv, D, ctypes.c_float(scale),
+            _ptr(o, "o", _BF16, (BH, S_q, D)), _ptr(lse, "lse", (torch.float32,), (BH, S_q)),
+            _ptr(k_recv, "k_recv", _BF16, (W, BH, S_kv, D)),
+            _ptr(vt_recv, "vt_recv", _BF16, (W, BH, D, S_kv)), flags)
+        self._check(st, "mk_ring_attention", self.h)

@@ -74,7 +74,8 @@ typedef enum {
   MK_OP_GEMM_RS = 1,
   MK_OP_GEMM_AR = 2,
   MK_OP_MOE = 3,
-  MK_OP_COUNT = 4
+  MK_OP_RING_ATTN = 4,
+  MK_OP_COUNT = 5
 } mk_op;
 
 typedef struct {
@@ -247,6 +248,36 @@ mk_status mk_moe_dispatch_gemm_combine(mk_handle h, mk_stream stream, int n_src,
                                        int32_t *chunk_offsets, mk_bf16 *x_slots, int cap,
                                        const mk_bf16 *y_peer, mk_bf16 *const *ret, mk_bf16 *out,
                                        unsigned flags);
+
+/*
+ * Ring attention  [P1, table "Die fuenf verschmolzenen Kerne", ring attention
+ * row: the ring KV exchange and the local attention in one persistent kernel]:
+ *   this rank's queries attend to the keys and values of every rank's block,
+ *   the blocks taken in ring order (step s: the block of rank (rank - s) mod
+ *   W), with softmax over all W * S_kv keys (no causal mask):
+ *     o   = bf16(softmax(q k^T * scale) v)      fp32 accumulation, online softmax
+ *     lse = max + log(sum exp(s - max))         natural log, fp32, per query row
+ *   The land role copies every block into the receive buffers, K as is and V
+ *   transposed, and releases one flag per chunk of keys; attention tiles start
+ *   as soon as their chunk has landed.
+ *
+ *   q        [B*H, S_q, D] bf16 device memory (D = 128)
+ *   k_src    host array of W pointers, each [B*H, S_kv, D] bf16: rank r's keys
+ *            (r = rank local; the others emulated peers, device or pinned host)
+ *   v_src    the same for the values
+ *   o        output [B*H, S_q, D] bf16;  lse: output [B*H, S_q] fp32
+ *   k_recv   output [W, B*H, S_kv, D] bf16 device memory: every block by source
+ *            rank, as received
+ *   vt_recv  output [W, B*H, D, S_kv] bf16 device memory: every value block,
+ *            transposed
+ *   scale    score factor (1/sqrt(D) is the usual choice)
+ *   Supported: D = 128, S_kv a multiple of 64, S_q >= 1, B*H >= 1.  Other
+ *   shapes return MK_ERR_UNSUPPORTED.
+ */
+mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, const mk_bf16 *q,
+                            const mk_bf16 *const *k_src, const mk_bf16 *const *v_src, int BH,
+                            int S_q, int S_kv, int D, float scale, mk_bf16 *o, float *lse,
+                            mk_bf16 *k_recv, mk_bf16 *vt_recv, unsigned flags);
 
 #ifdef __cplusplus
 }

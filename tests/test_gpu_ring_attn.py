@@ -1,0 +1,163 @@
+"""GPU parity of the fused ring attention against the CPU oracle.
+
+The receive buffers are data movement and must hold every rank's keys and
+transposed values bit for bit.  The output uses the float rule
+|gpu - ref| <= 1e-2 |ref| + 1e-2 rms(ref); the log-sum-exp uses
+|gpu - ref| <= 1e-3 + 1e-4 |ref|: fp32 scores from 128-term dot products of
+bf16 values, the hardware exp2 / log2 and per-lane fp32 sums of up to
+W * S_kv / 4 terms stay well inside it.  With zero queries every score is 0
+and every P entry exactly 1, so equal value rows come back bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from communication_gemm_persistent_amd import inputs as I
+from tests.gpu_util import bits, dev_bf16, empty_bf16
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def lse_close(gpu, ref, what="lse"):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    bad = ~(np.abs(gpu - ref) <= 1e-3 + 1e-4 * np.abs(ref))
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside; first {np.argwhere(bad)[:3]}"
+
+
+@pytest.fixture(scope="module")
+def handle(mk):
+    h = mk.Handle(0, spin_timeout_ms=10000)
+    yield h
+    h.close()
+
+
+def run_ring(h, d, rank=0, where="hbm"):
+    W = len(d["k"])
+    B, H, S_q, _ = d["q"].shape
+    S_kv = d["k"][0].shape[2]
+    BH = B * H
+    q = dev_bf16(d["q"].reshape(BH, S_q, D))
+    ks = [dev_bf16(k.reshape(BH, S_kv, D), "hbm" if r == rank else where) for r, k in enumerate(d["k"])]
+    vs = [dev_bf16(v.reshape(BH, S_kv, D), "hbm" if r == rank else where) for r, v in enumerate(d["v"])]
+    o = empty_bf16((BH, S_q, D))
+    lse = torch.full((BH, S_q), float("nan"), dtype=torch.float32, device="cuda")
+    k_recv = empty_bf16((W, BH, S_kv, D))
+    vt_recv = empty_bf16((W, BH, D, S_kv))
+    h.ring_attention(q, ks, vs, o, lse, k_recv, vt_recv, rank=rank)
+    h.sync()
+    torch.cuda.synchronize()
+    return dict(o=bits(o).reshape(B, H, S_q, D), lse=lse.cpu().numpy().reshape(B, H, S_q),
+                k_recv=bits(k_recv), vt_recv=bits(vt_recv))
+
+
+def check_recv(d, out):
+    W = len(d["k"])
+    B, H, _, _ = d["q"].shape
+    S_kv = d["k"][0].shape[2]
+    k_ref = np.stack([k.reshape(B * H, S_kv, D) for k in d["k"]])
+    vt_ref = np.stack([np.swapaxes(v.reshape(B * H, S_kv, D), -1, -2) for v in d["v"]])
+    O.assert_bits_equal(out["k_recv"], k_ref, "k_recv")
+    O.assert_bits_equal(out["vt_recv"], vt_ref, "vt_recv (transposed values)")
+
+
+SMALL = [  # W, rank, B, H, S_q, S_kv, peers
+    (3, 1, 1, 2, 200, 128, "hbm"),
+    (1, 0, 1, 1, 64, 64, "hbm"),
+    (4, 3, 1, 3, 129, 320, "host"),
+    (2, 0, 2, 2, 256, 512, "hbm"),
+    (5, 2, 1, 1, 1, 64, "hbm"),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL)
+def test_ring_attention_small(handle, cfg):
+    W, rank, B, H, S_q, S_kv, where = cfg
+    print(f"ring attention W={W} rank={rank} B={B} H={H} S_q={S_q} S_kv={S_kv} peers={where}", flush=True)
+    d = I.gen_ring(W, B, H, S_q, S_kv, D, config=500 + W)
+    out = run_ring(handle, d, rank=rank, where=where)
+    ref = O.ring_attention(d["q"], d["k"], d["v"], rank=rank, scale=float(np.float32(1 / np.sqrt(D))))
+    check_recv(d, out)
+    O.assert_close_bf16(out["o"], ref["o"], "o")
+    lse_close(out["lse"], ref["lse"])
+
+
+def test_ring_attention_zero_queries_equal_values_exact(handle):
+    """Q = 0: every P entry is exactly 1 and l = W * S_kv; equal value rows
+    (one vector per head) come back bit for bit, lse = ln(W * S_kv)."""
+    W, B, H, S_q, S_kv = 3, 1, 2, 130, 192
+    d = I.gen_ring(W, B, H, S_q, S_kv, D, config=510)
+    d["q"] = np.zeros_like(d["q"])
+    u = d["v"][0][:, :, :1, :]  # one row per head
+    d["v"] = [np.broadcast_to(u, v.shape).copy() for v in d["v"]]
+    out = run_ring(handle, d, rank=1)
+    O.assert_bits_equal(out["o"], np.broadcast_to(u, out["o"].shape), "o (equal values)")
+    lse_close(out["lse"], np.full(out["lse"].shape, np.log(W * S_kv)))
+
+
+def test_ring_attention_role_counts_do_not_change_bits(handle, mk):
+    """Every task takes its tiles in the same order whatever the schedule:
+    one land and one compute workgroup give the default launch's bits."""
+    W, B, H, S_q, S_kv = 3, 1, 2, 256, 256
+    d = I.gen_ring(W, B, H, S_q, S_kv, D, config=520)
+    base = run_ring(handle, d, rank=2)
+    handle.set_roles(mk.OP_RING_ATTN, n_land=1, n_compute=1)
+    try:
+        few = run_ring(handle, d, rank=2)
+    finally:
+        handle.set_roles(mk.OP_RING_ATTN)
+    O.assert_bits_equal(few["o"], base["o"], "o (1 land, 1 compute)")
+    O.assert_bits_equal(few["lse"].view(np.uint32), base["lse"].view(np.uint32), "lse")
+    check_recv(d, few)
+
+
+@pytest.mark.parametrize("shape,what", [((1, 64, 64, 64), "D = 64"), ((1, 64, 100, 128), "S_kv = 100")])
+def test_ring_attention_rejects_unsupported_shapes(handle, mk, shape, what):
+    BH, S_q, S_kv, d_ = shape
+    q = torch.zeros((BH, S_q, d_), dtype=torch.bfloat16, device="cuda")
+    k = [torch.zeros((BH, S_kv, d_), dtype=torch.bfloat16, device="cuda")]
+    o = torch.empty_like(q)
+    lse = torch.empty((BH, S_q), dtype=torch.float32, device="cuda")
+    kr = torch.empty((1, BH, S_kv, d_), dtype=torch.bfloat16, device="cuda")
+    vr = torch.empty((1, BH, d_, S_kv), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mk.MkError) as e:
+        handle.ring_attention(q, k, k, o, lse, kr, vr)
+    assert e.value.status == 2, what  # MK_ERR_UNSUPPORTED
+
+
+def test_ring_attention_full_size_sampled(handle):
+    """8 ranks x 4096 keys, 4096 local queries, 32 heads of 128: the receive
+    buffers in full, o and lse on sampled rows of sampled heads."""
+    name = "ring_attn_w8_h32_s4096_d128"
+    p = I.CONFIGS[name].params
+    print(name, flush=True)
+    d = I.gen_workload(name)
+    W, B, H, S_q, S_kv = p["world"], p["B"], p["H"], p["S_q"], p["S_kv"]
+    BH = B * H
+    q = dev_bf16(d["q"].reshape(BH, S_q, D))
+    ks = [dev_bf16(k.reshape(BH, S_kv, D)) for k in d["k"]]
+    vs = [dev_bf16(v.reshape(BH, S_kv, D)) for v in d["v"]]
+    o = empty_bf16((BH, S_q, D))
+    lse = torch.full((BH, S_q), float("nan"), dtype=torch.float32, device="cuda")
+    k_recv = empty_bf16((W, BH, S_kv, D))
+    vt_recv = empty_bf16((W, BH, D, S_kv))
+    handle.ring_attention(q, ks, vs, o, lse, k_recv, vt_recv, rank=p["rank"])
+    handle.sync()
+    torch.cuda.synchronize()
+    for r in range(W):  # data movement: compared on the device, bit for bit
+        assert torch.equal(k_recv[r].view(torch.int16), ks[r].view(torch.int16)), f"k_recv[{r}]"
+        assert torch.equal(vt_recv[r].view(torch.int16), vs[r].transpose(1, 2).contiguous().view(torch.int16)), f"vt_recv[{r}]"
+    assert not torch.isnan(o.float()).any() and not torch.isnan(lse).any(), "unwritten output"
+    g = np.random.default_rng(9)
+    rows = np.array(sorted(set([0, 1, 127, 128, S_q - 1] + [int(x) for x in g.integers(0, S_q, 11)])))
+    heads = [0, 13, H - 1]
+    ob = bits(o).reshape(B, H, S_q, D)
+    lb = lse.cpu().numpy().reshape(B, H, S_q)
+    for hh in heads:
+        ref = O.ring_attention(d["q"][:, hh:hh + 1], [k[:, hh:hh + 1] for k in d["k"]],
+                               [v[:, hh:hh + 1] for v in d["v"]], rank=p["rank"],
+                               scale=float(np.float32(1 / np.sqrt(D))), rows=rows)
+        O.assert_close_bf16(ob[:, hh:hh + 1][:, :, rows], ref["o"], f"o (head {hh})")
+        lse_close(lb[:, hh:hh + 1][:, :, rows], ref["lse"], f"lse (head {hh})")

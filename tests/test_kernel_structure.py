@@ -32,7 +32,7 @@ def _asm(src_dir, name, out_dir):
     return out
 
 
-@pytest.mark.parametrize("name", ["mk_kernels.hip", "mk_moe.hip"])
+@pytest.mark.parametrize("name", ["mk_kernels.hip", "mk_moe.hip", "mk_attn.hip"])
 def test_no_barrier_in_divergent_loop(tmp_path, name):
     bad = check_file(_asm(CSRC, name, str(tmp_path)))
     assert not bad, f"barriers inside divergent loops: {bad}"
@@ -56,7 +56,7 @@ def test_checker_flags_merged_single_thread_regions(tmp_path):
         "checker missed the known-bad variant"
 
 
-@pytest.mark.parametrize("name", ["mk_kernels.hip", "mk_moe.hip"])
+@pytest.mark.parametrize("name", ["mk_kernels.hip", "mk_moe.hip", "mk_attn.hip"])
 def test_no_sgpr_hazard_at_lds_dma(tmp_path, name):
     bad = check_hazards(_asm(CSRC, name, str(tmp_path)))
     assert not bad, f"LDS DMAs reading a VALU-written SGPR too early: {bad[:5]}"
