@@ -12,7 +12,8 @@
 //            ring order (at step s the block of rank (rank - s) mod W), a
 //            chunk of keys at a time: K as it is, V transposed (keys
 //            contiguous, the layout the P V product reads); then releases
-//            the chunk's flag.  Land workgroups run tasks when done.
+//            the chunk's flag.  Land workgroups run tasks when done (unless
+//            the launch only lands).
 //   compute  takes (batch*head, 128-query tile) tasks.  For every ring step
 //            and every 64-key tile of that step's block it waits for the
 //            tile's chunk, stages K and V^T in LDS (DMA, double-buffered) and
@@ -202,7 +203,7 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, c
     const int src = (p.rank - step + p.world) % p.world;
     const int c = kt * kAttnKT / p.chunk_keys;
     const int id = src * p.chunks + c;
-    if (id == have) return true;
+    if (id == have || p.prelanded) return true;
     have = id;
     bool ok0 = true;
     const uint32_t f = attn_flag(p, src, bh, c);
@@ -240,35 +241,41 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, c
     }
     // online softmax (log2 domain)
     bf16x8_t pf[2][2];
+    // The scale is positive, so the row max is taken over the raw scores
+    // and scaled once; exp2(s scale_log2 - m) is one fma and one exp2.  When
+    // no row's max grows, alpha is exactly 1 for every row of the wave and
+    // the rescale of O is skipped (the same bits).
+    const float c = p.scale_log2;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sacc[mb][kb][r] *= p.scale_log2;
-          mx = fmaxf(mx, sacc[mb][kb][r]);
-        }
-      mx = xor_max(xor_max(mx, 16), 32);
-      const float mnew = fmaxf(mrow[mb], mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrow[mb] - mnew);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[mb][kb][r]);
+      mx = xor_max(xor_max(mx, 16), 32) * c;
+      const float mold = mrow[mb];
+      const float mnew = fmaxf(mold, mx);
       mrow[mb] = mnew;
       float sum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(sacc[mb][kb][r] - mnew);
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][kb][r], c, -mnew));
           sacc[mb][kb][r] = e;
           sum += e;
         }
-      lpart[mb] = lpart[mb] * alpha + sum;
+      if (__any(mnew > mold)) {
+        const float alpha = __builtin_amdgcn_exp2f(mold - mnew);
+        lpart[mb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        oacc[mb][db][0] *= alpha; oacc[mb][db][1] *= alpha;
-        oacc[mb][db][2] *= alpha; oacc[mb][db][3] *= alpha;
+        for (int db = 0; db < 8; ++db) {
+          oacc[mb][db][0] *= alpha; oacc[mb][db][1] *= alpha;
+          oacc[mb][db][2] *= alpha; oacc[mb][db][3] *= alpha;
+        }
       }
+      lpart[mb] += sum;
       pf[mb][0] = pack_p(sacc[mb][0], sacc[mb][1]);
       pf[mb][1] = pack_p(sacc[mb][2], sacc[mb][3]);
     }
@@ -322,11 +329,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnParams p) {
       attn_land_item(p, (int)it, smem);
     }
   }
-  if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
+  // land workgroups join once landing is done, unless the launch lands only
+  if (ticket < (uint32_t)p.n_compute + (p.n_compute > 0 ? (uint32_t)p.n_land : 0u)) {
     for (;;) {
+      // query-tile-major: the tasks running together cover every head and
+      // consume the ring's blocks in the order they land
       const uint32_t t = next_index(&ctrl->tile_ctr, &s_word);
       if (t >= (uint32_t)p.n_tasks) break;
-      if (!attn_task(p, (int)t / p.q_tiles, (int)t % p.q_tiles, smem, &s_word)) break;
+      if (!attn_task(p, (int)t % p.BH, (int)t / p.BH, smem, &s_word)) break;
     }
   }
   finish_launch(p.sync);

@@ -789,8 +789,9 @@ mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, 
   h->err.clear();
   if (world < 1 || world > MK_MAX_WORLD || rank < 0 || rank >= world)
     return fail(h, MK_ERR_INVALID, "bad world / rank");
-  if (flags != 0) return fail(h, MK_ERR_INVALID, "unknown flag bits");
-  if (!k_src || !v_src) return fail(h, MK_ERR_INVALID, "k_src / v_src is NULL");
+  if (flags & ~MK_F_PRELANDED) return fail(h, MK_ERR_INVALID, "unknown flag bits");
+  const bool pre = (flags & MK_F_PRELANDED) != 0;
+  if (!pre && (!k_src || !v_src)) return fail(h, MK_ERR_INVALID, "k_src / v_src is NULL");
   if (BH < 1 || S_q < 1 || S_kv < 1) return fail(h, MK_ERR_INVALID, "bad BH / S_q / S_kv");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(h, MK_ERR_INVALID, "scale must be positive and finite");
   if (D != mk::kAttnD || S_kv % 64 != 0)
@@ -804,7 +805,7 @@ mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, 
   mk_status st;
   if ((st = resolve(h, q, false, &dp, "q")) != MK_OK) return st;
   p.q = static_cast<const uint16_t *>(dp);
-  for (int r = 0; r < world; ++r) {
+  for (int r = 0; r < world && !pre; ++r) {
     char what[32];
     std::snprintf(what, sizeof(what), "k_src[%d]", r);
     if ((st = resolve(h, k_src[r], r != rank, &dp, what)) != MK_OK) return st;
@@ -843,13 +844,17 @@ mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, 
   const int gmax = max_grid(h, MK_OP_RING_ATTN, 256);
   const mk_roles &r = h->roles[MK_OP_RING_ATTN];
   // every workgroup waits for land workgroups, so all must be resident at once
-  int land = r.n_land >= 0 ? r.n_land : std::min(p.n_items, std::max(1, std::min(32, gmax / 8)));
-  land = std::max(1, std::min(land, gmax));
+  // the blocks are as large as the queries' share of the work is small:
+  // 3/16 of the grid lands (then computes), which keeps every ring step
+  // landed ahead of the tasks that consume it
+  int land = r.n_land >= 0 ? r.n_land : std::min(p.n_items, std::max(1, gmax * 3 / 16));
+  land = pre ? 0 : std::max(1, std::min(land, gmax));
+  p.prelanded = pre ? 1 : 0;
   int compute = r.n_compute >= 0 ? r.n_compute : std::min(p.n_tasks, gmax - land);
   compute = std::max(0, std::min(compute, gmax - land));
   p.n_land = land;
   p.n_compute = compute;
-  const int grid = land + compute;
+  const int grid = std::max(1, land + compute);
   p.sync = make_sync(h, (uint32_t)p.n_items);
   hipError_t e = mk::launch_attn(p, grid, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(h, e, "launching the ring attention kernel");

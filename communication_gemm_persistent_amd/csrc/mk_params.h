@@ -83,6 +83,7 @@ struct AttnParams {
   int chunk_keys, chunks;                 // keys per landing chunk, chunks per block
   int q_tiles, n_tasks, n_items;
   int light_acquire;
+  int prelanded;                          // receive buffers already hold every block
 };
 
 // MoE dispatch + grouped GEMM.  Route items are blocks of kRouteTokens

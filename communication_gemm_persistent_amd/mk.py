@@ -301,12 +301,14 @@ class Handle:
         """Ring attention of this rank's queries q [BH, S_q, D] over every rank's
         keys / values k_src[r], v_src[r] [BH, S_kv, D]: o [BH, S_q, D] bf16,
         lse [BH, S_q] fp32, k_recv [W, BH, S_kv, D] and vt_recv [W, BH, D, S_kv]
-        (the landed blocks, values transposed).  scale defaults to 1/sqrt(D)."""
-        W = len(k_src)
+        (the landed blocks, values transposed).  scale defaults to 1/sqrt(D).
+        With F_PRELANDED the receive buffers are inputs and k_src / v_src may
+        hold None."""
+        W = k_recv.shape[0]
         BH, S_q, D = q.shape
-        S_kv = k_src[0].shape[1]
-        if len(v_src) != W:
-            raise ValueError("k_src and v_src differ in length")
+        S_kv = k_recv.shape[2]
+        if len(k_src) != W or len(v_src) != W:
+            raise ValueError(f"k_src / v_src need {W} entries (one per rank)")
         if scale is None:
             scale = 1.0 / float(D) ** 0.5
         kp = [_ptr(k, f"k_src[{r}]", _BF16, (BH, S_kv, D)) for r, k in enumerate(k_src)]

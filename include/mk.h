@@ -94,7 +94,8 @@ typedef struct {
 } mk_roles;
 
 /* Per-call option bits. */
-#define MK_F_PRELANDED 0x1u /* AG: a_gathered already holds the gathered A; skip landing (GEMM alone) */
+#define MK_F_PRELANDED 0x1u /* AG: a_gathered already holds the gathered A; ring attention: the
+                               receive buffers hold every block; skip landing (compute alone) */
 #define MK_F_NO_GATE 0x2u   /* MoE: store x @ W_e without the gate factor */
 #define MK_F_STATIC_ROLES 0x4u /* AG: every workgroup keeps its ticket role for the whole launch
                                  (by default compute workgroups land chunks while their rows
@@ -273,6 +274,8 @@ mk_status mk_moe_dispatch_gemm_combine(mk_handle h, mk_stream stream, int n_src,
  *   scale    score factor (1/sqrt(D) is the usual choice)
  *   Supported: D = 128, S_kv a multiple of 64, S_q >= 1, B*H >= 1.  Other
  *   shapes return MK_ERR_UNSUPPORTED.
+ *   MK_F_PRELANDED: k_recv / vt_recv already hold every block (attention
+ *   alone); k_src / v_src are not read and may be NULL.
  */
 mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, const mk_bf16 *q,
                             const mk_bf16 *const *k_src, const mk_bf16 *const *v_src, int BH,

@@ -161,3 +161,23 @@ def test_ring_attention_full_size_sampled(handle):
                                scale=float(np.float32(1 / np.sqrt(D))), rows=rows)
         O.assert_close_bf16(ob[:, hh:hh + 1][:, :, rows], ref["o"], f"o (head {hh})")
         lse_close(lb[:, hh:hh + 1][:, :, rows], ref["lse"], f"lse (head {hh})")
+
+
+def test_ring_attention_prelanded_equals_fused(handle, mk):
+    """Attention alone on the landed receive buffers gives the fused bits."""
+    W, B, H, S_q, S_kv = 3, 1, 2, 200, 192
+    d = I.gen_ring(W, B, H, S_q, S_kv, D, config=530)
+    BH = B * H
+    q = dev_bf16(d["q"].reshape(BH, S_q, D))
+    ks = [dev_bf16(k.reshape(BH, S_kv, D)) for k in d["k"]]
+    vs = [dev_bf16(v.reshape(BH, S_kv, D)) for v in d["v"]]
+    o1, o2 = empty_bf16((BH, S_q, D)), empty_bf16((BH, S_q, D))
+    l1 = torch.empty((BH, S_q), dtype=torch.float32, device="cuda")
+    l2 = torch.empty_like(l1)
+    kr = empty_bf16((W, BH, S_kv, D))
+    vr = empty_bf16((W, BH, D, S_kv))
+    handle.ring_attention(q, ks, vs, o1, l1, kr, vr, rank=1)
+    handle.ring_attention(q, [None] * W, [None] * W, o2, l2, kr, vr, rank=1, flags=mk.F_PRELANDED)
+    handle.sync()
+    O.assert_bits_equal(bits(o2), bits(o1), "o (pre-landed)")
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), "lse (pre-landed)"
