@@ -391,6 +391,43 @@ def other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev):
         "roles": h.last_launch(mk.OP_MOE)[0]}
     del x, lg, wt, y, idx, gate, st, eo, co, xs, d, yp, ret, o
     torch.cuda.empty_cache()
+
+    # Ring attention
+    name = "ring_attn_w8_h32_s4096_d128"
+    log(f"[bench] {name}")
+    wl = I.CONFIGS[name]
+    p = wl.params
+    d = I.gen_workload(name)
+    W, BH, S_q, S_kv, D = p["world"], p["B"] * p["H"], p["S_q"], p["S_kv"], p["D"]
+    q = to_dev(d["q"].reshape(BH, S_q, D))
+    ks = [to_dev(k.reshape(BH, S_kv, D)) for k in d["k"]]
+    vs = [to_dev(v.reshape(BH, S_kv, D)) for v in d["v"]]
+    o = torch.empty((BH, S_q, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((BH, S_q), dtype=torch.float32, device=dev)
+    kr = torch.empty((W, BH, S_kv, D), dtype=torch.bfloat16, device=dev)
+    vr = torch.empty((W, BH, D, S_kv), dtype=torch.bfloat16, device=dev)
+
+    def ring():
+        h.ring_attention(q, ks, vs, o, lse, kr, vr, rank=p["rank"])
+
+    t = float(np.median(time_calls(ring, 10, 2)))
+    roles = h.last_launch(mk.OP_RING_ATTN)[0]
+    t_alone = float(np.median(time_calls(
+        lambda: h.ring_attention(q, [None] * W, [None] * W, o, lse, kr, vr, rank=p["rank"],
+                                 flags=mk.F_PRELANDED), 10, 2)))
+    h.set_roles(mk.OP_RING_ATTN, n_land=roles[0], n_compute=0)
+    t_land = float(np.median(time_calls(ring, 10, 2)))
+    h.set_roles(mk.OP_RING_ATTN)
+    fl = wl.flops()
+    landed = 2 * W * BH * S_kv * D * 2
+    out[name] = {"ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 2),
+                 "attn_alone_ms": round(t_alone, 4),
+                 "attn_alone_tflops": round(fl / (t_alone * 1e-3) / 1e12, 2),
+                 "land_alone_ms": round(t_land, 4),
+                 "landing_GBps": round(2 * landed / (t_land * 1e-3) / 1e9, 1),
+                 "overlap_efficiency": round(max(t_alone, t_land) / t, 4), "roles": roles}
+    del q, ks, vs, o, lse, kr, vr, d
+    torch.cuda.empty_cache()
     return out
 
 
