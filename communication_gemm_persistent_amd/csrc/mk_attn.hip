@@ -43,6 +43,8 @@ constexpr int kAttnStage = kAttnVOff + kAttnD * 128;
 constexpr int kAttnLds = 2 * kAttnStage;
 // land transpose tile: [128 d][64 keys] with a 132-byte pitch
 constexpr int kAttnTPitch = 132;
+// workspace slot of a (bh, qt) pair: unnormalised O [128][128], row max, row sum
+constexpr int kAttnSlot = kAttnQ * kAttnD + 2 * kAttnQ;
 static_assert(kAttnD * kAttnTPitch <= kAttnLds, "transpose tile fits the staging area");
 static_assert(kAttnD == 128, "the task layout assumes 128-wide heads");
 
@@ -133,15 +135,17 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// One task: query tile qt of batch*head bh over every block of the ring.
-__device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, char *smem,
-                                          uint32_t *s_word) {
+// One task: query tile qt of batch*head bh over ring tiles [j0, j1) (tile j:
+// ring step j / tiles-per-block, key tile j % tiles-per-block).  With one
+// split the task covers the whole ring and stores o and lse; with two, the
+// halves of a (bh, qt) pair combine through the workspace (attn_merge).
+__device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, int j0, int j1,
+                                          char *smem, uint32_t *s_word) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int row0 = qt * kAttnQ + wave * 32;  // this wave's first query row
   const int tpb = p.S_kv / kAttnKT;          // tiles per block
-  const int n_tiles = p.world * tpb;
   const uint32_t base = lds_addr(smem);
   const int ldk = kAttnD * 2, ldv = p.S_kv * 2;
 
@@ -211,12 +215,12 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, c
     return wg_sync_ok(ok0, s_word, !p.light_acquire);
   };
 
-  if (!acquire(0)) return false;
-  stage_tile(0, 0);
-  for (int j = 0; j < n_tiles; ++j) {
+  if (!acquire(j0)) return false;
+  stage_tile(j0, j0 & 1);
+  for (int j = j0; j < j1; ++j) {
     wait_vmcnt<0>();
     wg_barrier();  // tile j landed; every wave is done with the other buffer
-    if (j + 1 < n_tiles) {
+    if (j + 1 < j1) {
       if (!acquire(j + 1)) return false;  // timeout or abort: nothing is in flight here
       stage_tile(j + 1, (j + 1) & 1);
     }
@@ -297,10 +301,75 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, c
     }
   }
   wg_barrier();  // both buffers are free for the next task
-  // finish: row sums over the 4 lane groups, O / l, lse = (m + log2 l) ln 2
+  // row sums over the 4 lane groups; then store, or combine with the other half
+  float lrow[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) lrow[mb] = xor_sum(xor_sum(lpart[mb], 16), 32);
+  if (p.splits == 2) {
+    // (bh, qt) pair: the first half to finish writes its unnormalised O, row
+    // max and row sum and releases the pair's flag; the second combines.
+    const uint32_t pair = (uint32_t)(qt * p.BH + bh);
+    const uint32_t f = p.merge_flag0 + pair;
+    float *slot = p.ws + (size_t)pair * kAttnSlot;
+    bool first = false;
+    if (threadIdx.x == 0) first = add_acq_rel(cnt_ptr(p.sync, f), 1u) == 0u;
+    first = wg_broadcast(first, s_word);
+    if (first) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int lr = wave * 32 + mb * 16 + r16;  // row within the tile
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          *reinterpret_cast<f32x4_t *>(slot + lr * kAttnD + db * 16 + 4 * g) = oacc[mb][db];
+        if (g == 0) {
+          slot[kAttnQ * kAttnD + lr] = mrow[mb];
+          slot[kAttnQ * kAttnD + kAttnQ + lr] = lrow[mb];
+        }
+      }
+      wait_stores();
+      __syncthreads();
+      if (threadIdx.x == 0) st_release(flag_ptr(p.sync, f), p.sync.epoch);
+      return true;
+    }
+    bool ok0 = true;
+    if (threadIdx.x == 0) {
+      st_relaxed(cnt_ptr(p.sync, f), 0u);  // for the next launch
+      ok0 = spin_until_eq(p.sync, flag_ptr(p.sync, f), p.sync.epoch, f);
+    }
+    if (!wg_sync_ok(ok0, s_word, !p.light_acquire)) return false;
+    // combine: the same operations whichever half finished first (products
+    // then one commutative add, no contraction into fma), so the bits do not
+    // depend on the order
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma clang fp contract(off)
+      const int lr = wave * 32 + mb * 16 + r16;
+      const float mo = slot[kAttnQ * kAttnD + lr], lo = slot[kAttnQ * kAttnD + kAttnQ + lr];
+      const float m = fmaxf(mrow[mb], mo);
+      const float a = __builtin_amdgcn_exp2f(mrow[mb] - m), b = __builtin_amdgcn_exp2f(mo - m);
+      const float l = lrow[mb] * a + lo * b;
+      const float inv = 1.f / l;
+      const int row = qt * kAttnQ + lr;
+      if (row < p.S_q) {
+        uint16_t *orow = p.o + ((size_t)bh * p.S_q + row) * kAttnD;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const f32x4_t w = *reinterpret_cast<const f32x4_t *>(slot + lr * kAttnD + db * 16 + 4 * g);
+          const f32x4_t v = oacc[mb][db];
+          float x[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = (v[r] * a + w[r] * b) * inv;
+          *reinterpret_cast<uint2 *>(orow + db * 16 + 4 * g) = pack_bf16x4(x[0], x[1], x[2], x[3]);
+        }
+        if (g == 0) p.lse[(size_t)bh * p.S_q + row] = (m + __log2f(l)) * 0.69314718055994530942f;
+      }
+    }
+    return true;
+  }
+  // O / l, lse = (m + log2 l) ln 2
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const float l = xor_sum(xor_sum(lpart[mb], 16), 32);
+    const float l = lrow[mb];
     const float inv = 1.f / l;
     const int row = row0 + mb * 16 + r16;
     if (row < p.S_q) {
@@ -336,7 +405,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnParams p) {
       // consume the ring's blocks in the order they land
       const uint32_t t = next_index(&ctrl->tile_ctr, &s_word);
       if (t >= (uint32_t)p.n_tasks) break;
-      if (!attn_task(p, (int)t % p.BH, (int)t / p.BH, smem, &s_word)) break;
+      // every first half before any second half: the first round covers the
+      // early ring steps, and the late steps have longer to land
+      const int half = (int)(t / (uint32_t)p.n_pairs), pair = (int)(t % (uint32_t)p.n_pairs);
+      const int n_tiles = p.world * (p.S_kv / kAttnKT);
+      const int j0 = half * n_tiles / p.splits, j1 = (half + 1) * n_tiles / p.splits;
+      if (!attn_task(p, pair % p.BH, pair / p.BH, j0, j1, smem, &s_word)) break;
     }
   }
   finish_launch(p.sync);

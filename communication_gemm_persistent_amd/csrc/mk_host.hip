@@ -35,6 +35,7 @@ struct mk_ctx {
   uint64_t timeout_ticks = 0;
   int force_tile = 0;  // MK_TILE env: 128 or 256 forces the tile edge
   bool no_slabs = true;   // MK_NO_SLABS=0 env: cut AllGather land blocks into K-slabs
+  int ring_splits = 0;  // MK_RING_SPLITS=1: one task per (head, query tile) (0: library choice)
   int tile_map = -1;  // MK_TILE_MAP env: 0 global m-major order, 1 XCD blocks, 2 XCD strided, 3 XCD rounds (-1: per op)
   int item_kib = 256;  // MK_ITEM_KIB env: target size of one AllGather land item
   int help_every = 0;  // MK_HELP_EVERY env: 1 in this many compute workgroups helps land (0: automatic)
@@ -282,6 +283,7 @@ mk_status mk_create(mk_handle *out, const mk_config *cfg) {
   h->timeout_ticks = (uint64_t)khz * (uint64_t)h->timeout_ms;
   if (const char *t = std::getenv("MK_TILE")) h->force_tile = std::atoi(t);
   if (const char *t = std::getenv("MK_NO_SLABS")) h->no_slabs = std::atoi(t) != 0;
+  if (const char *t = std::getenv("MK_RING_SPLITS")) h->ring_splits = std::atoi(t) == 1 ? 1 : 0;
   if (const char *t = std::getenv("MK_TILE_MAP")) h->tile_map = std::min(3, std::max(0, std::atoi(t)));
   if (const char *t = std::getenv("MK_ITEM_KIB")) h->item_kib = std::min(4096, std::max(4, std::atoi(t)));
   if (const char *t = std::getenv("MK_HELP_EVERY")) h->help_every = std::max(1, std::atoi(t));
@@ -836,8 +838,20 @@ mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, 
   p.chunks = cdiv(S_kv, p.chunk_keys);
   p.n_items = world * BH * p.chunks;
   p.q_tiles = cdiv(S_q, 128);
-  p.n_tasks = BH * p.q_tiles;
-  if (p.n_tasks >= (1 << 30)) return fail(h, MK_ERR_UNSUPPORTED, "too many attention tasks");
+  p.n_pairs = BH * p.q_tiles;
+  if (p.n_pairs >= (1 << 29)) return fail(h, MK_ERR_UNSUPPORTED, "too many attention tasks");
+  // two tasks per (bh, q-tile), one per half of the ring's key tiles, when
+  // there are two tiles and flags for the pairs: smaller tasks balance the
+  // workgroups that join after landing
+  const long n_tiles = (long)world * (S_kv / 64);
+  p.splits = (h->ring_splits != 1 && n_tiles >= 2 && (long)p.n_items + p.n_pairs <= mk::kMaxFlags) ? 2 : 1;
+  p.n_tasks = p.splits * p.n_pairs;
+  p.merge_flag0 = (uint32_t)p.n_items;
+  if (p.splits == 2) {
+    const size_t slot = (size_t)(128 * 128 + 2 * 128) * sizeof(float);
+    if ((st = ensure_ws(h, slot * p.n_pairs)) != MK_OK) return st;
+    p.ws = static_cast<float *>(h->ws);
+  }
   // chunks of both receive buffers start and end on 128-byte lines
   p.light_acquire = ((reinterpret_cast<uintptr_t>(p.k_recv) | reinterpret_cast<uintptr_t>(p.vt_recv)) & 127u) == 0 ? 1 : 0;
 
@@ -855,7 +869,7 @@ mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, 
   p.n_land = land;
   p.n_compute = compute;
   const int grid = std::max(1, land + compute);
-  p.sync = make_sync(h, (uint32_t)p.n_items);
+  p.sync = make_sync(h, (uint32_t)(p.n_items + (p.splits == 2 ? p.n_pairs : 0)));
   hipError_t e = mk::launch_attn(p, grid, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(h, e, "launching the ring attention kernel");
   record(h, MK_OP_RING_ATTN, land, compute, 0, grid);

@@ -84,6 +84,9 @@ struct AttnParams {
   int q_tiles, n_tasks, n_items;
   int light_acquire;
   int prelanded;                          // receive buffers already hold every block
+  int splits, n_pairs;                    // tasks per (bh, q-tile) pair: 1, or 2 ring halves
+  uint32_t merge_flag0;                   // flag / counter of pair i: merge_flag0 + i
+  float *ws;                              // splits == 2: one combine slot per pair
 };
 
 // MoE dispatch + grouped GEMM.  Route items are blocks of kRouteTokens

@@ -181,3 +181,24 @@ def test_ring_attention_prelanded_equals_fused(handle, mk):
     handle.sync()
     O.assert_bits_equal(bits(o2), bits(o1), "o (pre-landed)")
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), "lse (pre-landed)"
+
+
+def test_ring_attention_one_task_per_query_tile(mk):
+    """MK_RING_SPLITS=1 (no split of the ring into two combined halves) is
+    checked against the oracle like the default."""
+    import os
+    os.environ["MK_RING_SPLITS"] = "1"
+    try:
+        h = mk.Handle(0, spin_timeout_ms=10000)
+    finally:
+        del os.environ["MK_RING_SPLITS"]
+    try:
+        W, rank, B, H, S_q, S_kv = 3, 2, 1, 2, 200, 192
+        d = I.gen_ring(W, B, H, S_q, S_kv, D, config=540)
+        out = run_ring(h, d, rank=rank)
+        ref = O.ring_attention(d["q"], d["k"], d["v"], rank=rank, scale=float(np.float32(1 / np.sqrt(D))))
+        check_recv(d, out)
+        O.assert_close_bf16(out["o"], ref["o"], "o (one task per query tile)")
+        lse_close(out["lse"], ref["lse"])
+    finally:
+        h.close()
