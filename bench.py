@@ -18,6 +18,7 @@ Also measured and reported in the same JSON line (context, not the value):
   * the fused call with the 256 MB Infinity Cache flushed before each step;
   * GEMM+ReduceScatter, GEMM+AllReduce and MoE dispatch + grouped GEMM at
     their workload sizes (--quick skips these);
+  * measured ceilings: an MFMA-only loop (TFLOP/s) and a plain device copy;
   * the CPU oracle timed on a bounded sample of the same workload.
 Exactly one JSON line goes to stdout; progress goes to stderr.
 """
@@ -208,6 +209,23 @@ def main() -> int:
             "pcie_read_GBps": round(landed_bytes / (t_xfer_host * 1e-3) / 1e9, 2),
             "efficiency": round(max(t_gemm, t_xfer_host) / t_fused_host, 4)}
 
+    # measured ceilings beside the nominal ones: an MFMA-only loop and a plain
+    # device copy (the PCIe rate of in-kernel host reads is in --extra)
+    log("[bench] measured ceilings")
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    mfma_flop = [0.0]
+
+    def mfma_loop():
+        mfma_flop[0] = h.mfma_ceiling(2000, sink)
+
+    t_mfma = float(np.median(time_calls(mfma_loop, 5, 2)))
+    cp_src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    t_copy = float(np.median(time_calls(lambda: cp_dst.copy_(cp_src), 10, 2)))
+    del cp_src, cp_dst
+    ceilings = {"mfma_loop_tflops": round(mfma_flop[0] / (t_mfma * 1e-3) / 1e12, 1),
+                "copy_read_plus_write_GBps": round(2 * COPY_BYTES / (t_copy * 1e-3) / 1e9, 1)}
+
     src_hash = kernel_source_hash()
     traffic = traffic_from_profile(src_hash)
     achieved = flops / (kern_avg * 1e-3) / 1e12
@@ -228,6 +246,7 @@ def main() -> int:
                    "m": W * m_s, "n": n, "k": k, "peers": "separate HBM region",
                    "roles": {"land": roles_fused[0], "compute": roles_fused[1]},
                    "grid": grid_fused},
+        "ceilings": dict(ceilings, fused_frac_of_mfma_loop=round(achieved / ceilings["mfma_loop_tflops"], 4)),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_avg_ms": round(kern_avg, 4),

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmk.so")
-SOURCES = ["mk_host.hip", "mk_kernels.hip", "mk_moe.hip", "mk_attn.hip"]
+SOURCES = ["mk_host.hip", "mk_kernels.hip", "mk_moe.hip", "mk_attn.hip", "mk_ceiling.hip"]
 ARCH = "gfx950"
 
 

@@ -26,6 +26,7 @@ hipError_t occupancy(int op, int bm, int bn, int *blocks_per_cu);
 hipError_t occupancy_moe(int bm, int *blocks_per_cu);
 hipError_t launch_attn(const AttnParams &p, int grid, hipStream_t s);
 hipError_t occupancy_attn(int *blocks_per_cu);
+hipError_t launch_mfma_loop(int grid, int iters, float *sink, hipStream_t s);
 }  // namespace mk
 
 struct mk_ctx {
@@ -873,6 +874,23 @@ mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, 
   hipError_t e = mk::launch_attn(p, grid, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(h, e, "launching the ring attention kernel");
   record(h, MK_OP_RING_ATTN, land, compute, 0, grid);
+  return MK_OK;
+}
+
+// ---------------------------------------------------------------- measurement aid
+
+mk_status mk_mfma_ceiling(mk_handle h, mk_stream stream, int iters, float *sink) {
+  if (!h) return MK_ERR_INVALID;
+  h->err.clear();
+  if (iters < 1 || iters > (1 << 24)) return fail(h, MK_ERR_INVALID, "iters out of range");
+  DeviceGuard g(h->device);
+  const void *dp;
+  mk_status st;
+  if ((st = resolve(h, sink, false, &dp, "sink")) != MK_OK) return st;
+  // two 256-thread workgroups per CU: 2 waves per SIMD
+  hipError_t e = mk::launch_mfma_loop(2 * h->cu_count, iters, static_cast<float *>(const_cast<void *>(dp)),
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(h, e, "launching the MFMA loop");
   return MK_OK;
 }
 

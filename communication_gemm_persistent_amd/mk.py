@@ -41,7 +41,7 @@ MAX_WORLD = 16
 EXPORTS = ("mk_create", "mk_destroy", "mk_set_roles", "mk_get_roles", "mk_last_launch",
            "mk_sync", "mk_status_string", "mk_last_error", "mk_ag_gemm", "mk_gemm_rs",
            "mk_gemm_ar", "mk_moe_dispatch_gemm", "mk_moe_dispatch_gemm_combine",
-           "mk_ring_attention")
+           "mk_ring_attention", "mk_mfma_ceiling")
 
 
 class MkError(RuntimeError):
@@ -93,6 +93,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_gemm_ar.argtypes = [_vp, _vp, _i, _i, _vp, _vp, _pp, _vp, _pp, _i, _i, _i, _i, _u]
     lib.mk_moe_dispatch_gemm.argtypes = [_vp, _vp, _i, _i, _pp, _pp, _vp, _i, _i, _i, _i, _i, _i,
                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _u]
+    lib.mk_mfma_ceiling.argtypes = [_vp, _vp, _i, _vp]
     lib.mk_ring_attention.argtypes = [_vp, _vp, _i, _i, _vp, _pp, _pp, _i, _i, _i, _i,
                                       ctypes.c_float, _vp, _vp, _vp, _vp, _u]
     lib.mk_moe_dispatch_gemm_combine.argtypes = [
@@ -293,6 +294,14 @@ class Handle:
             _ptr(y_peer, "y_peer", _BF16, (T * top_k, N)), _ptr_array(rp),
             _ptr(out, "out", _BF16, (T, N)), flags)
         self._check(st, "mk_moe_dispatch_gemm_combine", self.h)
+
+    def mfma_ceiling(self, iters: int, sink: torch.Tensor, stream=None) -> float:
+        """Launch the MFMA-only loop; returns its FLOP count (time it with events)."""
+        st = self.lib.mk_mfma_ceiling(self.h, _vp(_stream(stream, self.device)), iters,
+                                      _ptr(sink, "sink", (torch.float32,)))
+        self._check(st, "mk_mfma_ceiling", self.h)
+        props = torch.cuda.get_device_properties(self.device)
+        return 2.0 * props.multi_processor_count * 4 * iters * 8 * 32768
 
     def ring_attention(self, q: torch.Tensor, k_src: Sequence[torch.Tensor],
                        v_src: Sequence[torch.Tensor], o: torch.Tensor, lse: torch.Tensor,

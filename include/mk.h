@@ -282,6 +282,17 @@ mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, 
                             int S_q, int S_kv, int D, float scale, mk_bf16 *o, float *lse,
                             mk_bf16 *k_recv, mk_bf16 *vt_recv, unsigned flags);
 
+/*
+ * Measurement aid (not part of the fused path): a loop of independent bf16
+ * 32x32x16 MFMAs with no memory traffic on 2 workgroups of 256 threads per CU,
+ * 8 accumulators per wave, iters rounds of 8 MFMAs (32768 FLOP each) per wave:
+ * 2 * cu_count * 4 waves * iters * 8 * 32768 FLOP in all.  Timing it gives the
+ * practical dense bf16 MFMA ceiling the fused kernels are compared with.
+ *   sink   device memory of at least 256 floats (written, values meaningless)
+ *   1 <= iters <= 2^24
+ */
+mk_status mk_mfma_ceiling(mk_handle h, mk_stream stream, int iters, float *sink);
+
 #ifdef __cplusplus
 }
 #endif

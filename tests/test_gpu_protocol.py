@@ -139,3 +139,18 @@ def test_two_handles_interleaved_on_one_stream(mk):
         h2.sync()
     O.assert_bits_equal(bits(c1), ref, "handle 1")
     O.assert_bits_equal(bits(c2), ref, "handle 2")
+
+
+def test_mfma_ceiling_loop_runs(mk):
+    """The measurement aid launches, completes and reports its FLOP count."""
+    import torch
+    h = mk.Handle(0)
+    try:
+        sink = torch.full((256,), float("nan"), dtype=torch.float32, device="cuda")
+        flop = h.mfma_ceiling(4, sink)
+        h.sync()
+        props = torch.cuda.get_device_properties(0)
+        assert flop == 2.0 * props.multi_processor_count * 4 * 4 * 8 * 32768
+        assert torch.isfinite(sink[: min(256, 2 * props.multi_processor_count)]).all()
+    finally:
+        h.close()

@@ -20,7 +20,7 @@ def declared():
 def test_header_declares_the_entry_points():
     names = declared()
     for want in ("mk_create", "mk_destroy", "mk_ag_gemm", "mk_gemm_rs", "mk_gemm_ar",
-                 "mk_moe_dispatch_gemm", "mk_moe_dispatch_gemm_combine", "mk_ring_attention", "mk_sync", "mk_status_string"):
+                 "mk_moe_dispatch_gemm", "mk_moe_dispatch_gemm_combine", "mk_ring_attention", "mk_mfma_ceiling", "mk_sync", "mk_status_string"):
         assert want in names
 
 
