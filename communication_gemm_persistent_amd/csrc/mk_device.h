@@ -530,11 +530,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // a spill with v_readlane) needs 5; the library's build is checked for that
 // pattern instead (an s_nop 4 here slows the MFMA stream the DMAs are
 // interleaved with).
+// PAD: 5 wait states in front instead of 1, for DMAs outside the MFMA
+// loop, where the compiler may restore a spilled descriptor SGPR with
+// v_readlane right before the asm (a vector memory read of a VALU-written
+// SGPR needs 5 wait states, and the compiler does not see asm operands).
+template <bool PAD = false>
 __device__ __forceinline__ void dma16(i32x4_t vdesc, uint32_t m0_base, uint32_t voff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(vdesc), "{m0}"(m0_base)
-               : "memory");
+  if constexpr (PAD)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(vdesc), "{m0}"(m0_base)
+                 : "memory");
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(vdesc), "{m0}"(m0_base)
+                 : "memory");
 }
 
 // One 4-byte-per-lane global->LDS DMA (lane l's word lands at m0_base + 4 l).
@@ -740,11 +751,12 @@ __device__ __forceinline__ int dma_chunk(int lane, int par) { return (lane & 7) 
 // operand's region of a stage plus 1024 g).  lane_off is the lane's offset
 // for g's parity; chunks at or past K and rows past the descriptor's range
 // read as zero.  k0 >= K fetches zeros only (no memory is touched).
+template <bool PAD = false>
 __device__ __forceinline__ void dma_row_group(i32x4_t vdesc, uint32_t lds_rows, uint32_t lane_off,
                                               int lane_c8, int ld_bytes, int k0, int K, int g) {
   const uint32_t uni = (uint32_t)__builtin_amdgcn_readfirstlane(g * 8 * ld_bytes + k0 * 2);
   const uint32_t off = lane_c8 < K - k0 ? lane_off + uni : kOOB;
-  dma16(vdesc, __builtin_amdgcn_readfirstlane(lds_rows), off);
+  dma16<PAD>(vdesc, __builtin_amdgcn_readfirstlane(lds_rows), off);
 }
 
 // Gate of a tile whose A rows arrive during the K loop in K-slabs of
@@ -831,6 +843,11 @@ __device__ __forceinline__ void gemm_tile_pingpong(
                   (own ? lds_own : lds_oth) + (stage & 1) * C::STAGE_BYTES + d * 1024,
                   lane_off[d & 1], lane_c8[d & 1], ld, stage * kBK, K, rg + d);
   };
+  auto fetch_padded = [&](bool own, int stage, int d) {  // prologue: see dma16
+    dma_row_group<true>(own ? v_own : v_oth,
+                        (own ? lds_own : lds_oth) + (stage & 1) * C::STAGE_BYTES + d * 1024,
+                        lane_off[d & 1], lane_c8[d & 1], ld, stage * kBK, K, rg + d);
+  };
   // slab gate: wave 0 fetches the flag of the slab starting at stage u into
   // an LDS slot in MEMORY(u-3) (completed by its wait at the end of
   // COMPUTE(u-3)) and reads it in MEMORY(u-2), before the barrier after
@@ -847,11 +864,11 @@ __device__ __forceinline__ void gemm_tile_pingpong(
   }
   // prologue, in the order the loop's waits expect: own 0, other 0, own 1
 #pragma unroll
-  for (int d = 0; d < R; ++d) fetch(true, 0, d);
+  for (int d = 0; d < R; ++d) fetch_padded(true, 0, d);
 #pragma unroll
-  for (int d = 0; d < R; ++d) fetch(false, 0, d);
+  for (int d = 0; d < R; ++d) fetch_padded(false, 0, d);
 #pragma unroll
-  for (int d = 0; d < R; ++d) fetch(true, 1, d);
+  for (int d = 0; d < R; ++d) fetch_padded(true, 1, d);
   wait_vmcnt<R>();                    // stage 0 landed
   phase_barrier();
   if (!g0) phase_barrier();           // group 1 starts one phase late
@@ -938,58 +955,119 @@ __device__ __forceinline__ f32x4_t acc_group(const A &v, int g) {
   return f32x4_t{v[g * 4 + 0], v[g * 4 + 1], v[g * 4 + 2], v[g * 4 + 3]};
 }
 
-// Epilogue through LDS.  The accumulator tile passes through LDS in blocks
-// of kEpiRows rows; every thread then takes 4 consecutive columns of a row,
-// so each wave instruction covers a whole row (1 KiB of fp32 for BN = 256)
-// and the epilogue's global loads and stores are fully contiguous.  LDS rows
-// are padded by 16 bytes so the 32 rows one accumulator write spans fall in
-// distinct bank groups.  f(row, col, v) is called for every 4-column group
-// (row, col relative to the tile) of the tile, each exactly once.
-constexpr int kEpiRows = 64;
+// Epilogue through LDS.  Block b holds accumulator row-block b of every
+// wave: 32 rows from each of the WAVES_M wave rows, EpiCfg::ROWS in all
+// (LDS row 32 u + l is tile row u WM + 32 b + l).  Every thread then takes
+// 4 consecutive columns of an LDS row, so each wave instruction covers a
+// whole row (1 KiB of fp32 for BN = 256) and the epilogue's global loads and
+// stores are fully contiguous.  Indexing blocks by the accumulator index
+// keeps every LDS write at one per-lane base plus an immediate offset and
+// lets each block's accumulators die once written, so nothing is spilled.
+// LDS rows are padded by 16 bytes so the 32 rows one accumulator write
+// spans fall in distinct bank groups.  f(row, col, v) is called for every
+// 4-column group (row, col relative to the tile) of the tile, each exactly
+// once.
+template <int BM, int BN>
+struct EpiCfg {
+  using C = TileCfg<BM, BN>;
+  static constexpr int ROWS = C::WAVES_M * 32;  // LDS rows per block
+  static constexpr int PITCH = BN * 4 + 16;
+  static constexpr int CHUNKS = ROWS * (BN / 4);
+};
+
+// Accumulator row-block b of this wave into the LDS block at wp (the
+// lane's position, set up by the staged epilogues).
+template <int BM, int BN>
+__device__ __forceinline__ void epi_write_block(const AccTile<BM, BN> &acc, int b, char *wp) {
+  using C = TileCfg<BM, BN>;
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4_t v;
+      v[0] = acc[b][j][g * 4 + 0];
+      v[1] = acc[b][j][g * 4 + 1];
+      v[2] = acc[b][j][g * 4 + 2];
+      v[3] = acc[b][j][g * 4 + 3];
+      *reinterpret_cast<f32x4_t *>(wp + (j * 32 + g * 8) * 4) = v;
+    }
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ char *epi_lane_pos(char *smem) {
+  using C = TileCfg<BM, BN>;
+  using E = EpiCfg<BM, BN>;
+  static_assert(C::MFMA == 32, "accumulator layout of the 32x32 MFMA tiles");
+  static_assert(E::ROWS * E::PITCH <= 2 * C::STAGE_BYTES, "epilogue block must fit the LDS stages");
+  static_assert(E::CHUNKS % C::THREADS == 0, "chunks split evenly over threads");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  return smem + (wm * 32 + (lane & 31)) * E::PITCH + (wn * C::WN + (lane >> 5) * 4) * 4;
+}
 
 template <int BM, int BN, class F>
 __device__ __forceinline__ void staged_epilogue(const AccTile<BM, BN> &acc, char *smem, F &&f) {
   using C = TileCfg<BM, BN>;
-  static_assert(C::MFMA == 32, "accumulator layout of the 32x32 MFMA tiles");
-  constexpr int PITCH = BN * 4 + 16;
-  static_assert(kEpiRows * PITCH <= 2 * C::STAGE_BYTES, "epilogue block must fit the LDS stages");
-  static_assert(BM % kEpiRows == 0 && kEpiRows % 32 == 0, "epilogue blocks of whole MFMA rows");
-  constexpr int CHUNKS = kEpiRows * (BN / 4);
-  static_assert(CHUNKS % C::THREADS == 0, "chunks split evenly over threads");
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  using E = EpiCfg<BM, BN>;
+  char *wp = epi_lane_pos<BM, BN>(smem);
 #pragma unroll
-  for (int r0 = 0; r0 < BM; r0 += kEpiRows) {
+  for (int b = 0; b < C::FM; ++b) {
     wg_barrier();  // the previous block's reads (or the K loop's) are done
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-      const int row0 = wm * C::WM + i * 32;
-      if (row0 < r0 || row0 >= r0 + kEpiRows) continue;
-      char *rp = smem + (row0 - r0 + (lane & 31)) * PITCH;
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = wn * C::WN + j * 32 + g * 8 + (lane >> 5) * 4;
-          f32x4_t v;
-          v[0] = acc[i][j][g * 4 + 0];
-          v[1] = acc[i][j][g * 4 + 1];
-          v[2] = acc[i][j][g * 4 + 2];
-          v[3] = acc[i][j][g * 4 + 3];
-          *reinterpret_cast<f32x4_t *>(rp + col * 4) = v;
-        }
-    }
+    epi_write_block<BM, BN>(acc, b, wp);
     wg_barrier();
-#pragma unroll
-    for (int k = 0; k < CHUNKS / C::THREADS; ++k) {
+    // kept rolled: f is inlined once per block, so the epilogue stays small
+    // enough for the instruction cache
+#pragma unroll 1
+    for (int k = 0; k < E::CHUNKS / C::THREADS; ++k) {
       const int idx = (int)threadIdx.x + k * C::THREADS;
       const int rr = idx / (BN / 4), c4 = idx % (BN / 4);
-      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(smem + rr * PITCH + c4 * 16);
-      f(r0 + rr, c4 * 4, v);
+      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(smem + rr * E::PITCH + c4 * 16);
+      f((rr >> 5) * C::WM + b * 32 + (rr & 31), c4 * 4, v);
     }
   }
   wg_barrier();  // LDS is free again for the next tile's stages
+}
+
+// The staged epilogue for epilogues that read global memory per 4-column
+// group: pre(row, col) issues those loads and returns their registers,
+// f(row, col, v, loaded) finishes the group.  The loads of the next group
+// are issued before the current group's stores: on gfx9 a wait for a load
+// also waits for every store issued before it, so loading after storing
+// would cost one memory round trip per group.
+template <int BM, int BN, class Pre, class F>
+__device__ __forceinline__ void staged_epilogue_pf(const AccTile<BM, BN> &acc, char *smem, Pre &&pre,
+                                                   F &&f) {
+  using C = TileCfg<BM, BN>;
+  using E = EpiCfg<BM, BN>;
+  constexpr int NK = E::CHUNKS / C::THREADS;
+  static_assert(NK % 2 == 0, "column groups are taken in pairs");
+  char *wp = epi_lane_pos<BM, BN>(smem);
+  // THREADS is a multiple of BN / 4: a thread keeps its column group
+  const int c4 = (int)threadIdx.x % (BN / 4);
+  const int rr0 = (int)threadIdx.x / (BN / 4);
+  constexpr int RSTEP = C::THREADS / (BN / 4);
+#pragma unroll
+  for (int b = 0; b < C::FM; ++b) {
+    wg_barrier();
+    epi_write_block<BM, BN>(acc, b, wp);
+    wg_barrier();
+    auto row_of = [&](int rr) { return (rr >> 5) * C::WM + b * 32 + (rr & 31); };
+    auto lds_val = [&](int rr) { return *reinterpret_cast<const f32x4_t *>(smem + rr * E::PITCH + c4 * 16); };
+    // two register sets in turn, never copied (a copy of registers a load
+    // is still filling waits for that load); the prefetch past the block's
+    // last group asks for rows past the tile, which pre() does not load
+    auto ra = pre(row_of(rr0), c4 * 4);
+#pragma unroll 1
+    for (int k = 0; k < NK; k += 2) {
+      const int rr = rr0 + k * RSTEP;
+      auto rb = pre(row_of(rr + RSTEP), c4 * 4);
+      f(row_of(rr), c4 * 4, lds_val(rr), ra);
+      ra = pre(k + 2 < NK ? row_of(rr + 2 * RSTEP) : BM, c4 * 4);
+      f(row_of(rr + RSTEP), c4 * 4, lds_val(rr + RSTEP), rb);
+    }
+  }
+  wg_barrier();
 }
 
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
@@ -999,6 +1077,33 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
   v[2] = (__bf16)c;
   v[3] = (__bf16)d;
   return *reinterpret_cast<uint2 *>(&v);
+}
+
+// Store a tile's accumulators as bf16 (RNE) straight from their register
+// layout: 8-byte stores of 4 consecutive columns into the matrix at base
+// (row pitch ld elements), the tile's element (r, c) going to row row0 + r,
+// column col0 + c, for rows below row1 and columns below col1 only.  No LDS
+// and no barrier, so the waves of a workgroup leave the tile as they finish
+// it.  Addresses are formed from the tile's origin, so no part of them is
+// invariant across tiles (hoisted out of the tile loop, such values would
+// hold registers through the K loop).
+template <int BM, int BN>
+__device__ __forceinline__ void store_tile_bf16(const AccTile<BM, BN> &acc, uint16_t *base, int ld,
+                                                int row0, int col0, int row1, int col1) {
+  using C = TileCfg<BM, BN>;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int g = 0; g < C::GROUPS; ++g) {
+        const AccPos<BM, BN> ps = acc_pos<BM, BN>(i, j, g);
+        const int row = row0 + ps.row, col = col0 + ps.col;
+        if (row < row1 && col < col1) {
+          const f32x4_t v = acc_group(acc[i][j], g);
+          *reinterpret_cast<uint2 *>(base + (size_t)row * ld + col) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+        }
+      }
 }
 
 }  // namespace mk

@@ -532,7 +532,7 @@ mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const m
     char what[32];
     std::snprintf(what, sizeof(what), "peer_part[%d]", q);
     if ((st = resolve(h, peer_part[q], true, &dp, what)) != MK_OK) return st;
-    p.peer[q] = static_cast<const float *>(dp);
+    p.peer_c[q < rank ? q : q - 1] = static_cast<const float *>(dp);
     std::snprintf(what, sizeof(what), "outbox[%d]", q);
     if ((st = resolve(h, outbox[q], true, &dp, what)) != MK_OK) return st;
     p.outbox[q] = static_cast<uint16_t *>(const_cast<void *>(dp));
@@ -590,7 +590,7 @@ mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const m
     char what[32];
     std::snprintf(what, sizeof(what), "peer_part[%d]", q);
     if ((st = resolve(h, peer_part[q], true, &dp, what)) != MK_OK) return st;
-    p.peer[q] = static_cast<const float *>(dp);
+    p.peer_c[q < rank ? q : q - 1] = static_cast<const float *>(dp);
   }
   for (int b = 0; b < n_bcast; ++b) {
     char what[32];

@@ -170,19 +170,7 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * ldb));
     AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc, gate);
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int g = 0; g < C::GROUPS; ++g) {
-          const AccPos<BM, BN> ps = acc_pos<BM, BN>(i, j, g);
-          const int row = m0 + ps.row, col = n0 + ps.col;
-          if (row < m1 && col < p.n) {
-            const f32x4_t v = acc_group(acc[i][j], g);
-            *reinterpret_cast<uint2 *>(p.c + (size_t)row * p.n + col) = pack_bf16x4(v[0], v[1], v[2], v[3]);
-          }
-        }
+    store_tile_bf16<BM, BN>(acc, p.c, p.n, m0, n0, m1, p.n);
     // this workgroup's share of the items later tiles need
     if constexpr (!PRE) {
       for (int i = 0; i < p.land_between; ++i) {
@@ -221,10 +209,104 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void ag_gemm_kernel(
   finish_launch(p.sync);
 }
 
+// ---------------------------------------------------------------- peer partials
+
+// One 4-column group of each of the np peers' fp32 partials (the compact
+// list, ascending rank).
+struct PeerRow {
+  f32x4_t v[MK_MAX_WORLD - 1];
+};
+
+__device__ __forceinline__ void load_peers(PeerRow &pr, const float *const *pc, int np, size_t off) {
+#pragma unroll
+  for (int i = 0; i < MK_MAX_WORLD - 1; ++i)
+    if (i < np) pr.v[i] = *reinterpret_cast<const f32x4_t *>(pc[i] + off);
+}
+
+// v + the peers' partials, in rank order.
+__device__ __forceinline__ f32x4_t sum_peers(const f32x4_t &v, const PeerRow &pr, int np) {
+  f32x4_t x = v;
+#pragma unroll
+  for (int i = 0; i < MK_MAX_WORLD - 1; ++i)
+    if (i < np) x += pr.v[i];
+  return x;
+}
+
+// The epilogues' pointer tables (compact peer list; RS outboxes by rank or
+// AR broadcast buffers), copied to LDS once per launch and read after each
+// tile's K loop.  Taken from the kernel arguments instead, they are loaded
+// into SGPRs at the start and held through the K loop, which then spills
+// its buffer descriptors to VGPR lanes; a descriptor restored right before
+// an LDS DMA violates the 5-wait-state rule for VALU-written SGPRs.
+struct PtrTable {
+  const float *peer[MK_MAX_WORLD];
+  uint16_t *dst[MK_MAX_WORLD];
+};
+
+__device__ __forceinline__ void fill_table(PtrTable *t, const float *const *peer, uint16_t *const *dst) {
+  if (threadIdx.x < MK_MAX_WORLD) {
+    t->peer[threadIdx.x] = peer[threadIdx.x];
+    t->dst[threadIdx.x] = dst[threadIdx.x];
+  }
+  __syncthreads();
+}
+
+template <class T>
+__device__ __forceinline__ T *table_ptr(T *const &slot) {
+  return static_cast<T *>(const_cast<void *>(uniform_ptr(slot)));
+}
+
+// The same for a peer count known at compile time, from the compact list
+// (ascending rank).  Every load is unconditional: loads behind uniform
+// branches leave the compiler unable to count them, and it then waits for
+// all memory traffic, the previous group's stores included, before using
+// any of them.
+template <int NP>
+struct PeerVals {
+  f32x4_t v[NP];
+};
+
+template <>
+struct PeerVals<0> {};
+
+template <int NP>
+__device__ __forceinline__ PeerVals<NP> load_peer_vals(const float *const *pc, size_t off) {
+  PeerVals<NP> r;
+  if constexpr (NP > 0) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) r.v[i] = *reinterpret_cast<const f32x4_t *>(pc[i] + off);
+  }
+  return r;
+}
+
+template <int NP>
+__device__ __forceinline__ f32x4_t add_peer_vals(const f32x4_t &v, const PeerVals<NP> &pv) {
+  f32x4_t x = v;
+  if constexpr (NP > 0) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) x += pv.v[i];
+  }
+  return x;
+}
+
+// body(std::integral_constant<int, NP>) for the peer counts with a
+// specialised epilogue (world 8, 4, 2 and 1); false for any other count.
+template <class Body>
+__device__ __forceinline__ bool with_peer_count(int np, Body &&body) {
+  switch (np) {
+    case 0: body(std::integral_constant<int, 0>{}); return true;
+    case 7: body(std::integral_constant<int, 7>{}); return true;
+    case 3: body(std::integral_constant<int, 3>{}); return true;
+    case 1: body(std::integral_constant<int, 1>{}); return true;
+    default: return false;
+  }
+}
+
 // ---------------------------------------------------------------- GEMM + ReduceScatter
 
 template <int BM, int BN>
-__device__ __forceinline__ void rs_compute(const RsParams &p, char *smem, uint32_t *s_word) {
+__device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &tab, char *smem,
+                                           uint32_t *s_word) {
   using C = TileCfg<BM, BN>;
   const int xcd = xcd_id();
   const int lda = p.k * 2;
@@ -241,27 +323,64 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, char *smem, uint32
     AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
     const int cols = min(BN, p.n - n0);
-    auto epi = [&](int r, int cc, const f32x4_t &v) {
-      const int row = m0 + r;
-      if (row >= m1 || cc >= cols) return;
-      const int q = row / p.ms;
+    // Row r of slice q: the own slice adds the peers' partials and goes to
+    // c_own, any other slice to outbox[q].
+    auto epi_row = [&](int row, int cc, const f32x4_t &v, int q, uint16_t *d) {
       const size_t off = (size_t)(row - q * p.ms) * p.n + n0 + cc;
       f32x4_t x = v;
       if (q == p.rank) {
-        // all peers' loads are issued before any is used
-        f32x4_t pv[MK_MAX_WORLD];
-#pragma unroll
-        for (int w = 0; w < MK_MAX_WORLD; ++w)
-          if (w < p.world && w != p.rank) pv[w] = *reinterpret_cast<const f32x4_t *>(p.peer[w] + off);
-#pragma unroll
-        for (int w = 0; w < MK_MAX_WORLD; ++w)
-          if (w < p.world && w != p.rank) x += pv[w];
-        *reinterpret_cast<uint2 *>(p.c_own + off) = pack_bf16x4(x[0], x[1], x[2], x[3]);
-      } else {
-        *reinterpret_cast<uint2 *>(p.outbox[q] + off) = pack_bf16x4(x[0], x[1], x[2], x[3]);
+        PeerRow pr;  // all peers' loads are issued before any is used
+        load_peers(pr, tab.peer, p.world - 1, off);
+        x = sum_peers(v, pr, p.world - 1);
       }
+      *reinterpret_cast<uint2 *>(d + off) = pack_bf16x4(x[0], x[1], x[2], x[3]);
     };
-    staged_epilogue<BM, BN>(acc, smem, epi);
+    // A tile inside one slice (every tile when the slice height is a
+    // multiple of BM) picks its destination once, with a scalar index.  A
+    // per-row pick indexes the parameter array with a vector index, which
+    // compiles to a vector load of the pointer whose wait also waits for
+    // every store before it: one memory round trip per row.
+    const int q0 = m0 / p.ms;
+    if ((m1 - 1) / p.ms == q0 && q0 == p.rank) {
+      // own slice: the peers' partials of the next column group are loaded
+      // before this one is stored
+      const int r0 = m0 - q0 * p.ms, rows = m1 - m0;
+      auto put = [&](int r, int cc, const f32x4_t &x) {
+        if (r < rows && cc < cols)
+          *reinterpret_cast<uint2 *>(p.c_own + (size_t)(r0 + r) * p.n + n0 + cc) = pack_bf16x4(x[0], x[1], x[2], x[3]);
+      };
+      // addresses clamped into the tile: a group past its edge loads an
+      // element of the tile that it does not use, so no load needs a branch
+      auto off_in = [&](int r, int cc) { return (size_t)(r0 + min(r, rows - 1)) * p.n + n0 + min(cc, cols - 4); };
+      if (!with_peer_count(p.world - 1, [&](auto np) {
+            constexpr int NP = decltype(np)::value;
+            const float *pc[NP > 0 ? NP : 1];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) pc[i] = table_ptr(tab.peer[i]);
+            staged_epilogue_pf<BM, BN>(
+                acc, smem, [&](int r, int cc) { return load_peer_vals<NP>(pc, off_in(r, cc)); },
+                [&](int r, int cc, const f32x4_t &v, const PeerVals<NP> &pv) { put(r, cc, add_peer_vals<NP>(v, pv)); });
+          }))
+        staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
+          if (r < rows && cc < cols) {
+            PeerRow pr;
+            load_peers(pr, tab.peer, p.world - 1, off_in(r, cc));
+            put(r, cc, sum_peers(v, pr, p.world - 1));
+          }
+        });
+    } else if ((m1 - 1) / p.ms == q0) {
+      uint16_t *d0 = table_ptr(tab.dst[q0]);
+      staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
+        if (r < m1 - m0 && cc < cols) epi_row(m0 + r, cc, v, q0, d0);
+      });
+    } else {
+      staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
+        const int row = m0 + r;
+        if (row >= m1 || cc >= cols) return;
+        const int q = row / p.ms;
+        epi_row(row, cc, v, q, q == p.rank ? p.c_own : tab.dst[q]);
+      });
+    }
   }
 }
 
@@ -269,15 +388,18 @@ template <int BM, int BN>
 __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_rs_kernel(RsParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
+  __shared__ PtrTable s_tab;
+  fill_table(&s_tab, p.peer_c, p.outbox);
   const uint32_t ticket = take_ticket(p.sync, &s_word);
-  if (ticket < (uint32_t)p.n_compute) rs_compute<BM, BN>(p, smem, &s_word);
+  if (ticket < (uint32_t)p.n_compute) rs_compute<BM, BN>(p, s_tab, smem, &s_word);
   finish_launch(p.sync);
 }
 
 // ---------------------------------------------------------------- GEMM + AllReduce
 
 template <int BM, int BN>
-__device__ __forceinline__ void ar_compute(const ArParams &p, char *smem, uint32_t *s_word) {
+__device__ __forceinline__ void ar_compute(const ArParams &p, const PtrTable &tab, char *smem,
+                                           uint32_t *s_word) {
   using C = TileCfg<BM, BN>;
   const int xcd = xcd_id();
   const int lda = p.k * 2;
@@ -293,25 +415,40 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, char *smem, uint32
     AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
     const int cols = min(BN, p.n - n0);
-    auto epi = [&](int r, int cc, const f32x4_t &v) {
-      const int row = m0 + r;
-      if (row >= m1 || cc >= cols) return;
-      const size_t off = (size_t)row * p.n + n0 + cc;
-      f32x4_t pv[MK_MAX_WORLD];
+    // the peers' partials of the next column group are loaded before this
+    // one is stored
+    const int rows = m1 - m0;
+    uint16_t *bc[MK_MAX_WORLD];
 #pragma unroll
-      for (int w = 0; w < MK_MAX_WORLD; ++w)
-        if (w < p.world && w != p.rank) pv[w] = *reinterpret_cast<const f32x4_t *>(p.peer[w] + off);
-      f32x4_t x = v;
-#pragma unroll
-      for (int w = 0; w < MK_MAX_WORLD; ++w)
-        if (w < p.world && w != p.rank) x += pv[w];
+    for (int b = 0; b < MK_MAX_WORLD; ++b)
+      if (b < p.n_bcast) bc[b] = table_ptr(tab.dst[b]);
+    auto put = [&](int r, int cc, const f32x4_t &x) {
+      if (r >= rows || cc >= cols) return;
+      const size_t off = (size_t)(m0 + r) * p.n + n0 + cc;
       const uint2 o = pack_bf16x4(x[0], x[1], x[2], x[3]);
       *reinterpret_cast<uint2 *>(p.c + off) = o;
 #pragma unroll
       for (int b = 0; b < MK_MAX_WORLD; ++b)
-        if (b < p.n_bcast) *reinterpret_cast<uint2 *>(p.bcast[b] + off) = o;
+        if (b < p.n_bcast) *reinterpret_cast<uint2 *>(bc[b] + off) = o;
     };
-    staged_epilogue<BM, BN>(acc, smem, epi);
+    // addresses clamped into the tile (see the ReduceScatter epilogue)
+    auto off_in = [&](int r, int cc) { return (size_t)(m0 + min(r, rows - 1)) * p.n + n0 + min(cc, cols - 4); };
+    if (!with_peer_count(p.world - 1, [&](auto np) {
+          constexpr int NP = decltype(np)::value;
+          const float *pc[NP > 0 ? NP : 1];
+#pragma unroll
+          for (int i = 0; i < NP; ++i) pc[i] = table_ptr(tab.peer[i]);
+          staged_epilogue_pf<BM, BN>(
+              acc, smem, [&](int r, int cc) { return load_peer_vals<NP>(pc, off_in(r, cc)); },
+              [&](int r, int cc, const f32x4_t &v, const PeerVals<NP> &pv) { put(r, cc, add_peer_vals<NP>(v, pv)); });
+        }))
+      staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
+        if (r < rows && cc < cols) {
+          PeerRow pr;
+          load_peers(pr, tab.peer, p.world - 1, off_in(r, cc));
+          put(r, cc, sum_peers(v, pr, p.world - 1));
+        }
+      });
   }
 }
 
@@ -319,8 +456,10 @@ template <int BM, int BN>
 __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_ar_kernel(ArParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
+  __shared__ PtrTable s_tab;
+  fill_table(&s_tab, p.peer_c, p.bcast);
   const uint32_t ticket = take_ticket(p.sync, &s_word);
-  if (ticket < (uint32_t)p.n_compute) ar_compute<BM, BN>(p, smem, &s_word);
+  if (ticket < (uint32_t)p.n_compute) ar_compute<BM, BN>(p, s_tab, smem, &s_word);
   finish_launch(p.sync);
 }
 

@@ -44,7 +44,7 @@ struct RsParams {
   Sync sync;
   const uint16_t *a;
   const uint16_t *bt;
-  const float *peer[MK_MAX_WORLD];
+  const float *peer_c[MK_MAX_WORLD];  // the world - 1 peers' partials, ascending rank
   uint16_t *c_own;
   uint16_t *outbox[MK_MAX_WORLD];
   int world, rank, m, n, k, ms;
@@ -57,7 +57,7 @@ struct ArParams {
   Sync sync;
   const uint16_t *a;
   const uint16_t *bt;
-  const float *peer[MK_MAX_WORLD];
+  const float *peer_c[MK_MAX_WORLD];  // the world - 1 peers' partials, ascending rank
   uint16_t *c;
   uint16_t *bcast[MK_MAX_WORLD];
   int world, rank, n_bcast, m, n, k;
