@@ -956,21 +956,21 @@ __device__ __forceinline__ f32x4_t acc_group(const A &v, int g) {
 }
 
 // Epilogue through LDS.  Block b holds accumulator row-block b of every
-// wave: 32 rows from each of the WAVES_M wave rows, EpiCfg::ROWS in all
-// (LDS row 32 u + l is tile row u WM + 32 b + l).  Every thread then takes
-// 4 consecutive columns of an LDS row, so each wave instruction covers a
-// whole row (1 KiB of fp32 for BN = 256) and the epilogue's global loads and
-// stores are fully contiguous.  Indexing blocks by the accumulator index
-// keeps every LDS write at one per-lane base plus an immediate offset and
-// lets each block's accumulators die once written, so nothing is spilled.
-// LDS rows are padded by 16 bytes so the 32 rows one accumulator write
-// spans fall in distinct bank groups.  f(row, col, v) is called for every
-// 4-column group (row, col relative to the tile) of the tile, each exactly
-// once.
+// wave: E = MFMA rows (32 or 16) from each of the WAVES_M wave rows,
+// EpiCfg::ROWS in all (LDS row E u + l is tile row u WM + E b + l).  Every
+// thread then takes 4 consecutive columns of an LDS row, so each wave
+// instruction covers whole rows (1 KiB of fp32 for BN = 256) and the
+// epilogue's global loads and stores are fully contiguous.  Indexing blocks
+// by the accumulator index keeps every LDS write at one per-lane base plus
+// an immediate offset and lets each block's accumulators die once written,
+// so nothing is spilled.  LDS rows are padded by 16 bytes so the rows one
+// accumulator write spans fall in distinct bank groups.  f(row, col, v) is
+// called for every 4-column group (row, col relative to the tile) of the
+// tile, each exactly once.
 template <int BM, int BN>
 struct EpiCfg {
   using C = TileCfg<BM, BN>;
-  static constexpr int ROWS = C::WAVES_M * 32;  // LDS rows per block
+  static constexpr int ROWS = C::WAVES_M * C::MFMA;  // LDS rows per block
   static constexpr int PITCH = BN * 4 + 16;
   static constexpr int CHUNKS = ROWS * (BN / 4);
 };
@@ -983,27 +983,22 @@ __device__ __forceinline__ void epi_write_block(const AccTile<BM, BN> &acc, int 
 #pragma unroll
   for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4_t v;
-      v[0] = acc[b][j][g * 4 + 0];
-      v[1] = acc[b][j][g * 4 + 1];
-      v[2] = acc[b][j][g * 4 + 2];
-      v[3] = acc[b][j][g * 4 + 3];
-      *reinterpret_cast<f32x4_t *>(wp + (j * 32 + g * 8) * 4) = v;
-    }
+    for (int g = 0; g < C::GROUPS; ++g)
+      *reinterpret_cast<f32x4_t *>(wp + (j * C::MFMA + g * 8) * 4) = acc_group(acc[b][j], g);
 }
 
 template <int BM, int BN>
 __device__ __forceinline__ char *epi_lane_pos(char *smem) {
   using C = TileCfg<BM, BN>;
   using E = EpiCfg<BM, BN>;
-  static_assert(C::MFMA == 32, "accumulator layout of the 32x32 MFMA tiles");
   static_assert(E::ROWS * E::PITCH <= 2 * C::STAGE_BYTES, "epilogue block must fit the LDS stages");
   static_assert(E::CHUNKS % C::THREADS == 0, "chunks split evenly over threads");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  return smem + (wm * 32 + (lane & 31)) * E::PITCH + (wn * C::WN + (lane >> 5) * 4) * 4;
+  // the lane's accumulator row and first column (see acc_pos)
+  return smem + (wm * C::MFMA + (lane & (C::MFMA - 1))) * E::PITCH +
+         (wn * C::WN + (lane / C::MFMA) * 4) * 4;
 }
 
 template <int BM, int BN, class F>
@@ -1023,7 +1018,7 @@ __device__ __forceinline__ void staged_epilogue(const AccTile<BM, BN> &acc, char
       const int idx = (int)threadIdx.x + k * C::THREADS;
       const int rr = idx / (BN / 4), c4 = idx % (BN / 4);
       const f32x4_t v = *reinterpret_cast<const f32x4_t *>(smem + rr * E::PITCH + c4 * 16);
-      f((rr >> 5) * C::WM + b * 32 + (rr & 31), c4 * 4, v);
+      f((rr / C::MFMA) * C::WM + b * C::MFMA + rr % C::MFMA, c4 * 4, v);
     }
   }
   wg_barrier();  // LDS is free again for the next tile's stages
@@ -1042,6 +1037,7 @@ __device__ __forceinline__ void staged_epilogue_pf(const AccTile<BM, BN> &acc, c
   using E = EpiCfg<BM, BN>;
   constexpr int NK = E::CHUNKS / C::THREADS;
   static_assert(NK % 2 == 0, "column groups are taken in pairs");
+  static_assert(C::THREADS % (BN / 4) == 0, "a thread keeps one column group");
   char *wp = epi_lane_pos<BM, BN>(smem);
   // THREADS is a multiple of BN / 4: a thread keeps its column group
   const int c4 = (int)threadIdx.x % (BN / 4);
@@ -1052,7 +1048,7 @@ __device__ __forceinline__ void staged_epilogue_pf(const AccTile<BM, BN> &acc, c
     wg_barrier();
     epi_write_block<BM, BN>(acc, b, wp);
     wg_barrier();
-    auto row_of = [&](int rr) { return (rr >> 5) * C::WM + b * 32 + (rr & 31); };
+    auto row_of = [&](int rr) { return (rr / C::MFMA) * C::WM + b * C::MFMA + rr % C::MFMA; };
     auto lds_val = [&](int rr) { return *reinterpret_cast<const f32x4_t *>(smem + rr * E::PITCH + c4 * 16); };
     // two register sets in turn, never copied (a copy of registers a load
     // is still filling waits for that load); the prefetch past the block's
@@ -1077,33 +1073,6 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
   v[2] = (__bf16)c;
   v[3] = (__bf16)d;
   return *reinterpret_cast<uint2 *>(&v);
-}
-
-// Store a tile's accumulators as bf16 (RNE) straight from their register
-// layout: 8-byte stores of 4 consecutive columns into the matrix at base
-// (row pitch ld elements), the tile's element (r, c) going to row row0 + r,
-// column col0 + c, for rows below row1 and columns below col1 only.  No LDS
-// and no barrier, so the waves of a workgroup leave the tile as they finish
-// it.  Addresses are formed from the tile's origin, so no part of them is
-// invariant across tiles (hoisted out of the tile loop, such values would
-// hold registers through the K loop).
-template <int BM, int BN>
-__device__ __forceinline__ void store_tile_bf16(const AccTile<BM, BN> &acc, uint16_t *base, int ld,
-                                                int row0, int col0, int row1, int col1) {
-  using C = TileCfg<BM, BN>;
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int g = 0; g < C::GROUPS; ++g) {
-        const AccPos<BM, BN> ps = acc_pos<BM, BN>(i, j, g);
-        const int row = row0 + ps.row, col = col0 + ps.col;
-        if (row < row1 && col < col1) {
-          const f32x4_t v = acc_group(acc[i][j], g);
-          *reinterpret_cast<uint2 *>(base + (size_t)row * ld + col) = pack_bf16x4(v[0], v[1], v[2], v[3]);
-        }
-      }
 }
 
 }  // namespace mk

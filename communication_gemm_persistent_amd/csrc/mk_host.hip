@@ -38,7 +38,7 @@ struct mk_ctx {
   bool no_slabs = true;   // MK_NO_SLABS=0 env: cut AllGather land blocks into K-slabs
   int ring_splits = 0;  // MK_RING_SPLITS=1: one task per (head, query tile) (0: library choice)
   int tile_map = -1;  // MK_TILE_MAP env: 0 global m-major order, 1 XCD blocks, 2 XCD strided, 3 XCD rounds (-1: per op)
-  int item_kib = 256;  // MK_ITEM_KIB env: target size of one AllGather land item
+  int item_kib = 512;  // MK_ITEM_KIB env: target size of one AllGather land item
   int help_every = 0;  // MK_HELP_EVERY env: 1 in this many compute workgroups helps land (0: automatic)
   int help_eager = -1;  // MK_HELP_EAGER env: helpers land until the queue is empty (-1: automatic)
   int land_split = 1;  // MK_LAND_SPLIT env: land first-round chunks at the start, the rest between tiles

@@ -170,7 +170,11 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * ldb));
     AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc, gate);
-    store_tile_bf16<BM, BN>(acc, p.c, p.n, m0, n0, m1, p.n);
+    staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
+      const int row = m0 + r, col = n0 + cc;
+      if (row < m1 && col < p.n)
+        *reinterpret_cast<uint2 *>(p.c + (size_t)row * p.n + col) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+    });
     // this workgroup's share of the items later tiles need
     if constexpr (!PRE) {
       for (int i = 0; i < p.land_between; ++i) {
