@@ -30,40 +30,16 @@ namespace mk {
 struct MoeShared {
   uint32_t word;
   int32_t wave_cnt[kMaxWaves][kMaxLocalExperts];
-  int32_t scan_tmp[kMaxWaves];
   int32_t list_tok[kRouteTokens * 8];   // (slot << 8 | token-in-item) of the item's local rows
   int32_t n_list;
   int32_t tile_base[kMaxLocalExperts + 2];
   int32_t expert_off[kMaxLocalExperts + 1];
+  int32_t expert_tot[kMaxLocalExperts];
 };
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
-}
-
-// Block-wide exclusive scan of one int per thread; returns the prefix and
-// writes the block total to *total.  Uses tmp[blockDim.x / 64].
-__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *tmp, int32_t *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) tmp[wave] = x;
-  __syncthreads();
-  int32_t before = 0, all = 0;
-  const int nw = blockDim.x >> 6;
-  for (int w = 0; w < nw; ++w) {
-    const int32_t t = tmp[w];
-    if (w < wave) before += t;
-    all += t;
-  }
-  __syncthreads();
-  *total = all;
-  return before + x - v;
 }
 
 // ---------------------------------------------------------------- route
@@ -82,24 +58,61 @@ __device__ __forceinline__ void moe_route_item(const MoeParams &p, int item, Moe
   float selv[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) { sel[j] = -1; selv[j] = 0.f; }
-  if (valid) {
-    const float *lg = p.logits[s] + (size_t)t * p.E;
-    for (int e = 0; e < p.E; ++e) {
-      const float v = lg[e];
+  auto insert = [&](int e, float v) {
 #pragma unroll
-      for (int j = 7; j >= 0; --j) {
-        if (j >= p.top_k) continue;
-        const bool here = sel[j] < 0 || v > selv[j];
-        const bool above = j > 0 && (sel[j - 1] < 0 || v > selv[j - 1]);
-        if (here) {
-          if (above) { sel[j] = sel[j - 1]; selv[j] = selv[j - 1]; }
-          else { sel[j] = e; selv[j] = v; }
-        }
+    for (int j = 7; j >= 0; --j) {
+      if (j >= p.top_k) continue;
+      const bool here = sel[j] < 0 || v > selv[j];
+      const bool above = j > 0 && (sel[j - 1] < 0 || v > selv[j - 1]);
+      if (here) {
+        if (above) { sel[j] = sel[j - 1]; selv[j] = selv[j - 1]; }
+        else { sel[j] = e; selv[j] = v; }
       }
     }
-    const float mx = selv[0];
+  };
+  if (valid) {
+    const float *lg = p.logits[s] + (size_t)t * p.E;
     float sum = 0.f;
-    for (int e = 0; e < p.E; ++e) sum += expf(lg[e] - mx);
+    if (p.E == 64) {
+      // the token's 64 logits in 16 vector loads issued together, then the
+      // top-k and the softmax sum from registers (one load per logit in a
+      // loop leaves every iteration waiting for its load)
+      f32x4_t l[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) l[q] = reinterpret_cast<const f32x4_t *>(lg)[q];
+      if (p.top_k == 2) {
+        // the same selection as insert() for two slots, without the general
+        // slot loop
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float v = l[q][u];
+            const int e = q * 4 + u;
+            if (sel[0] < 0 || v > selv[0]) {
+              sel[1] = sel[0]; selv[1] = selv[0];
+              sel[0] = e; selv[0] = v;
+            } else if (sel[1] < 0 || v > selv[1]) {
+              sel[1] = e; selv[1] = v;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) insert(q * 4 + u, l[q][u]);
+      }
+      const float mx = selv[0];
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sum += expf(l[q][u] - mx);
+    } else {
+      for (int e = 0; e < p.E; ++e) insert(e, lg[e]);
+      const float mx = selv[0];
+      for (int e = 0; e < p.E; ++e) sum += expf(lg[e] - mx);
+    }
+    const float mx = selv[0];
     const size_t o = ((size_t)s * p.T + t) * p.top_k;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -148,38 +161,69 @@ __device__ __forceinline__ void moe_route_item(const MoeParams &p, int item, Moe
 
 // ---------------------------------------------------------------- scan
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t y = __shfl_up(v, d, 64);
+    if (lane >= d) v += y;
+  }
+  return v;
+}
+
+// Slot offsets in (expert, source, token) order.  Each wave takes whole
+// experts, so the experts are scanned in parallel: (1) every expert's total,
+// (2) expert offsets, (3) each item's base = its expert's offset plus the
+// counts of the expert's earlier items.
 template <int BM>
 __device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
-  int32_t running = 0;
-  for (int e = 0; e < p.E_loc; ++e) {
-    if (threadIdx.x == 0) p.expert_offsets[e] = running;
-    for (int base = 0; base < p.n_items; base += (int)blockDim.x) {
-      const int i = base + (int)threadIdx.x;
-      const int32_t v = i < p.n_items ? p.item_cnt[(size_t)i * p.E_loc + e] : 0;
-      int32_t total;
-      const int32_t ex = block_exclusive_scan(v, sh.scan_tmp, &total);
-      if (i < p.n_items) {
-        p.item_base[(size_t)i * p.E_loc + e] = running + ex;
-        if (i % p.items_per_src == 0) p.chunk_offsets[e * (p.S + 1) + i / p.items_per_src] = running + ex;
-      }
-      running += total;
-    }
-    if (threadIdx.x == 0) p.chunk_offsets[e * (p.S + 1) + p.S] = running;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int e = wave; e < p.E_loc; e += nw) {
+    int32_t tot = 0;
+    for (int i = lane; i < p.n_items; i += 64) tot += p.item_cnt[(size_t)i * p.E_loc + e];
+    tot = wave_inclusive_scan(tot);
+    if (lane == 63) sh.expert_tot[e] = tot;
   }
+  __syncthreads();
   if (threadIdx.x == 0) {
+    int32_t running = 0;
+    for (int e = 0; e < p.E_loc; ++e) {
+      sh.expert_off[e] = running;
+      p.expert_offsets[e] = running;
+      running += sh.expert_tot[e];
+    }
+    sh.expert_off[p.E_loc] = running;
     p.expert_offsets[p.E_loc] = running;
     p.tile_base[1] = running;
   }
   __syncthreads();
+  for (int e = wave; e < p.E_loc; e += nw) {
+    int32_t carry = sh.expert_off[e];
+    for (int i0 = 0; i0 < p.n_items; i0 += 64) {
+      const int i = i0 + lane;
+      const int32_t v = i < p.n_items ? p.item_cnt[(size_t)i * p.E_loc + e] : 0;
+      const int32_t incl = wave_inclusive_scan(v);
+      const int32_t base = carry + incl - v;
+      if (i < p.n_items) {
+        p.item_base[(size_t)i * p.E_loc + e] = base;
+        if (i % p.items_per_src == 0) p.chunk_offsets[e * (p.S + 1) + i / p.items_per_src] = base;
+      }
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) p.chunk_offsets[e * (p.S + 1) + p.S] = carry;
+  }
+  __syncthreads();
   // grouped-GEMM row tiles in m-tile-major order across experts (tokens of
-  // the first sources land first and fill every expert's first rows)
+  // the first sources land first and fill every expert's first rows); the
+  // offsets are read from LDS (one thread, many dependent reads)
   if (threadIdx.x == 0) {
     int ntile_rows = 0, max_mt = 0;
     for (int e = 0; e < p.E_loc; ++e)
-      max_mt = max(max_mt, (p.expert_offsets[e + 1] - p.expert_offsets[e] + BM - 1) / BM);
+      max_mt = max(max_mt, (sh.expert_off[e + 1] - sh.expert_off[e] + BM - 1) / BM);
     for (int mt = 0; mt < max_mt; ++mt)
       for (int e = 0; e < p.E_loc; ++e)
-        if (mt * BM < p.expert_offsets[e + 1] - p.expert_offsets[e])
+        if (mt * BM < sh.expert_off[e + 1] - sh.expert_off[e])
           p.tile_base[2 + ntile_rows++] = (e << 16) | mt;
     p.tile_base[0] = ntile_rows;
   }
@@ -216,37 +260,84 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, MoeS
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t row_vec = (size_t)p.H / 8;   // 16-byte vectors per token row
   const int nw = blockDim.x >> 6;
-  for (int r = wave; r < n; r += nw) {
+  auto row = [&](int r, const u32x4_t *&src, u32x4_t *&dst) {
     const int v = sh.list_tok[r];
     const int slot = v >> 8, tt = b * kRouteTokens + (v & 255);
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(p.x[s] + (size_t)tt * p.H);
-    u32x4_t *dst = reinterpret_cast<u32x4_t *>(p.x_slots + (size_t)slot * p.H);
+    src = reinterpret_cast<const u32x4_t *>(p.x[s] + (size_t)tt * p.H);
+    dst = reinterpret_cast<u32x4_t *>(p.x_slots + (size_t)slot * p.H);
+  };
+  // two rows per wave at a time, 8 loads per lane and row in flight before
+  // the stores (two whole 8 KiB rows per wave for H = 4096)
+  for (int r = wave; r < n; r += 2 * nw) {
+    const bool two = r + nw < n;
+    const u32x4_t *src0, *src1;
+    u32x4_t *dst0, *dst1;
+    row(r, src0, dst0);
+    if (two) row(r + nw, src1, dst1);
+    else { src1 = src0; dst1 = dst0; }
     size_t i = lane;
-    for (; i + 3 * 64 < row_vec; i += 4 * 64) {
-      const u32x4_t a0 = src[i], a1 = src[i + 64], a2 = src[i + 128], a3 = src[i + 192];
-      dst[i] = a0; dst[i + 64] = a1; dst[i + 128] = a2; dst[i + 192] = a3;
+    for (; i + 7 * 64 < row_vec; i += 8 * 64) {
+      u32x4_t a0[8], a1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a0[u] = src0[i + u * 64];
+      if (two) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a1[u] = src1[i + u * 64];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dst0[i + u * 64] = a0[u];
+      if (two) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dst1[i + u * 64] = a1[u];
+      }
     }
-    for (; i < row_vec; i += 64) dst[i] = src[i];
+    for (; i < row_vec; i += 64) {
+      dst0[i] = src0[i];
+      if (two) dst1[i] = src1[i];
+    }
   }
 }
 
 // ---------------------------------------------------------------- compute
 
-// Thread 0: wait for every route item whose tokens of local expert e fall in
-// slots [slot0, slot1).  item_base[i][e] is non-decreasing in i.
-__device__ __forceinline__ bool moe_wait_rows(const MoeParams &p, int e, int slot0, int slot1) {
-  // first item whose range for e ends after slot0
+// First route item whose range of slots of local expert e ends after slot0
+// (item_base[i][e] is non-decreasing in i).
+__device__ __forceinline__ int moe_first_item(const MoeParams &p, int e, int slot0) {
   int lo = 0, hi = p.n_items;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     const int end = p.item_base[(size_t)mid * p.E_loc + e] + p.item_cnt[(size_t)mid * p.E_loc + e];
     if (end > slot0) hi = mid; else lo = mid + 1;
   }
-  for (int i = lo; i < p.n_items; ++i) {
+  return lo;
+}
+
+// Thread 0: wait for every route item whose tokens of local expert e fall in
+// slots [slot0, slot1).
+__device__ __forceinline__ bool moe_wait_rows(const MoeParams &p, int e, int slot0, int slot1) {
+  for (int i = moe_first_item(p, e, slot0); i < p.n_items; ++i) {
     if (p.item_base[(size_t)i * p.E_loc + e] >= slot1) break;
     if (!spin_until_eq(p.sync, flag_ptr(p.sync, (uint32_t)i), p.sync.epoch, (uint32_t)i)) return false;
   }
   return true;
+}
+
+// Thread 0: have those route items landed?  (moe_wait_rows without waiting)
+__device__ __forceinline__ bool moe_rows_ready(const MoeParams &p, int e, int slot0, int slot1) {
+  for (int i = moe_first_item(p, e, slot0); i < p.n_items; ++i) {
+    if (p.item_base[(size_t)i * p.E_loc + e] >= slot1) break;
+    if (ld_relaxed(flag_ptr(p.sync, (uint32_t)i)) != p.sync.epoch) return false;
+  }
+  return true;
+}
+
+// Land route item it and release its flag (every thread waits for its own
+// stores; after the barrier one release store publishes the item).
+__device__ __forceinline__ void moe_land_and_release(const MoeParams &p, uint32_t it, MoeShared &sh) {
+  moe_land_item(p, (int)it, sh);
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) st_release(flag_ptr(p.sync, it), p.sync.epoch);
 }
 
 template <int BM, int BN>
@@ -271,6 +362,18 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
       break;
     }
     const int n0 = nb * BN;
+    // while the tile's rows are missing, land queued route items (landing
+    // then runs on every workgroup, not only on the land role's)
+    for (;;) {
+      // the barrier closes the previous item's single-thread release
+      __syncthreads();
+      bool ready = false;
+      if (threadIdx.x == 0) ready = moe_rows_ready(p, e, slot0, slot1);
+      if (wg_broadcast(ready, &sh.word)) break;
+      const uint32_t it = next_index(&p.sync.ctrl->land_ctr, &sh.word);
+      if (it >= (uint32_t)p.n_items) break;
+      moe_land_and_release(p, it, sh);
+    }
     bool ok0 = true;
     if (threadIdx.x == 0) ok0 = moe_wait_rows(p, e, slot0, slot1);
     if (!wg_sync_ok(ok0, &sh.word)) break;
@@ -439,10 +542,7 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeP
       for (;;) {
         const uint32_t it = next_index(&ctrl->land_ctr, &sh.word);
         if (it >= (uint32_t)p.n_items) break;
-        moe_land_item(p, (int)it, sh);
-        wait_stores();
-        __syncthreads();
-        if (threadIdx.x == 0) st_release(flag_ptr(p.sync, it), p.sync.epoch);
+        moe_land_and_release(p, it, sh);
       }
     } else if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
       moe_compute<BM, BN>(p, smem, sh);
