@@ -45,10 +45,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the sources the AllGather+GEMM kernel and its launch are built from
+AG_KERNEL_SOURCES = ("mk_device.h", "mk_host.hip", "mk_kernels.hip", "mk_params.h")
+
+
 def kernel_source_hash() -> str:
+    """Hash of the AllGather+GEMM kernel's sources: the stored counters apply
+    only while it is unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "communication_gemm_persistent_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in AG_KERNEL_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
