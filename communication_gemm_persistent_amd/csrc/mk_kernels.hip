@@ -16,6 +16,13 @@
 
 namespace mk {
 
+// 4 bf16 values (8 bytes) stored with a non-temporal hint: outputs the
+// kernel never reads again.
+__device__ __forceinline__ void store_nt(uint16_t *dst, const uint2 &o) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u32x2_t{o.x, o.y}, reinterpret_cast<u32x2_t *>(dst));
+}
+
 // ---------------------------------------------------------------- AllGather + GEMM
 
 __device__ __forceinline__ uint32_t ag_flag(const AgParams &p, int q, int j, int s) {
@@ -172,8 +179,7 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
     gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc, gate);
     staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
       const int row = m0 + r, col = n0 + cc;
-      if (row < m1 && col < p.n)
-        *reinterpret_cast<uint2 *>(p.c + (size_t)row * p.n + col) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+      if (row < m1 && col < p.n) store_nt(p.c + (size_t)row * p.n + col, pack_bf16x4(v[0], v[1], v[2], v[3]));
     });
     // this workgroup's share of the items later tiles need
     if constexpr (!PRE) {
@@ -273,15 +279,19 @@ struct PeerVals {
 template <>
 struct PeerVals<0> {};
 
+// The partials are read once: non-temporal loads keep them from displacing
+// cached data.
 template <int NP>
 __device__ __forceinline__ PeerVals<NP> load_peer_vals(const float *const *pc, size_t off) {
   PeerVals<NP> r;
   if constexpr (NP > 0) {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) r.v[i] = *reinterpret_cast<const f32x4_t *>(pc[i] + off);
+    for (int i = 0; i < NP; ++i)
+      r.v[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(pc[i] + off));
   }
   return r;
 }
+
 
 template <int NP>
 __device__ __forceinline__ f32x4_t add_peer_vals(const f32x4_t &v, const PeerVals<NP> &pv) {
@@ -337,7 +347,7 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &ta
         load_peers(pr, tab.peer, p.world - 1, off);
         x = sum_peers(v, pr, p.world - 1);
       }
-      *reinterpret_cast<uint2 *>(d + off) = pack_bf16x4(x[0], x[1], x[2], x[3]);
+      store_nt(d + off, pack_bf16x4(x[0], x[1], x[2], x[3]));
     };
     // A tile inside one slice (every tile when the slice height is a
     // multiple of BM) picks its destination once, with a scalar index.  A
@@ -351,7 +361,7 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &ta
       const int r0 = m0 - q0 * p.ms, rows = m1 - m0;
       auto put = [&](int r, int cc, const f32x4_t &x) {
         if (r < rows && cc < cols)
-          *reinterpret_cast<uint2 *>(p.c_own + (size_t)(r0 + r) * p.n + n0 + cc) = pack_bf16x4(x[0], x[1], x[2], x[3]);
+          store_nt(p.c_own + (size_t)(r0 + r) * p.n + n0 + cc, pack_bf16x4(x[0], x[1], x[2], x[3]));
       };
       // addresses clamped into the tile: a group past its edge loads an
       // element of the tile that it does not use, so no load needs a branch
@@ -430,10 +440,10 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, const PtrTable &ta
       if (r >= rows || cc >= cols) return;
       const size_t off = (size_t)(m0 + r) * p.n + n0 + cc;
       const uint2 o = pack_bf16x4(x[0], x[1], x[2], x[3]);
-      *reinterpret_cast<uint2 *>(p.c + off) = o;
+      store_nt(p.c + off, o);
 #pragma unroll
       for (int b = 0; b < MK_MAX_WORLD; ++b)
-        if (b < p.n_bcast) *reinterpret_cast<uint2 *>(bc[b] + off) = o;
+        if (b < p.n_bcast) store_nt(bc[b] + off, o);
     };
     // addresses clamped into the tile (see the ReduceScatter epilogue)
     auto off_in = [&](int r, int cc) { return (size_t)(m0 + min(r, rows - 1)) * p.n + n0 + min(cc, cols - 4); };
