@@ -107,6 +107,40 @@ def test_moe_ties_and_peers_in_host_memory(handle):
     check_moe(d, out, top_k, 0, I.FLOAT)
 
 
+@pytest.mark.parametrize("top_k", [2, 3])
+def test_moe_e64_routing_with_ties(handle, top_k):
+    """E = 64 routes from vector loads of each token's logits (top-2 by a
+    two-slot selection); forced ties keep the lower expert id first."""
+    S, T, H, N, E, E_loc = 2, 300, 64, 64, 64, 8
+    print(f"moe E=64 top_k={top_k} with ties", flush=True)
+    d = I.gen_moe(S, T, H, N, E, E_loc, I.FLOAT, config=440 + top_k)
+    for s in range(S):
+        lg = d["logits"][s]
+        lg[::3, 5] = lg[::3, 6] = lg[::3].max(axis=1) + 1.0   # tie at the top (local experts)
+        lg[1::4, 40] = lg[1::4, 3] = lg[1::4].max(axis=1) + 2.0  # tie across the local boundary
+        lg[2::7, :] = 0.25                                      # all equal
+    out = run_moe(handle, d, E, top_k, rank=0)
+    check_moe(d, out, top_k, 0, I.FLOAT)
+
+
+@pytest.mark.parametrize("roles", [(1, -1), (1, 3), (4, 60)])
+def test_moe_role_splits_bit_identical(handle, mk, roles):
+    """Landing is shared by the land role and by compute workgroups whose rows
+    are missing; every split of the roles gives the same bits."""
+    S, T, H, N, E, E_loc, top_k = 4, 700, 128, 136, 64, 8, 2
+    print(f"moe role split {roles}", flush=True)
+    d = I.gen_moe(S, T, H, N, E, E_loc, I.INTEGER, config=450)
+    ref = run_moe(handle, d, E, top_k, rank=1)
+    check_moe(d, ref, top_k, 1, I.INTEGER)
+    handle.set_roles(mk.OP_MOE, n_land=roles[0], n_compute=roles[1])
+    try:
+        out = run_moe(handle, d, E, top_k, rank=1)
+    finally:
+        handle.set_roles(mk.OP_MOE)
+    for key in ref:
+        assert np.array_equal(out[key], ref[key]), f"{key} differs with roles {roles}"
+
+
 def test_moe_no_local_tokens(handle):
     """Degenerate case: no token picks a local expert -> zero slots, no tiles."""
     S, T, H, N, E, E_loc, top_k = 2, 64, 32, 32, 8, 2, 1
