@@ -420,7 +420,7 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   // balance better in the global order (own slice first)
   p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapStrided;
   // landing geometry: one flag per lb_rows rows of a shard and K-slab,
-  // items of ~256 KiB.  Shards are cut into K-slabs (about 8, of at least
+  // items of about item_kib KiB (512 by default).  Shards are cut into K-slabs (about 8, of at least
   // 256 columns) when every slab of every row starts on a 128-byte line, so
   // that tiles can start once their first slab has landed; otherwise one
   // slab spans K.
