@@ -261,13 +261,14 @@ __device__ __forceinline__ void fill_table(PtrTable *t, const float *const *peer
   __syncthreads();
 }
 
+// A table entry as a uniform (scalar) pointer: every lane reads the same slot.
 template <class T>
 __device__ __forceinline__ T *table_ptr(T *const &slot) {
   return static_cast<T *>(const_cast<void *>(uniform_ptr(slot)));
 }
 
-// The same for a peer count known at compile time, from the compact list
-// (ascending rank).  Every load is unconditional: loads behind uniform
+// load_peers / sum_peers for a peer count known at compile time, from the
+// compact list (ascending rank).  Every load is unconditional: loads behind uniform
 // branches leave the compiler unable to count them, and it then waits for
 // all memory traffic, the previous group's stores included, before using
 // any of them.
@@ -350,10 +351,10 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &ta
       store_nt(d + off, pack_bf16x4(x[0], x[1], x[2], x[3]));
     };
     // A tile inside one slice (every tile when the slice height is a
-    // multiple of BM) picks its destination once, with a scalar index.  A
-    // per-row pick indexes the parameter array with a vector index, which
-    // compiles to a vector load of the pointer whose wait also waits for
-    // every store before it: one memory round trip per row.
+    // multiple of BM) reads its destination once; only a tile that straddles
+    // slices picks one per row (from the LDS table: a per-row pick from the
+    // kernel arguments compiles to a vector load of the pointer, whose wait
+    // also waits for every store before it).
     const int q0 = m0 / p.ms;
     if ((m1 - 1) / p.ms == q0 && q0 == p.rank) {
       // own slice: the peers' partials of the next column group are loaded
