@@ -737,7 +737,9 @@ static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
 
   const int gmax = max_grid(h, MK_OP_MOE, bm);
   const mk_roles &r = h->roles[MK_OP_MOE];
-  int land = r.n_land >= 0 ? r.n_land : std::max(1, std::min(p.n_items, gmax / 8));
+  // compute workgroups land while their rows are missing, so a small land
+  // role suffices (1/16 of the grid measured 1-3% faster than 1/8)
+  int land = r.n_land >= 0 ? r.n_land : std::max(1, std::min(p.n_items, gmax / 16));
   land = std::max(1, std::min(land, 4 * gmax));  // landing cannot be switched off: compute depends on it
   int compute = r.n_compute >= 0 ? std::min(r.n_compute, 4 * gmax)
                                  : (int)std::max(1L, std::min(max_row_tiles * p.tiles_n, (long)gmax - land));
