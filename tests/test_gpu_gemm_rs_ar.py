@@ -211,3 +211,35 @@ def test_rs_ar_tile_orders(mk, tile_map):
                 O.assert_bits_equal(b, c, f"bcast[{i}] vs c")
     finally:
         h.close()
+
+
+@pytest.mark.parametrize("tile", ["256", "128"])
+def test_rs_ar_own_slice_pipelined_epilogue(mk, tile):
+    """Slice heights that are tile multiples put every own-slice tile inside
+    one slice, where the reduce epilogue loads the next row group's peer
+    partials before storing the current one (7, 3 and 1 peers), with ragged
+    N and K; the AllReduce takes the same epilogue for every tile."""
+    old = os.environ.get("MK_TILE")
+    os.environ["MK_TILE"] = tile
+    try:
+        h = mk.Handle(0, spin_timeout_ms=10000)
+    finally:
+        if old is None:
+            del os.environ["MK_TILE"]
+        else:
+            os.environ["MK_TILE"] = old
+    try:
+        for shape in [(8, 3, 2048, 264, 72), (4, 1, 2048, 520, 200), (2, 1, 512, 136, 40)]:
+            W, rank, m, n, k = shape
+            print(f"rs/ar pipelined epilogue tile={tile} {shape}", flush=True)
+            d = I.gen_rs(W, m, n, k, rank=rank, variant=I.INTEGER, config=360 + W)
+            c_own, outbox = run_rs(h, d, rank)
+            check_rs(d, rank, c_own, outbox, exact=True)
+            d = I.gen_ar(W, m, n, k, rank=rank, variant=I.INTEGER, config=370 + W)
+            c, bc = run_ar(h, d, rank, 3)
+            ref = O.gemm_ar(d["a"], d["b"], d["peers"], rank=rank, n_bcast=3)
+            O.assert_bits_equal(c, ref["c"], "c")
+            for i, b in enumerate(bc):
+                O.assert_bits_equal(b, c, f"bcast[{i}] vs c")
+    finally:
+        h.close()
