@@ -340,6 +340,7 @@ def other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev):
     t = float(np.median(time_calls(lambda: h.gemm_rs(a, bt, peers, c_own, outbox, rank=0), 20, 3)))
     byts = (W - 1) * ms * n * 4 + ms * n * 2 + (W - 1) * ms * n * 2
     out[name] = {"ms": round(t, 4), "tflops": round(wl.flops() / (t * 1e-3) / 1e12, 2),
+                 "mfma_frac": round(wl.flops() / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                  "reduce_scatter_GBps": round(byts / (t * 1e-3) / 1e9, 1),
                  "roles": h.last_launch(mk.OP_GEMM_RS)[0]}
     del a, bt, peers, c_own, outbox, d
@@ -392,6 +393,8 @@ def other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev):
     fl = wl.flops(n_slots)
     byts = S * T * E * 4 + 2 * n_slots * H * 2 + n_slots * H * 2 + E_loc * H * N * 2 + n_slots * N * 2
     out[name] = {"ms": round(t, 4), "n_slots": n_slots, "tflops": round(fl / (t * 1e-3) / 1e12, 2),
+                 "mfma_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                 "hbm_frac": round(byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                  "GBps": round(byts / (t * 1e-3) / 1e9, 1), "roles": h.last_launch(mk.OP_MOE)[0]}
 
     # the same layer with the return of every remote token's rows and the combine
@@ -446,6 +449,7 @@ def other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev):
     fl = wl.flops()
     landed = 2 * W * BH * S_kv * D * 2
     out[name] = {"ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 2),
+                 "mfma_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                  "attn_alone_ms": round(t_alone, 4),
                  "attn_alone_tflops": round(fl / (t_alone * 1e-3) / 1e12, 2),
                  "land_alone_ms": round(t_land, 4),
