@@ -83,10 +83,31 @@ mk_status hip_fail(mk_ctx *h, hipError_t e, const char *what) {
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Resolve a pointer the kernel will dereference.  Device memory must belong
-// to the handle's device; pinned host memory is accepted when allow_host
-// and replaced by its device-side address.
-mk_status resolve(mk_ctx *h, const void *p, bool allow_host, const void **out, const char *what) {
+// A buffer of `bytes` bytes at p must end inside the allocation that holds p.
+// The runtime knows the extent of device and pinned host allocations; where
+// it reports none, nothing is checked.  A caching allocator's blocks sit
+// inside larger runtime allocations, so this catches a short buffer only
+// near the end of such an allocation.
+mk_status check_extent(mk_ctx *h, const void *p, size_t bytes, const char *what) {
+  void *base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) != hipSuccess || !base || !size) {
+    (void)hipGetLastError();
+    return MK_OK;
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+  if (q < b || q - b >= size) return MK_OK;  // not the allocation p lies in
+  const size_t left = size - (q - b);
+  if (bytes > left)
+    return fail(h, MK_ERR_INVALID, std::string(what) + " is smaller than its shape: " + std::to_string(bytes) +
+                                       " bytes needed, " + std::to_string(left) + " left in its allocation");
+  return MK_OK;
+}
+
+// Resolve a pointer the kernel will dereference, for a buffer of `bytes`
+// bytes.  Device memory must belong to the handle's device; pinned host
+// memory is accepted when allow_host and replaced by its device-side address.
+mk_status resolve(mk_ctx *h, const void *p, size_t bytes, bool allow_host, const void **out, const char *what) {
   if (p == nullptr) return fail(h, MK_ERR_INVALID, std::string(what) + " is NULL");
   if (reinterpret_cast<uintptr_t>(p) & 15u)
     return fail(h, MK_ERR_INVALID, std::string(what) + " is not 16-byte aligned");
@@ -97,6 +118,7 @@ mk_status resolve(mk_ctx *h, const void *p, bool allow_host, const void **out, c
     (void)hipGetLastError();
     return fail(h, MK_ERR_INVALID, std::string(what) + " is not HIP-allocated memory (pageable host memory?)");
   }
+  if (mk_status st = check_extent(h, p, bytes, what)) return st;
   switch (a.type) {
     case hipMemoryTypeDevice:
       if (a.device != h->device)
@@ -394,14 +416,14 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
     if (pre && q != rank) continue;  // peers are not read when pre-landed
     char what[32];
     std::snprintf(what, sizeof(what), "a_shards[%d]", q);
-    if ((st = resolve(h, a_shards[q], q != rank, &dp, what)) != MK_OK) return st;
+    if ((st = resolve(h, a_shards[q], (size_t)m_s * k * 2, q != rank, &dp, what)) != MK_OK) return st;
     p.shard[q] = static_cast<const uint16_t *>(dp);
   }
-  if ((st = resolve(h, bt, false, &dp, "bt")) != MK_OK) return st;
+  if ((st = resolve(h, bt, (size_t)n * k * 2, false, &dp, "bt")) != MK_OK) return st;
   p.bt = static_cast<const uint16_t *>(dp);
-  if ((st = resolve(h, c, true, &dp, "c")) != MK_OK) return st;
+  if ((st = resolve(h, c, (size_t)world * m_s * n * 2, true, &dp, "c")) != MK_OK) return st;
   p.c = static_cast<uint16_t *>(const_cast<void *>(dp));
-  if ((st = resolve(h, a_gathered, false, &dp, "a_gathered")) != MK_OK) return st;
+  if ((st = resolve(h, a_gathered, (size_t)world * m_s * k * 2, false, &dp, "a_gathered")) != MK_OK) return st;
   p.ag = static_cast<uint16_t *>(const_cast<void *>(dp));
 
   const int M = world * m_s;
@@ -521,20 +543,20 @@ mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const m
   mk::RsParams p;
   std::memset(&p, 0, sizeof(p));
   const void *dp;
-  if ((st = resolve(h, a, false, &dp, "a")) != MK_OK) return st;
+  if ((st = resolve(h, a, (size_t)m * k * 2, false, &dp, "a")) != MK_OK) return st;
   p.a = static_cast<const uint16_t *>(dp);
-  if ((st = resolve(h, bt, false, &dp, "bt")) != MK_OK) return st;
+  if ((st = resolve(h, bt, (size_t)n * k * 2, false, &dp, "bt")) != MK_OK) return st;
   p.bt = static_cast<const uint16_t *>(dp);
-  if ((st = resolve(h, c_own, true, &dp, "c_own")) != MK_OK) return st;
+  if ((st = resolve(h, c_own, (size_t)(m / world) * n * 2, true, &dp, "c_own")) != MK_OK) return st;
   p.c_own = static_cast<uint16_t *>(const_cast<void *>(dp));
   for (int q = 0; q < world; ++q) {
     if (q == rank) continue;
     char what[32];
     std::snprintf(what, sizeof(what), "peer_part[%d]", q);
-    if ((st = resolve(h, peer_part[q], true, &dp, what)) != MK_OK) return st;
+    if ((st = resolve(h, peer_part[q], (size_t)(m / world) * n * 4, true, &dp, what)) != MK_OK) return st;
     p.peer_c[q < rank ? q : q - 1] = static_cast<const float *>(dp);
     std::snprintf(what, sizeof(what), "outbox[%d]", q);
-    if ((st = resolve(h, outbox[q], true, &dp, what)) != MK_OK) return st;
+    if ((st = resolve(h, outbox[q], (size_t)(m / world) * n * 2, true, &dp, what)) != MK_OK) return st;
     p.outbox[q] = static_cast<uint16_t *>(const_cast<void *>(dp));
   }
   const int bm = pick_tile(h, (long)cdiv(m, 256) * cdiv(n, 256));
@@ -579,23 +601,23 @@ mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const m
   mk::ArParams p;
   std::memset(&p, 0, sizeof(p));
   const void *dp;
-  if ((st = resolve(h, a, false, &dp, "a")) != MK_OK) return st;
+  if ((st = resolve(h, a, (size_t)m * k * 2, false, &dp, "a")) != MK_OK) return st;
   p.a = static_cast<const uint16_t *>(dp);
-  if ((st = resolve(h, bt, false, &dp, "bt")) != MK_OK) return st;
+  if ((st = resolve(h, bt, (size_t)n * k * 2, false, &dp, "bt")) != MK_OK) return st;
   p.bt = static_cast<const uint16_t *>(dp);
-  if ((st = resolve(h, c, true, &dp, "c")) != MK_OK) return st;
+  if ((st = resolve(h, c, (size_t)m * n * 2, true, &dp, "c")) != MK_OK) return st;
   p.c = static_cast<uint16_t *>(const_cast<void *>(dp));
   for (int q = 0; q < world; ++q) {
     if (q == rank) continue;
     char what[32];
     std::snprintf(what, sizeof(what), "peer_part[%d]", q);
-    if ((st = resolve(h, peer_part[q], true, &dp, what)) != MK_OK) return st;
+    if ((st = resolve(h, peer_part[q], (size_t)m * n * 4, true, &dp, what)) != MK_OK) return st;
     p.peer_c[q < rank ? q : q - 1] = static_cast<const float *>(dp);
   }
   for (int b = 0; b < n_bcast; ++b) {
     char what[32];
     std::snprintf(what, sizeof(what), "bcast[%d]", b);
-    if ((st = resolve(h, bcast[b], true, &dp, what)) != MK_OK) return st;
+    if ((st = resolve(h, bcast[b], (size_t)m * n * 2, true, &dp, what)) != MK_OK) return st;
     p.bcast[b] = static_cast<uint16_t *>(const_cast<void *>(dp));
   }
   const int bm = pick_tile(h, (long)cdiv(m, 256) * cdiv(n, 256));
@@ -654,41 +676,41 @@ static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
   for (int s = 0; s < n_src; ++s) {
     char what[32];
     std::snprintf(what, sizeof(what), "x_src[%d]", s);
-    if ((st = resolve(h, x_src[s], s != rank, &dp, what)) != MK_OK) return st;
+    if ((st = resolve(h, x_src[s], (size_t)T * H * 2, s != rank, &dp, what)) != MK_OK) return st;
     p.x[s] = static_cast<const uint16_t *>(dp);
     std::snprintf(what, sizeof(what), "logits_src[%d]", s);
-    if ((st = resolve(h, logits_src[s], true, &dp, what)) != MK_OK) return st;
+    if ((st = resolve(h, logits_src[s], (size_t)T * E * 4, true, &dp, what)) != MK_OK) return st;
     p.logits[s] = static_cast<const float *>(dp);
   }
-  if ((st = resolve(h, wt, false, &dp, "wt")) != MK_OK) return st;
+  if ((st = resolve(h, wt, (size_t)E_loc * N * H * 2, false, &dp, "wt")) != MK_OK) return st;
   p.wt = static_cast<const uint16_t *>(dp);
-  if ((st = resolve(h, y, true, &dp, "y")) != MK_OK) return st;
+  if ((st = resolve(h, y, (size_t)cap * N * 2, true, &dp, "y")) != MK_OK) return st;
   p.y = static_cast<uint16_t *>(const_cast<void *>(dp));
-  if ((st = resolve(h, topk_idx, true, &dp, "topk_idx")) != MK_OK) return st;
+  if ((st = resolve(h, topk_idx, (size_t)n_src * T * top_k * 4, true, &dp, "topk_idx")) != MK_OK) return st;
   p.topk_idx = static_cast<int32_t *>(const_cast<void *>(dp));
-  if ((st = resolve(h, topk_gate, true, &dp, "topk_gate")) != MK_OK) return st;
+  if ((st = resolve(h, topk_gate, (size_t)n_src * T * top_k * 4, true, &dp, "topk_gate")) != MK_OK) return st;
   p.topk_gate = static_cast<float *>(const_cast<void *>(dp));
-  if ((st = resolve(h, slot_token, true, &dp, "slot_token")) != MK_OK) return st;
+  if ((st = resolve(h, slot_token, (size_t)cap * 4, true, &dp, "slot_token")) != MK_OK) return st;
   p.slot_token = static_cast<int32_t *>(const_cast<void *>(dp));
-  if ((st = resolve(h, expert_offsets, true, &dp, "expert_offsets")) != MK_OK) return st;
+  if ((st = resolve(h, expert_offsets, (size_t)(E_loc + 1) * 4, true, &dp, "expert_offsets")) != MK_OK) return st;
   p.expert_offsets = static_cast<int32_t *>(const_cast<void *>(dp));
-  if ((st = resolve(h, chunk_offsets, true, &dp, "chunk_offsets")) != MK_OK) return st;
+  if ((st = resolve(h, chunk_offsets, (size_t)E_loc * (n_src + 1) * 4, true, &dp, "chunk_offsets")) != MK_OK) return st;
   p.chunk_offsets = static_cast<int32_t *>(const_cast<void *>(dp));
-  if ((st = resolve(h, x_slots, false, &dp, "x_slots")) != MK_OK) return st;
+  if ((st = resolve(h, x_slots, (size_t)cap * H * 2, false, &dp, "x_slots")) != MK_OK) return st;
   p.x_slots = static_cast<uint16_t *>(const_cast<void *>(dp));
   if (combine) {
     if (flags & MK_F_NO_GATE) return fail(h, MK_ERR_INVALID, "the combine sums gated rows: MK_F_NO_GATE");
     if (rank >= n_src) return fail(h, MK_ERR_INVALID, "the combine sums this rank's own tokens: rank >= n_src");
     if (n_src > 1 && !ret) return fail(h, MK_ERR_INVALID, "ret is NULL");
-    if ((st = resolve(h, y_peer, true, &dp, "y_peer")) != MK_OK) return st;
+    if ((st = resolve(h, y_peer, (size_t)T * top_k * N * 2, true, &dp, "y_peer")) != MK_OK) return st;
     p.y_peer = static_cast<const uint16_t *>(dp);
-    if ((st = resolve(h, out, true, &dp, "out")) != MK_OK) return st;
+    if ((st = resolve(h, out, (size_t)T * N * 2, true, &dp, "out")) != MK_OK) return st;
     p.out = static_cast<uint16_t *>(const_cast<void *>(dp));
     for (int s = 0; s < n_src; ++s) {
       if (s == rank) continue;
       char what[32];
       std::snprintf(what, sizeof(what), "ret[%d]", s);
-      if ((st = resolve(h, ret[s], true, &dp, what)) != MK_OK) return st;
+      if ((st = resolve(h, ret[s], (size_t)T * top_k * N * 2, true, &dp, what)) != MK_OK) return st;
       p.ret[s] = static_cast<uint16_t *>(const_cast<void *>(dp));
     }
     p.combine = 1;
@@ -808,24 +830,24 @@ mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, 
   std::memset(&p, 0, sizeof(p));
   const void *dp;
   mk_status st;
-  if ((st = resolve(h, q, false, &dp, "q")) != MK_OK) return st;
+  if ((st = resolve(h, q, (size_t)BH * S_q * D * 2, false, &dp, "q")) != MK_OK) return st;
   p.q = static_cast<const uint16_t *>(dp);
   for (int r = 0; r < world && !pre; ++r) {
     char what[32];
     std::snprintf(what, sizeof(what), "k_src[%d]", r);
-    if ((st = resolve(h, k_src[r], r != rank, &dp, what)) != MK_OK) return st;
+    if ((st = resolve(h, k_src[r], (size_t)BH * S_kv * D * 2, r != rank, &dp, what)) != MK_OK) return st;
     p.k_src[r] = static_cast<const uint16_t *>(dp);
     std::snprintf(what, sizeof(what), "v_src[%d]", r);
-    if ((st = resolve(h, v_src[r], r != rank, &dp, what)) != MK_OK) return st;
+    if ((st = resolve(h, v_src[r], (size_t)BH * S_kv * D * 2, r != rank, &dp, what)) != MK_OK) return st;
     p.v_src[r] = static_cast<const uint16_t *>(dp);
   }
-  if ((st = resolve(h, o, false, &dp, "o")) != MK_OK) return st;
+  if ((st = resolve(h, o, (size_t)BH * S_q * D * 2, false, &dp, "o")) != MK_OK) return st;
   p.o = static_cast<uint16_t *>(const_cast<void *>(dp));
-  if ((st = resolve(h, lse, false, &dp, "lse")) != MK_OK) return st;
+  if ((st = resolve(h, lse, (size_t)BH * S_q * 4, false, &dp, "lse")) != MK_OK) return st;
   p.lse = static_cast<float *>(const_cast<void *>(dp));
-  if ((st = resolve(h, k_recv, false, &dp, "k_recv")) != MK_OK) return st;
+  if ((st = resolve(h, k_recv, (size_t)world * BH * S_kv * D * 2, false, &dp, "k_recv")) != MK_OK) return st;
   p.k_recv = static_cast<uint16_t *>(const_cast<void *>(dp));
-  if ((st = resolve(h, vt_recv, false, &dp, "vt_recv")) != MK_OK) return st;
+  if ((st = resolve(h, vt_recv, (size_t)world * BH * S_kv * D * 2, false, &dp, "vt_recv")) != MK_OK) return st;
   p.vt_recv = static_cast<uint16_t *>(const_cast<void *>(dp));
 
   p.world = world;
@@ -888,7 +910,7 @@ mk_status mk_mfma_ceiling(mk_handle h, mk_stream stream, int iters, float *sink)
   DeviceGuard g(h->device);
   const void *dp;
   mk_status st;
-  if ((st = resolve(h, sink, false, &dp, "sink")) != MK_OK) return st;
+  if ((st = resolve(h, sink, 256 * sizeof(float), false, &dp, "sink")) != MK_OK) return st;
   // two 256-thread workgroups per CU: 2 waves per SIMD
   hipError_t e = mk::launch_mfma_loop(2 * h->cu_count, iters, static_cast<float *>(const_cast<void *>(dp)),
                                       reinterpret_cast<hipStream_t>(stream));

@@ -43,6 +43,13 @@
  *   - Argument errors return MK_ERR_INVALID / MK_ERR_UNSUPPORTED before
  *     anything is launched.  Launch failures return MK_ERR_HIP.  Device-side
  *     timeouts are reported by mk_sync as MK_ERR_TIMEOUT.
+ *   - Every buffer is checked for being non-NULL, 16-byte aligned, on the
+ *     handle's device (or pinned host memory where allowed), and for ending
+ *     inside the runtime allocation it starts in, given the byte size its
+ *     shape implies (MK_ERR_INVALID otherwise; mk_last_error names it).  A
+ *     caching allocator's blocks are sub-ranges of larger allocations, so a
+ *     buffer that is too short but ends inside such an allocation is not
+ *     detected: sizes remain the caller's responsibility.
  */
 #ifndef MK_H
 #define MK_H

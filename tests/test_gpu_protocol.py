@@ -72,6 +72,37 @@ def test_invalid_arguments_launch_nothing(mk):
         assert b"a_gathered" in lib.mk_last_error(h.h)
 
 
+def test_short_buffers_are_rejected_before_launch(mk):
+    # A raw hipMalloc gives an allocation whose extent is exactly known: a
+    # buffer that starts inside it but ends past it must be refused with
+    # MK_ERR_INVALID, and one that fits exactly must be accepted.
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    hip.hipFree.argtypes = [ctypes.c_void_p]
+    d = I.gen_ag(2, 64, 64, 64, I.INTEGER, config=502)
+    shards, bt, c, _ = _ag_buffers(d)
+    need = 2 * 64 * 64 * 2                      # a_gathered: [W*m_s, k] bf16
+    raw = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(raw), need) == 0
+    try:
+        with mk.Handle(0) as h:
+            lib = h.lib
+            arr = (ctypes.c_void_p * 2)(*[s.data_ptr() for s in shards])
+
+            def call(ag):
+                return lib.mk_ag_gemm(h.h, None, 2, 0, arr, bt.data_ptr(), c.data_ptr(), ag,
+                                      64, 64, 64, 0)
+
+            assert call(raw.value + 4096) == mk.MK_ERR_INVALID
+            assert b"a_gathered is smaller than its shape" in lib.mk_last_error(h.h)
+            assert call(raw.value) == mk.MK_OK
+            h.sync()
+            O.assert_bits_equal(bits(c), O.ag_gemm(d["shards"], d["b"])["c"], "exact-size a_gathered")
+    finally:
+        torch.cuda.synchronize()
+        assert hip.hipFree(raw) == 0
+
+
 def test_dynamic_roles_land_without_land_workgroups(mk):
     """With the default dynamic roles, compute workgroups land missing chunks
     themselves, so even n_land = 0 completes."""
