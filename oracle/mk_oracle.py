@@ -343,6 +343,33 @@ def moe_dispatch_gemm(x: Sequence[np.ndarray], logits: Sequence[np.ndarray], w: 
     return out
 
 
+def moe_y_given_gates(x_slots: np.ndarray, w: np.ndarray, expert_offsets: np.ndarray,
+                      gates_f32: np.ndarray) -> np.ndarray:
+    """Expert outputs recomputed with given fp32 gates, for a bit-exact check
+    of the gated output on integer-valued inputs (reading of the integer
+    variant: the gate a kernel computed is taken as an input).
+
+    y[slot] = bf16(fp32(gate[slot] * acc)), acc = x_slots[slot] @ W_e: the
+    gate multiply is one fp32 multiply (rounded to nearest even in fp32), then
+    the product is rounded to bf16.  With integer-valued bf16 inputs whose
+    products sum below 2**24 in magnitude, acc is an exact integer in fp32 and
+    in float64, so the float64 product of the fp32 gate and acc is exact and
+    its fp32 rounding is the kernel's.  Returns [n_slots, N] bf16 bits.
+    """
+    n_slots = int(expert_offsets[-1])
+    g = np.asarray(gates_f32, dtype=np.float32)[:n_slots].astype(np.float64)
+    y = np.zeros((n_slots, w.shape[2]), dtype=np.uint16)
+    for e in range(w.shape[0]):
+        lo, hi = int(expert_offsets[e]), int(expert_offsets[e + 1])
+        if hi <= lo:
+            continue
+        acc = gemm(np.asarray(x_slots)[lo:hi], w[e])
+        if np.abs(acc).max(initial=0.0) >= 2.0 ** 24 or not np.array_equal(acc, np.round(acc)):
+            raise ValueError("the accumulator is not an exact integer below 2**24")
+        y[lo:hi] = f32_to_bf16((g[lo:hi, None] * acc).astype(np.float32))
+    return y
+
+
 # --------------------------------------------------------------------------
 # MoE combine (completes the MoE layer after dispatch + grouped GEMM)
 # --------------------------------------------------------------------------

@@ -145,7 +145,19 @@ def _ring_variant(kind):
     return ring
 
 
+def _y_given_gates_direct(x_slots, w, expert_offsets, gates_f32):
+    n = int(expert_offsets[-1])
+    y = np.zeros((n, w.shape[2]), dtype=np.uint16)
+    for e in range(w.shape[0]):
+        lo, hi = int(expert_offsets[e]), int(expert_offsets[e + 1])
+        if hi > lo:
+            acc = M.gemm(np.asarray(x_slots)[lo:hi], w[e])
+            y[lo:hi] = M.f64_to_bf16(np.asarray(gates_f32, np.float64)[lo:hi, None] * acc)
+    return y
+
+
 MUTANTS = [
+    ("moe_y_given_gates", _y_given_gates_direct, [P.test_moe_y_given_gates_rounds_in_fp32_first]),
     ("f64_to_bf16", _truncating_bf16, [P.test_bf16_hand_patterns]),
     ("gemm", _gemm_transposed_b, [lambda: P.test_gemm_exact_bruteforce((5, 6, 6))]),
     ("gemm", _gemm_drops_last_k, [lambda: P.test_gemm_exact_bruteforce((3, 5, 7))]),
@@ -178,4 +190,74 @@ def test_planted_mistake_is_caught(monkeypatch, name, mutant, pins):
         monkeypatch.setattr(O, name, mutant)
     for pin in pins:
         with pytest.raises((AssertionError, ValueError)):
+            pin()
+
+
+# ---------------------------------------------------------------- the comparison rules
+
+import oracle.compare as C  # noqa: E402
+from tests import test_compare_pins as CP  # noqa: E402
+
+_orig_report = C.tolerance_report
+
+
+def _report_variant(kind):
+    """tolerance_report with one plausible mistake: 'nan' lets non-finite
+    values through (d > bound is False for NaN), 'noabs' uses ref instead of
+    |ref|, 'sample_rms' ignores the whole tensor's rms, 'strict' uses < for <=,
+    'norel' drops the relative term."""
+    def report(gpu_bits, ref_bits, rms=None, rel=C.REL_TOL, rms_tol=C.RMS_TOL):
+        g = M.bf16_to_f64(np.asarray(gpu_bits, dtype=np.uint16))
+        r = M.bf16_to_f64(np.asarray(ref_bits, dtype=np.uint16))
+        if g.shape != r.shape:
+            return dict(ok=False, worst=np.inf, n_bad=-1, rms=np.nan, n=r.size, why="shape")
+        if rms is None or kind == "sample_rms":
+            rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+        relterm = 0.0 if kind == "norel" else rel * (r if kind == "noabs" else np.abs(r))
+        bound = relterm + rms_tol * rms
+        d = np.abs(g - r)
+        with np.errstate(invalid="ignore"):
+            if kind == "nan":
+                bad = d > bound
+            elif kind == "strict":
+                bad = ~(d < bound)
+            else:
+                bad = ~(d <= bound)
+        return dict(ok=not bad.any(), worst=0.0, n_bad=int(bad.sum()), rms=rms, n=r.size, why="")
+    report.__name__ = f"_report_{kind}"
+    return report
+
+
+def _bits_equal_as_floats(gpu, ref, what=""):
+    g = M.bf16_to_f64(np.asarray(gpu, np.uint16)) if np.asarray(gpu).dtype == np.uint16 else gpu
+    r = M.bf16_to_f64(np.asarray(ref, np.uint16)) if np.asarray(ref).dtype == np.uint16 else ref
+    if np.shape(g) != np.shape(r) or not np.array_equal(g, r):
+        raise AssertionError(what)
+
+
+def _gates_absolute(gpu, ref, what=""):
+    if not (np.abs(np.asarray(gpu) - np.asarray(ref)) <= C.GATE_RTOL).all():
+        raise AssertionError(what)
+
+
+COMPARE_MUTANTS = [
+    ("tolerance_report", _report_variant("nan"), [lambda: CP.test_non_finite_gpu_values_fail(0x7FC0)]),
+    ("tolerance_report", _report_variant("noabs"), [CP.test_relative_term_inside_and_outside]),
+    ("tolerance_report", _report_variant("sample_rms"), [CP.test_part_of_an_output_uses_the_whole_tensors_rms]),
+    ("tolerance_report", _report_variant("strict"), [CP.test_rms_term_inside_boundary_and_outside]),
+    ("tolerance_report", _report_variant("norel"), [CP.test_rms_term_inside_boundary_and_outside]),
+    ("assert_bits_equal", _bits_equal_as_floats, [CP.test_bit_equality]),
+    ("assert_gates_close", _gates_absolute, [CP.test_gate_rule]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pins", COMPARE_MUTANTS,
+                         ids=[f"{m[0]}-{m[1].__name__}" for m in COMPARE_MUTANTS])
+def test_planted_comparator_mistake_is_caught(monkeypatch, name, mutant, pins):
+    monkeypatch.setattr(C, name, mutant)
+    if hasattr(O, name):
+        monkeypatch.setattr(O, name, mutant)
+    for pin in pins:
+        # a pin fails by an assertion, or by a pytest.raises that saw nothing
+        with pytest.raises((AssertionError, ValueError, pytest.fail.Exception)):
             pin()

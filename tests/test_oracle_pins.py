@@ -639,3 +639,88 @@ def test_ring_attention_peaked_scores_select_one_value():
     ks[1][0, 0, 2] = _bf([15.0, 0, 0, 0])
     r = O.ring_attention(q, ks, vs, rank=0, scale=1.0)
     np.testing.assert_allclose(r["o_f64"][0, 0, 0], O.bf16_to_f64(vs[1][0, 0, 2]), atol=1e-20)
+
+
+# ---------------------------------------------------------------- gated output from given fp32 gates
+
+def _round_even(x, frac_bits):
+    """Exact round-to-nearest-even of a Fraction to a binary float with
+    frac_bits fraction bits (normal range only)."""
+    from fractions import Fraction
+    if x == 0:
+        return Fraction(0)
+    sgn = -1 if x < 0 else 1
+    a = abs(x)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    ulp = Fraction(2) ** (e - frac_bits)
+    q = abs(x) / ulp
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sgn * fl * ulp
+
+
+def _two_step(gate32, acc):
+    """fp32(gate * acc), then bf16: the kernel's gate multiply and store."""
+    from fractions import Fraction
+    return float(_round_even(_round_even(Fraction(float(gate32)) * int(acc), 23), 7))
+
+
+def test_moe_y_given_gates_bruteforce():
+    """Integer expert products times fp32 gates: y equals, element by element,
+    exact rational arithmetic rounded to fp32 and then to bf16."""
+    g = np.random.default_rng(11)
+    n_slots, H, N, E_loc = 12, 24, 8, 2
+    x = O.f64_to_bf16(g.integers(-2, 3, (n_slots, H)).astype(np.float64))
+    w = O.f64_to_bf16(g.integers(-2, 3, (E_loc, H, N)).astype(np.float64))
+    eoff = np.array([0, 5, n_slots], dtype=np.int32)
+    gates = g.uniform(0.01, 1.0, n_slots).astype(np.float32)
+    y = O.moe_y_given_gates(x, w, eoff, gates)
+    xf = O.bf16_to_f64(x)
+    wf = O.bf16_to_f64(w)
+    for slot in range(n_slots):
+        e = 0 if slot < 5 else 1
+        for j in range(N):
+            acc = int(sum(int(xf[slot, h]) * int(wf[e, h, j]) for h in range(H)))
+            want = _two_step(gates[slot], acc)
+            assert O.bf16_to_f64(y[slot:slot + 1, j])[0] == want, (slot, j, acc)
+
+
+def test_moe_y_given_gates_rounds_in_fp32_first():
+    """Where rounding the exact product straight to bf16 differs from rounding
+    it to fp32 first (a double rounding), the fp32-first result is taken.
+    Cases: gate = fp32(m / acc) for a bf16 midpoint m, so that gate * acc lies
+    within half an fp32 ulp of m, above it; fp32 rounding lands on m, which
+    then ties to even, while a direct rounding goes up."""
+    found = 0
+    for m in (1.0 + 2.0 ** -8, 3.0 + 2.0 ** -7, 0.75 + 2.0 ** -9):
+        for acc in range(3, 256, 2):
+            gate = np.float32(m / acc)
+            prod = float(gate) * acc
+            if not prod > m:
+                continue
+            direct = O.bf16_to_f64(O.f64_to_bf16(np.array([prod])))[0]
+            two = _two_step(gate, acc)
+            assert two != direct
+            x = O.f64_to_bf16(np.array([[float(acc)]]))      # a 1 x 1 x 1 product: acc itself
+            w = O.f64_to_bf16(np.ones((1, 1, 1)))
+            y = O.moe_y_given_gates(x, w, np.array([0, 1], np.int32), np.array([gate]))
+            assert O.bf16_to_f64(y)[0, 0] == two
+            found += 1
+            break
+    assert found == 3, "no double-rounding case found"
+
+
+def test_moe_y_given_gates_unit_gates_give_the_product():
+    g = np.random.default_rng(13)
+    x = O.f64_to_bf16(g.integers(-2, 3, (9, 16)).astype(np.float64))
+    w = O.f64_to_bf16(g.integers(-2, 3, (1, 16, 8)).astype(np.float64))
+    y = O.moe_y_given_gates(x, w, np.array([0, 9], np.int32), np.ones(9, np.float32))
+    O.assert_bits_equal(y, O.f64_to_bf16(O.gemm(x, w[0])), "unit gates")
