@@ -1,6 +1,6 @@
 """Benchmark of the fused AllGather+GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
 
 One step = one persistent fused AllGather+GEMM launch of one rank's share of
 a tensor-parallel MLP up-projection with 8 emulated ranks: local shard
@@ -8,18 +8,26 @@ a tensor-parallel MLP up-projection with 8 emulated ranks: local shard
 B [8192, 3584] bf16, C [8192, 3584] bf16 (481.04 GFLOP).  W untimed warm-up
 steps, then K timed steps between device synchronisations; every step is
 also bracketed by HIP events on the stream the kernel runs on, which gives
-the kernel's average duration for the roofline.
+the kernel's duration per step (mean for the roofline; median, p10, p90).
 
 Also measured and reported in the same JSON line (context, not the value):
   * overlap efficiency = max(GEMM alone, transfer alone) / fused, where GEMM
     alone is the same launch with A already gathered and transfer alone the
-    same launch with no compute workgroups;
-  * the same with the peers in pinned host memory (landing over PCIe);
-  * the fused call with the 256 MB Infinity Cache flushed before each step;
-  * GEMM+ReduceScatter, GEMM+AllReduce and MoE dispatch + grouped GEMM at
-    their workload sizes (--quick skips these);
+    same launch with no compute workgroups; the unfused baselines (the
+    library's landing launch then its GEMM launch, and torch.cat + hipBLASLt
+    matmul) on the same stream;
+  * the same three with the 256 MB Infinity Cache flushed before each call;
+  * the peers in pinned host memory (landing over PCIe): fused, transfer
+    alone, landing GB/s, overlap efficiency;
+  * the small AllGather+GEMM workload's latency (4 ranks, 512x256x256);
+  * engine and memory clocks read before and after the timed steps;
+  * GEMM+ReduceScatter and GEMM+AllReduce (fused, compute alone, transfer
+    alone, with reduce workgroups, overlap efficiency), MoE dispatch +
+    grouped GEMM (with and without the combine) and ring attention at their
+    workload sizes (--quick skips these);
   * measured ceilings: an MFMA-only loop (TFLOP/s) and a plain device copy;
-  * the CPU oracle timed on a bounded sample of the same workload.
+  * the CPU oracle timed on the same workload (median of 3 runs, the CPU
+    model and the BLAS thread count).
 Exactly one JSON line goes to stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -81,10 +89,6 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--extra", action="store_true",
-                    help="also time the fused call with peers in pinned host memory and with "
-                         "the Infinity Cache flushed (these reuse the fused kernel, so a "
-                         "profile of such a run mixes their durations into its average)")
     ap.add_argument("--profile-run", choices=["fused", "gemm_alone", "transfer_alone", "copy"],
                     help="only launch the named kernel a few times (for rocprofv3 counter runs)")
     args = ap.parse_args()
@@ -156,6 +160,7 @@ def main() -> int:
     for _ in range(args.warmup):
         fused()
     torch.cuda.synchronize()
+    clocks_before = read_clocks()
     log(f"[bench] timing {args.steps} fused steps")
     events = []
     torch.cuda.synchronize()
@@ -178,45 +183,85 @@ def main() -> int:
 
     # overlap efficiency: GEMM alone (pre-landed) and transfer alone (no compute)
     reps = max(10, args.steps // 2)
-    log("[bench] GEMM alone / transfer alone")
-    t_gemm = float(np.median(time_calls(lambda: h.ag_gemm(shards, bt, c, ag, rank=0,
-                                                          flags=mk.F_PRELANDED), reps, 3)))
+    log("[bench] GEMM alone / transfer alone / unfused")
+    gemm_alone = lambda: h.ag_gemm(shards, bt, c, ag, rank=0, flags=mk.F_PRELANDED)
+    t_gemm_l = time_calls(gemm_alone, reps, 3)
     # the same landing with no compute: the fused launch's land workgroups, or
     # its whole grid when every workgroup lands between tiles (land = 0)
     n_land_alone = roles_fused[0] if roles_fused[0] > 0 else grid_fused
-    h.set_roles(mk.OP_AG_GEMM, n_land=n_land_alone, n_compute=0)
-    t_xfer = float(np.median(time_calls(fused, reps, 3)))
-    h.set_roles(mk.OP_AG_GEMM)
-    t_fused_med = float(np.median(kern_ms))
-    landed_bytes = (W - 1) * m_s * k * 2
-    extra = {}
-    if args.extra:
-        t_fused_flushed = float(np.median(time_calls(fused, reps, 2, flushed=True)))
-        t_gemm_flushed = float(np.median(time_calls(
-            lambda: h.ag_gemm(shards, bt, c, ag, rank=0, flags=mk.F_PRELANDED), reps, 2,
-            flushed=True)))
-        extra["mall_flushed"] = {"t_fused_ms": round(t_fused_flushed, 4),
-                                 "t_gemm_alone_ms": round(t_gemm_flushed, 4),
-                                 "fused_tflops": round(flops / (t_fused_flushed * 1e-3) / 1e12, 2)}
-        # peers in pinned host memory: landing reads cross PCIe
-        log("[bench] PCIe (pinned host) peers")
-        shards_host = [shards[0]] + [to_dev(s, "host") for s in d["shards"][1:]]
 
-        def fused_host():
-            h.ag_gemm(shards_host, bt, c, ag, rank=0)
-
-        t_fused_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
+    def transfer_alone():
         h.set_roles(mk.OP_AG_GEMM, n_land=n_land_alone, n_compute=0)
-        t_xfer_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
-        h.set_roles(mk.OP_AG_GEMM)
-        del shards_host
-        extra["pcie_host_peers"] = {
-            "t_fused_ms": round(t_fused_host, 4), "t_transfer_alone_ms": round(t_xfer_host, 4),
+        try:
+            fused()
+        finally:
+            h.set_roles(mk.OP_AG_GEMM)
+
+    t_xfer_l = time_calls(transfer_alone, reps, 3)
+    # unfused: the landing launch, then the GEMM launch, on the same stream;
+    # and torch's own: concatenate the shards, then hipBLASLt's matmul
+    t_unfused_l = time_calls(lambda: (transfer_alone(), gemm_alone()), reps, 3)
+    b_kn = bt.t()  # [k, n] view of B for torch.matmul (a column-major operand)
+    a_full = torch.empty((W * m_s, k), dtype=torch.bfloat16, device=dev)
+    c_torch = torch.empty((W * m_s, n), dtype=torch.bfloat16, device=dev)
+
+    def torch_unfused():
+        torch.cat(shards, dim=0, out=a_full)
+        torch.matmul(a_full, b_kn, out=c_torch)
+
+    t_torch_l = time_calls(torch_unfused, reps, 3)
+    t_torch_gemm_l = time_calls(lambda: torch.matmul(a_full, b_kn, out=c_torch), reps, 3)
+    t_fused_med = float(np.median(kern_ms))
+    t_gemm, t_xfer = float(np.median(t_gemm_l)), float(np.median(t_xfer_l))
+    landed_bytes = (W - 1) * m_s * k * 2
+
+    log("[bench] Infinity-Cache-flushed calls")
+    t_fused_fl = float(np.median(time_calls(fused, reps, 2, flushed=True)))
+    t_gemm_fl = float(np.median(time_calls(gemm_alone, reps, 2, flushed=True)))
+    t_xfer_fl = float(np.median(time_calls(transfer_alone, reps, 2, flushed=True)))
+    mall_flushed = {"t_fused_ms": round(t_fused_fl, 4), "t_gemm_alone_ms": round(t_gemm_fl, 4),
+                    "t_transfer_alone_ms": round(t_xfer_fl, 4),
+                    "fused_tflops": round(flops / (t_fused_fl * 1e-3) / 1e12, 2),
+                    "efficiency": round(max(t_gemm_fl, t_xfer_fl) / t_fused_fl, 4)}
+
+    # peers in pinned host memory: landing reads cross PCIe
+    log("[bench] PCIe (pinned host) peers")
+    shards_host = [shards[0]] + [to_dev(s, "host") for s in d["shards"][1:]]
+
+    def fused_host():
+        h.ag_gemm(shards_host, bt, c, ag, rank=0)
+
+    t_fused_host = float(np.median(time_calls(fused_host, max(5, reps // 2), 2)))
+    (nl_h, _, _), grid_h = h.last_launch(mk.OP_AG_GEMM)
+
+    def xfer_host():
+        h.set_roles(mk.OP_AG_GEMM, n_land=nl_h if nl_h > 0 else grid_h, n_compute=0)
+        try:
+            fused_host()
+        finally:
+            h.set_roles(mk.OP_AG_GEMM)
+
+    t_xfer_host = float(np.median(time_calls(xfer_host, max(5, reps // 2), 2)))
+    del shards_host
+    pcie = {"t_fused_ms": round(t_fused_host, 4), "t_transfer_alone_ms": round(t_xfer_host, 4),
             "pcie_read_GBps": round(landed_bytes / (t_xfer_host * 1e-3) / 1e9, 2),
+            "fused_pcie_read_GBps": round(landed_bytes / (t_fused_host * 1e-3) / 1e9, 2),
+            "fused_tflops": round(flops / (t_fused_host * 1e-3) / 1e12, 2),
             "efficiency": round(max(t_gemm, t_xfer_host) / t_fused_host, 4)}
 
+    # the small workload: latency of one call
+    log("[bench] ag_gemm_w4_512x256x256 latency")
+    d1 = I.gen_workload("ag_gemm_w4_512x256x256")
+    sh1 = [to_dev(s) for s in d1["shards"]]
+    bt1 = to_dev(I.transpose_bits(d1["b"]))
+    c1 = torch.empty((4 * 128, 256), dtype=torch.bfloat16, device=dev)
+    ag1 = torch.empty((4 * 128, 256), dtype=torch.bfloat16, device=dev)
+    t_c1 = time_calls(lambda: h.ag_gemm(sh1, bt1, c1, ag1, rank=0), 50, 5)
+    c1_latency = {"workload": "ag_gemm_w4_512x256x256", **pctl(t_c1, scale=1e3, unit="us")}
+    del sh1, bt1, c1, ag1, d1
+
     # measured ceilings beside the nominal ones: an MFMA-only loop and a plain
-    # device copy (the PCIe rate of in-kernel host reads is in --extra)
+    # device copy
     log("[bench] measured ceilings")
     sink = torch.zeros(256, dtype=torch.float32, device=dev)
     mfma_flop = [0.0]
@@ -252,6 +297,8 @@ def main() -> int:
                    "m": W * m_s, "n": n, "k": k, "peers": "separate HBM region",
                    "roles": {"land": roles_fused[0], "compute": roles_fused[1]},
                    "grid": grid_fused},
+        "timing": {"fused_kernel_ms": pctl(kern_ms), "clocks_before": clocks_before,
+                   "clocks_after": read_clocks()},
         "ceilings": dict(ceilings, fused_frac_of_mfma_loop=round(achieved / ceilings["mfma_loop_tflops"], 4)),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -262,12 +309,21 @@ def main() -> int:
             "t_transfer_alone_ms": round(t_xfer, 4), "transfer_alone_land_wgs": n_land_alone,
             "efficiency": round(max(t_gemm, t_xfer) / t_fused_med, 4),
             "gemm_alone_over_fused": round(t_gemm / t_fused_med, 4),
+            "transfer_hidden_frac": round((t_gemm + t_xfer - t_fused_med) / t_xfer, 4),
             "gemm_alone_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 2),
             "landing_GBps": round(2 * landed_bytes / (t_xfer * 1e-3) / 1e9, 1),
-            **extra,
+            "gemm_alone_ms_pctl": pctl(t_gemm_l), "transfer_alone_ms_pctl": pctl(t_xfer_l),
         },
+        "unfused": {"library_land_then_gemm_ms": round(float(np.median(t_unfused_l)), 4),
+                    "torch_cat_then_matmul_ms": round(float(np.median(t_torch_l)), 4),
+                    "torch_matmul_alone_ms": round(float(np.median(t_torch_gemm_l)), 4),
+                    "fused_speedup_vs_library_unfused": round(float(np.median(t_unfused_l)) / t_fused_med, 4),
+                    "fused_speedup_vs_torch_unfused": round(float(np.median(t_torch_l)) / t_fused_med, 4)},
+        "mall_flushed": mall_flushed,
+        "pcie_host_peers": pcie,
+        "c1_latency": c1_latency,
     }
-    del shards, bt, c, ag, d
+    del shards, bt, c, ag, d, a_full, c_torch
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ other fused ops
@@ -280,6 +336,54 @@ def main() -> int:
     h.close()
     print(json.dumps(result), flush=True)
     return 0
+
+
+def pctl(xs, scale=1.0, unit="ms"):
+    """Median, p10 and p90 of per-call times (ms, times scale)."""
+    a = np.asarray(xs, dtype=np.float64) * scale
+    return {"unit": unit, "median": round(float(np.median(a)), 4),
+            "p10": round(float(np.percentile(a, 10)), 4), "p90": round(float(np.percentile(a, 90)), 4),
+            "n": int(a.size)}
+
+
+def read_clocks():
+    """Current engine / memory clocks as amd-smi (or rocm-smi) reports them,
+    best effort: a dict, or the reason none could be read."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.TimeoutExpired) as e:
+            last = f"{cmd[0]}: {e}"
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            try:
+                return {"tool": cmd[0], "data": _trim_clocks(json.loads(r.stdout))}
+            except ValueError:
+                return {"tool": cmd[0], "text": r.stdout.strip()[:400]}
+        last = f"{cmd[0]}: rc {r.returncode} {r.stderr.strip()[:200]}"
+    return {"error": last}
+
+
+def _trim_clocks(j):
+    """The current clock of each clock domain in an smi JSON dump, in MHz
+    (keys ending in clk/value, or cur_clk-like entries)."""
+    out = {}
+
+    def walk(x, path):
+        if isinstance(x, dict):
+            for k, v in x.items():
+                walk(v, path + [str(k)])
+        elif isinstance(x, list):
+            for i, v in enumerate(x):
+                walk(v, path + [str(i)])
+        else:
+            if len(path) >= 3 and path[-1] == "value" and path[-2] == "clk":
+                out[path[-3]] = x
+            elif "sclk" in "/".join(path).lower() or "mclk" in "/".join(path).lower():
+                out["/".join(path[-2:])] = x
+    walk(j, [])
+    return out
 
 
 COPY_BYTES = 256 << 20
@@ -325,7 +429,9 @@ def profile_run(which, h, I, mk, to_dev, dev):
 def other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev):
     import torch
     out = {}
-    # GEMM + ReduceScatter
+    # GEMM + ReduceScatter: fused (in-epilogue reduction, the default),
+    # compute alone (no peer partials), transfer alone (no compute: the
+    # reduce and scatter bytes), with 32 reduce workgroups
     name = "gemm_rs_w8_8192x8192x3584"
     log(f"[bench] {name}")
     wl = I.CONFIGS[name]
@@ -337,12 +443,9 @@ def other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev):
     peers = [None] + [to_dev_f32(x) for x in d["peers"][1:]]
     c_own = torch.empty((ms, n), dtype=torch.bfloat16, device=dev)
     outbox = [None] + [torch.empty((ms, n), dtype=torch.bfloat16, device=dev) for _ in range(W - 1)]
-    t = float(np.median(time_calls(lambda: h.gemm_rs(a, bt, peers, c_own, outbox, rank=0), 20, 3)))
-    byts = (W - 1) * ms * n * 4 + ms * n * 2 + (W - 1) * ms * n * 2
-    out[name] = {"ms": round(t, 4), "tflops": round(wl.flops() / (t * 1e-3) / 1e12, 2),
-                 "mfma_frac": round(wl.flops() / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                 "reduce_scatter_GBps": round(byts / (t * 1e-3) / 1e9, 1),
-                 "roles": h.last_launch(mk.OP_GEMM_RS)[0]}
+    rs = lambda fl=0: h.gemm_rs(a, bt, peers, c_own, outbox, rank=0, flags=fl)
+    out[name] = reduce_op_legs(h, mk, mk.OP_GEMM_RS, rs, time_calls, wl.flops(),
+                               (W - 1) * ms * n * 4 + ms * n * 2 + (W - 1) * ms * n * 2)
     del a, bt, peers, c_own, outbox, d
     torch.cuda.empty_cache()
 
@@ -357,12 +460,11 @@ def other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev):
     peers = [None] + [to_dev_f32(x) for x in d["peers"][1:]]
     c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     bc = [torch.empty((m, n), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
-    t = float(np.median(time_calls(lambda: h.gemm_ar(a, bt, peers, c, bc, rank=0), 20, 3)))
+    ar = lambda fl=0: h.gemm_ar(a, bt, peers, c, bc, rank=0, flags=fl)
     byts = (W - 1) * m * n * 4 + (1 + nb) * m * n * 2 + (m * k + n * k) * 2
-    out[name] = {"ms": round(t, 4), "tflops": round(wl.flops() / (t * 1e-3) / 1e12, 2),
-                 "hbm_GBps": round(byts / (t * 1e-3) / 1e9, 1),
-                 "hbm_frac": round(byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                 "roles": h.last_launch(mk.OP_GEMM_AR)[0]}
+    out[name] = reduce_op_legs(h, mk, mk.OP_GEMM_AR, ar, time_calls, wl.flops(), byts)
+    out[name]["hbm_GBps"] = round(byts / (out[name]["ms"] * 1e-3) / 1e9, 1)
+    out[name]["hbm_frac"] = round(out[name]["hbm_GBps"] / PEAK_HBM_GBS, 4)
     del a, bt, peers, c, bc, d
     torch.cuda.empty_cache()
 
@@ -460,10 +562,51 @@ def other_ops(h, I, mk, to_dev, to_dev_f32, time_calls, dev):
     return out
 
 
+def reduce_op_legs(h, mk, op, call, time_calls, flops, comm_bytes):
+    """GEMM+RS / GEMM+AR: fused (default roles), compute alone (MK_F_NO_PEERS),
+    transfer alone (n_compute = 0: reduce workgroups move the reduce and
+    scatter bytes), and fused with 32 reduce workgroups; overlap efficiency
+    = max(compute alone, transfer alone) / fused."""
+    t = float(np.median(time_calls(call, 20, 5)))
+    roles = h.last_launch(op)[0]
+    t_gemm = float(np.median(time_calls(lambda: call(mk.F_NO_PEERS), 20, 3)))
+
+    def with_roles(**r):
+        def f():
+            h.set_roles(op, **r)
+            try:
+                call()
+            finally:
+                h.set_roles(op)
+        return f
+
+    t_xfer = float(np.median(time_calls(with_roles(n_compute=0), 20, 3)))
+    t_red = float(np.median(time_calls(with_roles(n_reduce=32), 20, 3)))
+    return {"ms": round(t, 4), "tflops": round(flops / (t * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "comm_GBps": round(comm_bytes / (t * 1e-3) / 1e9, 1), "roles": roles,
+            "t_compute_alone_ms": round(t_gemm, 4), "t_transfer_alone_ms": round(t_xfer, 4),
+            "transfer_alone_GBps": round(comm_bytes / (t_xfer * 1e-3) / 1e9, 1),
+            "efficiency": round(max(t_gemm, t_xfer) / t, 4),
+            "t_fused_32_reduce_wgs_ms": round(t_red, 4)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(I, flops_full):
-    """The float64 CPU oracle on a bounded sample of the headline workload:
-    the first R output rows (all 3584 columns, K = 8192, the gather included),
-    R chosen from a short calibration so the sample takes about 10 s."""
+    """The float64 CPU oracle on the headline workload: the first R output
+    rows (all 3584 columns, K = 8192, the gather included), R chosen from a
+    short calibration so one run takes about 10 s (at most the whole
+    workload); median of 3 runs."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -480,14 +623,18 @@ def cpu_baseline(I, flops_full):
     t_cal = time.perf_counter() - t0
     R = int(min(m_total, max(128, 128 * 10.0 / max(t_cal, 1e-3))))
     rows = np.arange(R)
-    t0 = time.perf_counter()
-    O.ag_gemm_rows(d["shards"], d["b"], rows)
-    t = time.perf_counter() - t0
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        O.ag_gemm_rows(d["shards"], d["b"], rows)
+        runs.append(time.perf_counter() - t0)
+    t = float(np.median(runs))
     fl = flops_full * R / m_total
     return {"value": round(fl / t / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "runs_s": [round(x, 3) for x in runs],
             "sample": f"{R} of {m_total} output rows of {WORKLOAD} (all columns, K=8192), "
-                      f"float64 numpy matmul with the gather, {t:.1f} s"}
+                      f"float64 numpy matmul with the gather; median of 3 runs, {t:.2f} s"}
 
 
 if __name__ == "__main__":

@@ -83,6 +83,11 @@ mk_status hip_fail(mk_ctx *h, hipError_t e, const char *what) {
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Workspace of a handle when mk_config.workspace_bytes is 0: enough for every
+// operation at the library's reference workloads (the largest user is the
+// GEMM+AllReduce reduce role, [2048, 8192] fp32 = 64 MiB).
+constexpr size_t kDefaultWorkspace = (size_t)128 << 20;
+
 // A buffer of `bytes` bytes at p must end inside the allocation that holds p.
 // The runtime knows the extent of device and pinned host allocations; where
 // it reports none, nothing is checked.  A caching allocator's blocks sit
@@ -230,6 +235,44 @@ void record(mk_ctx *h, mk_op op, int land, int compute, int reduce, int grid) {
   h->launched[op] = true;
 }
 
+// Roles of a GEMM+ReduceScatter / GEMM+AllReduce launch.
+//   compute  workgroups that run tiles (0: transfer alone)
+//   reduce   workgroups that take reduce items first (they take the first
+//            tickets); by default none: the tile epilogues read the peers'
+//            partials themselves
+//   items    the fused launch has reduce items (reduce > 0 and something to
+//            reduce)
+//   xfer     transfer alone: reduce workgroups move the operation's
+//            reduce and scatter bytes, nothing is computed
+//   joins    reduce workgroups run tiles once every item is claimed
+struct Roles {
+  int compute = 0, reduce = 0;
+  bool items = false, xfer = false;
+  int joins = 0;
+};
+
+mk_status choose_reduce_roles(mk_ctx *h, mk_op op, int gmax, int n_tiles, bool has_peers, unsigned flags,
+                              Roles *out) {
+  const mk_roles &r = h->roles[op];
+  if (r.n_land > 0) return fail(h, MK_ERR_INVALID, "this operation has no land role");
+  Roles ro;
+  if (r.n_compute == 0) {  // transfer alone
+    if (flags & MK_F_NO_PEERS)
+      return fail(h, MK_ERR_INVALID, "transfer alone (n_compute = 0) with MK_F_NO_PEERS moves nothing");
+    ro.xfer = true;
+    ro.reduce = std::max(1, std::min(r.n_reduce > 0 ? r.n_reduce : gmax, 4 * gmax));
+    *out = ro;
+    return MK_OK;
+  }
+  ro.reduce = r.n_reduce > 0 ? std::min(r.n_reduce, 4 * gmax) : 0;
+  if (r.n_compute > 0) ro.compute = std::min(r.n_compute, 4 * gmax);
+  else ro.compute = std::max(1, std::min(n_tiles, gmax - ro.reduce));
+  ro.items = ro.reduce > 0 && has_peers;
+  ro.joins = (flags & MK_F_STATIC_ROLES) ? 0 : 1;
+  *out = ro;
+  return MK_OK;
+}
+
 mk_status check_common(mk_ctx *h, int world, int rank) {
   if (!h) return MK_ERR_INVALID;
   h->err.clear();
@@ -247,22 +290,14 @@ mk_status check_gemm_shape(mk_ctx *h, long m, long n, long k) {
   return MK_OK;
 }
 
-mk_status ensure_ws(mk_ctx *h, size_t bytes) {
+// The workspace is allocated by mk_create (mk_config.workspace_bytes) and
+// never grown by a call: an operation that needs more refuses before
+// launching, so no call allocates, frees or synchronises.
+mk_status need_ws(mk_ctx *h, size_t bytes, const char *what) {
   if (bytes <= h->ws_bytes) return MK_OK;
-  // a previous launch may still use the old workspace
-  hipError_t e = hipDeviceSynchronize();
-  if (e != hipSuccess) return hip_fail(h, e, "hipDeviceSynchronize");
-  if (h->ws) (void)hipFree(h->ws);
-  h->ws = nullptr;
-  h->ws_bytes = 0;
-  size_t b = std::max(bytes, (size_t)1 << 20);
-  e = hipMalloc(&h->ws, b);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(h, MK_ERR_OOM, "workspace allocation failed");
-  }
-  h->ws_bytes = b;
-  return MK_OK;
+  return fail(h, MK_ERR_INVALID, std::string(what) + " needs a workspace of " + std::to_string(bytes) +
+                                     " bytes; the handle has " + std::to_string(h->ws_bytes) +
+                                     " (mk_config.workspace_bytes)");
 }
 
 }  // namespace
@@ -286,6 +321,7 @@ const char *mk_last_error(mk_handle h) { return h ? h->err.c_str() : ""; }
 mk_status mk_create(mk_handle *out, const mk_config *cfg) {
   if (!out || !cfg) return MK_ERR_INVALID;
   if (cfg->flags != 0) return MK_ERR_INVALID;
+  if (cfg->workspace_bytes > ((size_t)1 << 40)) return MK_ERR_INVALID;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device < 0 || cfg->device >= ndev) {
     (void)hipGetLastError();
@@ -316,12 +352,17 @@ mk_status mk_create(mk_handle *out, const mk_config *cfg) {
   if (const char *r = std::getenv("MK_ROLES")) {
     int l = -1, c = -1, d = -1;
     if (std::sscanf(r, "%d,%d,%d", &l, &c, &d) >= 1)
-      for (int i = 0; i < MK_OP_COUNT; ++i) h->roles[i] = mk_roles{l, c, d};
+      for (int i = 0; i < MK_OP_COUNT; ++i) {
+        const bool red = i == MK_OP_GEMM_RS || i == MK_OP_GEMM_AR;  // a reduce role, no land role
+        h->roles[i] = mk_roles{red ? -1 : l, c, red ? d : -1};
+      }
   }
   const size_t flag_bytes = (size_t)mk::kMaxFlags * mk::kFlagStride * sizeof(uint32_t);
   hipError_t e = hipMalloc(reinterpret_cast<void **>(&h->ctrl), sizeof(mk::Ctrl));
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&h->flags), flag_bytes);
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&h->cnt), flag_bytes);
+  h->ws_bytes = cfg->workspace_bytes ? cfg->workspace_bytes : kDefaultWorkspace;
+  if (e == hipSuccess) e = hipMalloc(&h->ws, h->ws_bytes);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     mk_destroy(h);
@@ -353,6 +394,9 @@ mk_status mk_destroy(mk_handle h) {
 
 mk_status mk_set_roles(mk_handle h, mk_op op, const mk_roles *roles) {
   if (!h || !roles || op < 0 || op >= MK_OP_COUNT) return MK_ERR_INVALID;
+  h->err.clear();
+  if (roles->n_reduce > 0 && op != MK_OP_GEMM_RS && op != MK_OP_GEMM_AR)
+    return fail(h, MK_ERR_INVALID, "only GEMM+ReduceScatter and GEMM+AllReduce have a reduce role");
   h->roles[op] = *roles;
   return MK_OK;
 }
@@ -534,12 +578,13 @@ mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const m
                      mk_bf16 *const *outbox, int m, int n, int k, unsigned flags) {
   mk_status st = check_common(h, world, rank);
   if (st != MK_OK) return st;
-  if (flags) return fail(h, MK_ERR_INVALID, "unknown flag bits");
+  if (flags & ~(MK_F_NO_PEERS | MK_F_STATIC_ROLES)) return fail(h, MK_ERR_INVALID, "unknown flag bits");
   if (world > 1 && (!peer_part || !outbox)) return fail(h, MK_ERR_INVALID, "peer_part / outbox is NULL");
   st = check_gemm_shape(h, m, n, k);
   if (st != MK_OK) return st;
   if (m % world) return fail(h, MK_ERR_INVALID, "m must be a multiple of world");
   DeviceGuard g(h->device);
+  const bool no_peers = (flags & MK_F_NO_PEERS) != 0;
   mk::RsParams p;
   std::memset(&p, 0, sizeof(p));
   const void *dp;
@@ -552,9 +597,11 @@ mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const m
   for (int q = 0; q < world; ++q) {
     if (q == rank) continue;
     char what[32];
-    std::snprintf(what, sizeof(what), "peer_part[%d]", q);
-    if ((st = resolve(h, peer_part[q], (size_t)(m / world) * n * 4, true, &dp, what)) != MK_OK) return st;
-    p.peer_c[q < rank ? q : q - 1] = static_cast<const float *>(dp);
+    if (!no_peers) {  // compute alone reads no partial
+      std::snprintf(what, sizeof(what), "peer_part[%d]", q);
+      if ((st = resolve(h, peer_part[q], (size_t)(m / world) * n * 4, true, &dp, what)) != MK_OK) return st;
+      p.peer_c[q < rank ? q : q - 1] = static_cast<const float *>(dp);
+    }
     std::snprintf(what, sizeof(what), "outbox[%d]", q);
     if ((st = resolve(h, outbox[q], (size_t)(m / world) * n * 2, true, &dp, what)) != MK_OK) return st;
     p.outbox[q] = static_cast<uint16_t *>(const_cast<void *>(dp));
@@ -566,21 +613,43 @@ mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const m
   p.n = n;
   p.k = k;
   p.ms = m / world;
+  p.no_peers = no_peers ? 1 : 0;
   p.tiles_m = cdiv(m, bm);
   p.tiles_n = cdiv(n, bm);
   p.n_tiles = p.tiles_m * p.tiles_n;
-  p.mb0 = (rank * p.ms) / bm;
   p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapRounds;
   const int gmax = max_grid(h, MK_OP_GEMM_RS, bm);
-  int land = 0, compute = 0;
-  choose_roles(h, MK_OP_GEMM_RS, gmax, 0, p.n_tiles, &land, &compute);
-  p.n_compute = compute;
-  rounds_order(p.tiles_m, p.tiles_n, std::max(1, compute), bm, bm, &p.tile_group_m, &p.tile_split_m);
-  const int grid = std::max(1, compute);
-  p.sync = make_sync(h, 0);
+  const int lo = rank * p.ms, hi = lo + p.ms;
+  const int mb_lo = lo / bm, mb_hi = (hi - 1) / bm;
+  Roles ro;
+  if ((st = choose_reduce_roles(h, MK_OP_GEMM_RS, gmax, p.n_tiles, world > 1 && !no_peers, flags, &ro)) != MK_OK)
+    return st;
+  p.n_compute = ro.compute;
+  p.red.n_reduce = ro.reduce;
+  p.red.xfer_only = ro.xfer;
+  p.red.joins_compute = ro.joins;
+  if (ro.xfer) {  // transfer alone: every tile's rows, no flags
+    p.red.mb_lo = 0;
+    p.red.mbs = p.tiles_m;
+    p.red.n_items = p.n_tiles;
+  } else if (ro.items) {  // the own slice's tiles
+    p.red.mb_lo = mb_lo;
+    p.red.mbs = mb_hi - mb_lo + 1;
+    p.red.n_items = p.red.mbs * p.tiles_n;
+    if (p.red.n_items > mk::kMaxFlags) return fail(h, MK_ERR_UNSUPPORTED, "too many reduce items for the flags");
+    if ((st = need_ws(h, (size_t)p.ms * n * 4, "the GEMM+ReduceScatter reduce role")) != MK_OK) return st;
+    p.red.ws = static_cast<float *>(h->ws);
+    p.red.light_acquire = n % 32 == 0 ? 1 : 0;
+  }
+  // tile order: the own slice first (its epilogue reads the peers' partials,
+  // the heaviest), or last when the reduce role sums the partials meanwhile
+  p.mb0 = p.red.n_items > 0 && !ro.xfer ? (mb_hi + 1) % p.tiles_m : mb_lo;
+  const int grid = std::max(1, ro.reduce + ro.compute);
+  rounds_order(p.tiles_m, p.tiles_n, grid, bm, bm, &p.tile_group_m, &p.tile_split_m);
+  p.sync = make_sync(h, ro.xfer ? 0u : (uint32_t)p.red.n_items);
   hipError_t e = mk::launch_rs(p, bm, grid, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(h, e, "launching the GEMM+ReduceScatter kernel");
-  record(h, MK_OP_GEMM_RS, 0, compute, 0, grid);
+  record(h, MK_OP_GEMM_RS, 0, ro.compute, ro.reduce, grid);
   return MK_OK;
 }
 
@@ -591,13 +660,14 @@ mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const m
                      mk_bf16 *const *bcast, int n_bcast, int m, int n, int k, unsigned flags) {
   mk_status st = check_common(h, world, rank);
   if (st != MK_OK) return st;
-  if (flags) return fail(h, MK_ERR_INVALID, "unknown flag bits");
+  if (flags & ~(MK_F_NO_PEERS | MK_F_STATIC_ROLES)) return fail(h, MK_ERR_INVALID, "unknown flag bits");
   if (n_bcast < 0 || n_bcast > MK_MAX_WORLD) return fail(h, MK_ERR_INVALID, "n_bcast out of range");
   if (world > 1 && !peer_part) return fail(h, MK_ERR_INVALID, "peer_part is NULL");
   if (n_bcast > 0 && !bcast) return fail(h, MK_ERR_INVALID, "bcast is NULL");
   st = check_gemm_shape(h, m, n, k);
   if (st != MK_OK) return st;
   DeviceGuard g(h->device);
+  const bool no_peers = (flags & MK_F_NO_PEERS) != 0;
   mk::ArParams p;
   std::memset(&p, 0, sizeof(p));
   const void *dp;
@@ -607,7 +677,7 @@ mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const m
   p.bt = static_cast<const uint16_t *>(dp);
   if ((st = resolve(h, c, (size_t)m * n * 2, true, &dp, "c")) != MK_OK) return st;
   p.c = static_cast<uint16_t *>(const_cast<void *>(dp));
-  for (int q = 0; q < world; ++q) {
+  for (int q = 0; q < world && !no_peers; ++q) {
     if (q == rank) continue;
     char what[32];
     std::snprintf(what, sizeof(what), "peer_part[%d]", q);
@@ -627,20 +697,36 @@ mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const m
   p.m = m;
   p.n = n;
   p.k = k;
+  p.no_peers = no_peers ? 1 : 0;
   p.tiles_m = cdiv(m, bm);
   p.tiles_n = cdiv(n, bm);
   p.n_tiles = p.tiles_m * p.tiles_n;
   p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapGlobal;
   const int gmax = max_grid(h, MK_OP_GEMM_AR, bm);
-  int land = 0, compute = 0;
-  choose_roles(h, MK_OP_GEMM_AR, gmax, 0, p.n_tiles, &land, &compute);
-  p.n_compute = compute;
-  rounds_order(p.tiles_m, p.tiles_n, std::max(1, compute), bm, bm, &p.tile_group_m, &p.tile_split_m);
-  const int grid = std::max(1, compute);
-  p.sync = make_sync(h, 0);
+  Roles ro;
+  if ((st = choose_reduce_roles(h, MK_OP_GEMM_AR, gmax, p.n_tiles, world > 1 && !no_peers, flags, &ro)) != MK_OK)
+    return st;
+  p.n_compute = ro.compute;
+  p.red.n_reduce = ro.reduce;
+  p.red.xfer_only = ro.xfer;
+  p.red.joins_compute = ro.joins;
+  if (ro.xfer || ro.items) {  // every tile is a reduce item
+    p.red.mb_lo = 0;
+    p.red.mbs = p.tiles_m;
+    p.red.n_items = p.n_tiles;
+  }
+  if (ro.items && !ro.xfer) {
+    if (p.red.n_items > mk::kMaxFlags) return fail(h, MK_ERR_UNSUPPORTED, "too many reduce items for the flags");
+    if ((st = need_ws(h, (size_t)m * n * 4, "the GEMM+AllReduce reduce role")) != MK_OK) return st;
+    p.red.ws = static_cast<float *>(h->ws);
+    p.red.light_acquire = n % 32 == 0 ? 1 : 0;
+  }
+  const int grid = std::max(1, ro.reduce + ro.compute);
+  rounds_order(p.tiles_m, p.tiles_n, grid, bm, bm, &p.tile_group_m, &p.tile_split_m);
+  p.sync = make_sync(h, ro.xfer ? 0u : (uint32_t)p.red.n_items);
   hipError_t e = mk::launch_ar(p, bm, grid, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(h, e, "launching the GEMM+AllReduce kernel");
-  record(h, MK_OP_GEMM_AR, 0, compute, 0, grid);
+  record(h, MK_OP_GEMM_AR, 0, ro.compute, ro.reduce, grid);
   return MK_OK;
 }
 
@@ -743,7 +829,7 @@ static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
   const size_t sz_tiles = (size_t)(max_row_tiles + 2) * sizeof(int32_t);
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t total = al(sz_items) * 2 + al(sz_rank) + al(sz_gate) * 2 + al(sz_tiles);
-  if ((st = ensure_ws(h, total)) != MK_OK) return st;
+  if ((st = need_ws(h, total, "the MoE dispatch")) != MK_OK) return st;
   char *w = static_cast<char *>(h->ws);
   p.item_cnt = reinterpret_cast<int32_t *>(w);
   w += al(sz_items);
@@ -874,7 +960,7 @@ mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, 
   p.merge_flag0 = (uint32_t)p.n_items;
   if (p.splits == 2) {
     const size_t slot = (size_t)(128 * 128 + 2 * 128) * sizeof(float);
-    if ((st = ensure_ws(h, slot * p.n_pairs)) != MK_OK) return st;
+    if ((st = need_ws(h, slot * p.n_pairs, "ring attention")) != MK_OK) return st;
     p.ws = static_cast<float *>(h->ws);
   }
   // chunks of both receive buffers start and end on 128-byte lines

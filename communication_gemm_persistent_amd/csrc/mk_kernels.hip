@@ -242,21 +242,30 @@ __device__ __forceinline__ f32x4_t sum_peers(const f32x4_t &v, const PeerRow &pr
   return x;
 }
 
-// The epilogues' pointer tables (compact peer list; RS outboxes by rank or
-// AR broadcast buffers), copied to LDS once per launch and read after each
-// tile's K loop.  Taken from the kernel arguments instead, they are loaded
-// into SGPRs at the start and held through the K loop, which then spills
-// its buffer descriptors to VGPR lanes; a descriptor restored right before
-// an LDS DMA violates the 5-wait-state rule for VALU-written SGPRs.
+// The pointer tables of a launch, copied to LDS once and read where they are
+// used.  Taken from the kernel arguments instead, they are loaded into SGPRs
+// at the start and held through the K loop, which then spills its buffer
+// descriptors to VGPR lanes; a descriptor restored right before an LDS DMA
+// violates the 5-wait-state rule for VALU-written SGPRs.
+//   peer  the peers' fp32 partials (compact list, ascending rank)
+//   epi   what a tile's epilogue adds to its accumulators: the peers, the
+//         reduce workspace (one entry), or nothing (compute alone)
+//   dst   RS outboxes by rank, or AR broadcast buffers
 struct PtrTable {
   const float *peer[MK_MAX_WORLD];
+  const float *epi[MK_MAX_WORLD];
   uint16_t *dst[MK_MAX_WORLD];
 };
 
-__device__ __forceinline__ void fill_table(PtrTable *t, const float *const *peer, uint16_t *const *dst) {
+// Which list the tile epilogues add.
+constexpr int kEpiNone = 0, kEpiWs = 1, kEpiPeers = 2;
+
+__device__ __forceinline__ void fill_table(PtrTable *t, const float *const *peer, uint16_t *const *dst,
+                                           const float *ws, int epi) {
   if (threadIdx.x < MK_MAX_WORLD) {
     t->peer[threadIdx.x] = peer[threadIdx.x];
     t->dst[threadIdx.x] = dst[threadIdx.x];
+    t->epi[threadIdx.x] = epi == kEpiPeers ? peer[threadIdx.x] : threadIdx.x == 0 && epi == kEpiWs ? ws : nullptr;
   }
   __syncthreads();
 }
@@ -317,7 +326,137 @@ __device__ __forceinline__ bool with_peer_count(int np, Body &&body) {
   }
 }
 
+// ---------------------------------------------------------------- reduce role
+
+constexpr int kRedToWs = 0, kRedToOut = 1, kRedZero = 2;
+
+// The four-column groups of rows [r0, r0 + rows) x columns [c0, c0 + cols)
+// of a row-major layout of row pitch n (cols a multiple of 4), with the whole
+// workgroup.  kRedToWs: the fp32 sum of the np partials pc[] (ascending
+// rank) goes to ws; kRedToOut: the sum, rounded to bf16, goes to d0 and to
+// every extra[0..n_extra); kRedZero: bf16 zeros go there and nothing is
+// read.  d0, ws and the partials share the layout.  With a peer count known
+// at compile time each thread issues the loads of its next group before it
+// stores the current one (group indices past the end load a group of the
+// region and store nothing, so no load needs a branch).
+template <int MODE>
+__device__ __forceinline__ void reduce_region(const float *const *pc, int np, float *ws, uint16_t *d0,
+                                              uint16_t *const *extra, int n_extra, size_t r0, int rows,
+                                              int c0, int cols, size_t n) {
+  const int cg = cols >> 2;
+  const int G = rows * cg;
+  const int nt = blockDim.x;
+  if (G <= 0) return;
+  auto off = [&](int g) {
+    g = min(g, G - 1);
+    return (r0 + (size_t)(g / cg)) * n + (size_t)c0 + (size_t)(g % cg) * 4;
+  };
+  auto put = [&](int g, const f32x4_t &x) {
+    if (g >= G) return;
+    const size_t o = off(g);
+    if constexpr (MODE == kRedToWs) {
+      *reinterpret_cast<f32x4_t *>(ws + o) = x;
+    } else {
+      const uint2 b = MODE == kRedZero ? make_uint2(0u, 0u) : pack_bf16x4(x[0], x[1], x[2], x[3]);
+      store_nt(d0 + o, b);
+      for (int i = 0; i < n_extra; ++i) store_nt(table_ptr(extra[i]) + o, b);
+    }
+  };
+  if constexpr (MODE == kRedZero) {
+    for (int g = (int)threadIdx.x; g < G; g += nt) put(g, f32x4_t{});
+    return;
+  } else {
+    if (!with_peer_count(np, [&](auto npc) {
+          constexpr int NP = decltype(npc)::value;
+          const float *p[NP > 0 ? NP : 1];
+#pragma unroll
+          for (int i = 0; i < NP; ++i) p[i] = table_ptr(pc[i]);
+          int g = (int)threadIdx.x;
+          auto va = load_peer_vals<NP>(p, off(g));
+#pragma unroll 1
+          for (; g < G; g += 2 * nt) {
+            auto vb = load_peer_vals<NP>(p, off(g + nt));
+            put(g, add_peer_vals<NP>(f32x4_t{}, va));
+            va = load_peer_vals<NP>(p, off(g + 2 * nt));
+            put(g + nt, add_peer_vals<NP>(f32x4_t{}, vb));
+          }
+        })) {
+      for (int g = (int)threadIdx.x; g < G; g += nt) {
+        PeerRow pr;
+        load_peers(pr, pc, np, off(g));
+        put(g, sum_peers(f32x4_t{}, pr, np));
+      }
+    }
+  }
+}
+
+// Release reduce item `it` (flag index = item) after the workgroup's stores
+// of it: every thread waits for its own stores, then one release fence
+// writes this XCD's L2 back before the flag moves.
+__device__ __forceinline__ void red_release(const Sync &s, uint32_t it) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    fence_release();
+    st_release(flag_ptr(s, it), s.epoch);
+  }
+  __syncthreads();
+}
+
+// Claim and process reduce items until none is left.  release: each item's
+// flag is released after its stores.
+template <class Item>
+__device__ __forceinline__ void red_loop(const Sync &s, int n_items, bool release, Item &&item,
+                                         uint32_t *s_word) {
+  for (;;) {
+    const uint32_t it = next_index(&s.ctrl->reduce_ctr, s_word);
+    if (it >= (uint32_t)n_items) break;
+    item((int)it);
+    if (release) red_release(s, it);
+  }
+}
+
+// After the K loop of a tile whose epilogue needs reduce item `it`: wait for
+// the item (thread 0) and acquire it.  Compute workgroups never reduce items
+// themselves: every item is taken by a reduce workgroup, and those took the
+// first tickets and wait for nothing, so every item a tile waits for is done
+// by a running workgroup.
+__device__ __forceinline__ bool red_wait(const Sync &s, uint32_t it, bool light, uint32_t *s_word) {
+  bool ok0 = true;
+  if (threadIdx.x == 0) ok0 = spin_until_eq(s, flag_ptr(s, it), s.epoch, 0x52000000u | it);
+  return wg_sync_ok(ok0, s_word, !light);
+}
+
 // ---------------------------------------------------------------- GEMM + ReduceScatter
+
+// Reduce item `it`: the own-slice rows of tile (mb_lo + it / tiles_n,
+// it % tiles_n) -- or, with no compute, every row of that tile, whose own
+// rows get bf16 of the peers' sum and whose other rows get zeros in their
+// outbox.
+template <int BM, int BN>
+__device__ __forceinline__ void rs_reduce_item(const RsParams &p, const PtrTable &tab, int it) {
+  const int mb = p.red.mb_lo + it / p.tiles_n, nb = it % p.tiles_n;
+  const int c0 = nb * BN, cols = min(BN, p.n - c0);
+  int r0 = mb * BM;
+  const int r1 = min(r0 + BM, p.m);
+  const int lo = p.rank * p.ms;
+  if (!p.red.xfer_only) {
+    const int a = max(r0, lo), b = min(r1, lo + p.ms);
+    reduce_region<kRedToWs>(tab.peer, p.world - 1, p.red.ws, nullptr, nullptr, 0, (size_t)(a - lo), b - a,
+                            c0, cols, (size_t)p.n);
+    return;
+  }
+  while (r0 < r1) {  // rows of one slice at a time
+    const int q = r0 / p.ms, b = min(r1, (q + 1) * p.ms);
+    if (q == p.rank)
+      reduce_region<kRedToOut>(tab.peer, p.world - 1, nullptr, p.c_own, nullptr, 0, (size_t)(r0 - lo),
+                               b - r0, c0, cols, (size_t)p.n);
+    else
+      reduce_region<kRedZero>(nullptr, 0, nullptr, table_ptr(tab.dst[q]), nullptr, 0,
+                              (size_t)(r0 - q * p.ms), b - r0, c0, cols, (size_t)p.n);
+    r0 = b;
+  }
+}
 
 template <int BM, int BN>
 __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &tab, char *smem,
@@ -325,11 +464,16 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &ta
   using C = TileCfg<BM, BN>;
   const int xcd = xcd_id();
   const int lda = p.k * 2;
+  // what the epilogues add to the own slice: the peers' partials, or their
+  // sum from the reduce role's workspace, or nothing (compute alone)
+  const bool red = p.red.n_items > 0;
+  const int enp = red ? 1 : p.no_peers ? 0 : p.world - 1;
+  const int lo = p.rank * p.ms, hi = lo + p.ms;
   for (;;) {
     const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, TileOrder{p.tile_map, p.tile_group_m, p.tile_split_m}, s_word);
     if (t < 0) break;
     const int mi = t / p.tiles_n, nb = t % p.tiles_n;
-    const int mb = (mi + p.mb0) % p.tiles_m;   // own slice first: its epilogue is the heaviest
+    const int mb = (mi + p.mb0) % p.tiles_m;   // tile order: see the launcher
     const int m0 = mb * BM, n0 = nb * BN;
     const int m1 = min(m0 + BM, p.m);
     const int valid_n = min(BN, p.n - n0);
@@ -337,16 +481,22 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &ta
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * lda));
     AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
+    // the reduce item of this tile's own-slice rows (worked out after the K
+    // loop: values held across it cost registers the loop needs)
+    if (red && m0 < hi && m1 > lo &&
+        !red_wait(p.sync, (uint32_t)((m0 / BM - p.red.mb_lo) * p.tiles_n + n0 / BN), p.red.light_acquire != 0,
+                  s_word))
+      break;
     const int cols = min(BN, p.n - n0);
-    // Row r of slice q: the own slice adds the peers' partials and goes to
+    // Row r of slice q: the own slice adds the epilogue list and goes to
     // c_own, any other slice to outbox[q].
     auto epi_row = [&](int row, int cc, const f32x4_t &v, int q, uint16_t *d) {
       const size_t off = (size_t)(row - q * p.ms) * p.n + n0 + cc;
       f32x4_t x = v;
       if (q == p.rank) {
-        PeerRow pr;  // all peers' loads are issued before any is used
-        load_peers(pr, tab.peer, p.world - 1, off);
-        x = sum_peers(v, pr, p.world - 1);
+        PeerRow pr;  // all loads are issued before any is used
+        load_peers(pr, tab.epi, enp, off);
+        x = sum_peers(v, pr, enp);
       }
       store_nt(d + off, pack_bf16x4(x[0], x[1], x[2], x[3]));
     };
@@ -357,8 +507,8 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &ta
     // also waits for every store before it).
     const int q0 = m0 / p.ms;
     if ((m1 - 1) / p.ms == q0 && q0 == p.rank) {
-      // own slice: the peers' partials of the next column group are loaded
-      // before this one is stored
+      // own slice: the partials of the next column group are loaded before
+      // this one is stored
       const int r0 = m0 - q0 * p.ms, rows = m1 - m0;
       auto put = [&](int r, int cc, const f32x4_t &x) {
         if (r < rows && cc < cols)
@@ -367,11 +517,11 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &ta
       // addresses clamped into the tile: a group past its edge loads an
       // element of the tile that it does not use, so no load needs a branch
       auto off_in = [&](int r, int cc) { return (size_t)(r0 + min(r, rows - 1)) * p.n + n0 + min(cc, cols - 4); };
-      if (!with_peer_count(p.world - 1, [&](auto np) {
+      if (!with_peer_count(enp, [&](auto np) {
             constexpr int NP = decltype(np)::value;
             const float *pc[NP > 0 ? NP : 1];
 #pragma unroll
-            for (int i = 0; i < NP; ++i) pc[i] = table_ptr(tab.peer[i]);
+            for (int i = 0; i < NP; ++i) pc[i] = table_ptr(tab.epi[i]);
             staged_epilogue_pf<BM, BN>(
                 acc, smem, [&](int r, int cc) { return load_peer_vals<NP>(pc, off_in(r, cc)); },
                 [&](int r, int cc, const f32x4_t &v, const PeerVals<NP> &pv) { put(r, cc, add_peer_vals<NP>(v, pv)); });
@@ -379,8 +529,8 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &ta
         staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
           if (r < rows && cc < cols) {
             PeerRow pr;
-            load_peers(pr, tab.peer, p.world - 1, off_in(r, cc));
-            put(r, cc, sum_peers(v, pr, p.world - 1));
+            load_peers(pr, tab.epi, enp, off_in(r, cc));
+            put(r, cc, sum_peers(v, pr, enp));
           }
         });
     } else if ((m1 - 1) / p.ms == q0) {
@@ -404,13 +554,38 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_rs_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
   __shared__ PtrTable s_tab;
-  fill_table(&s_tab, p.peer_c, p.outbox);
+  fill_table(&s_tab, p.peer_c, p.outbox, p.red.ws,
+             p.red.n_items > 0 && !p.red.xfer_only ? kEpiWs : p.no_peers ? kEpiNone : kEpiPeers);
+  // reduce workgroups take the first tickets: every item a tile waits for
+  // belongs to a workgroup that is already running
   const uint32_t ticket = take_ticket(p.sync, &s_word);
-  if (ticket < (uint32_t)p.n_compute) rs_compute<BM, BN>(p, s_tab, smem, &s_word);
+  const uint32_t nr = (uint32_t)p.red.n_reduce;
+  if (ticket < nr) {
+    red_loop(p.sync, p.red.n_items, !p.red.xfer_only, [&](int it) { rs_reduce_item<BM, BN>(p, s_tab, it); },
+             &s_word);
+    if (p.red.joins_compute) rs_compute<BM, BN>(p, s_tab, smem, &s_word);
+  } else if (ticket < nr + (uint32_t)p.n_compute) {
+    rs_compute<BM, BN>(p, s_tab, smem, &s_word);
+  }
   finish_launch(p.sync);
 }
 
 // ---------------------------------------------------------------- GEMM + AllReduce
+
+// Reduce item `it` = tile it: the peers' sum into the workspace, or, with no
+// compute, bf16 of it to c and every broadcast buffer.
+template <int BM, int BN>
+__device__ __forceinline__ void ar_reduce_item(const ArParams &p, const PtrTable &tab, int it) {
+  const int mb = it / p.tiles_n, nb = it % p.tiles_n;
+  const int c0 = nb * BN, cols = min(BN, p.n - c0);
+  const int r0 = mb * BM, rows = min(BM, p.m - r0);
+  if (!p.red.xfer_only)
+    reduce_region<kRedToWs>(tab.peer, p.world - 1, p.red.ws, nullptr, nullptr, 0, (size_t)r0, rows, c0,
+                            cols, (size_t)p.n);
+  else
+    reduce_region<kRedToOut>(tab.peer, p.world - 1, nullptr, p.c, tab.dst, p.n_bcast, (size_t)r0, rows, c0,
+                             cols, (size_t)p.n);
+}
 
 template <int BM, int BN>
 __device__ __forceinline__ void ar_compute(const ArParams &p, const PtrTable &tab, char *smem,
@@ -418,6 +593,8 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, const PtrTable &ta
   using C = TileCfg<BM, BN>;
   const int xcd = xcd_id();
   const int lda = p.k * 2;
+  const bool red = p.red.n_items > 0;
+  const int enp = red ? 1 : p.no_peers ? 0 : p.world - 1;
   for (;;) {
     const int t = next_tile(p.sync, p.tiles_m, p.tiles_n, xcd, TileOrder{p.tile_map, p.tile_group_m, p.tile_split_m}, s_word);
     if (t < 0) break;
@@ -429,9 +606,11 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, const PtrTable &ta
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * lda));
     AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
+    if (red && !red_wait(p.sync, (uint32_t)((m0 / BM) * p.tiles_n + n0 / BN), p.red.light_acquire != 0, s_word))
+      break;
     const int cols = min(BN, p.n - n0);
-    // the peers' partials of the next column group are loaded before this
-    // one is stored
+    // the partials of the next column group are loaded before this one is
+    // stored
     const int rows = m1 - m0;
     uint16_t *bc[MK_MAX_WORLD];
 #pragma unroll
@@ -448,11 +627,11 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, const PtrTable &ta
     };
     // addresses clamped into the tile (see the ReduceScatter epilogue)
     auto off_in = [&](int r, int cc) { return (size_t)(m0 + min(r, rows - 1)) * p.n + n0 + min(cc, cols - 4); };
-    if (!with_peer_count(p.world - 1, [&](auto np) {
+    if (!with_peer_count(enp, [&](auto np) {
           constexpr int NP = decltype(np)::value;
           const float *pc[NP > 0 ? NP : 1];
 #pragma unroll
-          for (int i = 0; i < NP; ++i) pc[i] = table_ptr(tab.peer[i]);
+          for (int i = 0; i < NP; ++i) pc[i] = table_ptr(tab.epi[i]);
           staged_epilogue_pf<BM, BN>(
               acc, smem, [&](int r, int cc) { return load_peer_vals<NP>(pc, off_in(r, cc)); },
               [&](int r, int cc, const f32x4_t &v, const PeerVals<NP> &pv) { put(r, cc, add_peer_vals<NP>(v, pv)); });
@@ -460,8 +639,8 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, const PtrTable &ta
       staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
         if (r < rows && cc < cols) {
           PeerRow pr;
-          load_peers(pr, tab.peer, p.world - 1, off_in(r, cc));
-          put(r, cc, sum_peers(v, pr, p.world - 1));
+          load_peers(pr, tab.epi, enp, off_in(r, cc));
+          put(r, cc, sum_peers(v, pr, enp));
         }
       });
   }
@@ -472,9 +651,17 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_ar_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
   __shared__ PtrTable s_tab;
-  fill_table(&s_tab, p.peer_c, p.bcast);
+  fill_table(&s_tab, p.peer_c, p.bcast, p.red.ws,
+             p.red.n_items > 0 && !p.red.xfer_only ? kEpiWs : p.no_peers ? kEpiNone : kEpiPeers);
   const uint32_t ticket = take_ticket(p.sync, &s_word);
-  if (ticket < (uint32_t)p.n_compute) ar_compute<BM, BN>(p, s_tab, smem, &s_word);
+  const uint32_t nr = (uint32_t)p.red.n_reduce;
+  if (ticket < nr) {
+    red_loop(p.sync, p.red.n_items, !p.red.xfer_only, [&](int it) { ar_reduce_item<BM, BN>(p, s_tab, it); },
+             &s_word);
+    if (p.red.joins_compute) ar_compute<BM, BN>(p, s_tab, smem, &s_word);
+  } else if (ticket < nr + (uint32_t)p.n_compute) {
+    ar_compute<BM, BN>(p, s_tab, smem, &s_word);
+  }
   finish_launch(p.sync);
 }
 

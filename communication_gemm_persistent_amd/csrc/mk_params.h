@@ -39,6 +39,25 @@ struct AgParams {
   int light_acquire;       // land blocks are cache-line aligned (see wg_sync_ok)
 };
 
+// Reduce role of GEMM+ReduceScatter and GEMM+AllReduce.  A reduce item is
+// the part of one output tile (tile grid of the GEMM, m-blocks
+// [mb_lo, mb_lo + mbs) x every n-block) whose rows need the peers' partials:
+// RS rows of this rank's slice, AR every row.  In the fused launch a reduce
+// workgroup sums the peers' fp32 partials of an item into the workspace
+// (same layout as the partials) and releases the item's flag (flag index =
+// item); the tile's epilogue then adds the workspace instead of the peers.
+// Transfer alone (no compute workgroups): items cover every tile and write
+// the outputs themselves -- bf16 of the peers' sum where the rows need it,
+// zeros to the RS outboxes -- so the same bytes move as in the fused call.
+struct RedParams {
+  float *ws;
+  int n_reduce;
+  int mb_lo, mbs, n_items;
+  int light_acquire;     // item regions start and end on 128-byte lines of ws
+  int xfer_only;         // no compute: items write the outputs
+  int joins_compute;     // reduce workgroups run tiles once every item is claimed
+};
+
 // GEMM + ReduceScatter.
 struct RsParams {
   Sync sync;
@@ -49,7 +68,9 @@ struct RsParams {
   uint16_t *outbox[MK_MAX_WORLD];
   int world, rank, m, n, k, ms;
   int n_compute;
+  int no_peers;                       // compute alone: epilogues leave out the peers' partials
   int tiles_m, tiles_n, n_tiles, mb0, tile_map, tile_group_m, tile_split_m;
+  RedParams red;
 };
 
 // GEMM + AllReduce.
@@ -62,7 +83,9 @@ struct ArParams {
   uint16_t *bcast[MK_MAX_WORLD];
   int world, rank, n_bcast, m, n, k;
   int n_compute;
+  int no_peers;
   int tiles_m, tiles_n, n_tiles, tile_map, tile_group_m, tile_split_m;
+  RedParams red;
 };
 
 // Ring attention.  Receive buffers are indexed by source rank: k_recv

@@ -34,6 +34,7 @@ OP_RING_ATTN = 4
 F_PRELANDED = 0x1
 F_NO_GATE = 0x2
 F_STATIC_ROLES = 0x4
+F_NO_PEERS = 0x8
 
 MAX_WORLD = 16
 
@@ -52,7 +53,7 @@ class MkError(RuntimeError):
 
 class _Config(ctypes.Structure):
     _fields_ = [("device", ctypes.c_int), ("spin_timeout_ms", ctypes.c_int),
-                ("flags", ctypes.c_uint)]
+                ("flags", ctypes.c_uint), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class Roles(ctypes.Structure):
@@ -141,11 +142,11 @@ def _stream(stream, device: int) -> int:
 class Handle:
     """One libmk handle bound to a device; calls on it must be stream-ordered."""
 
-    def __init__(self, device: int = 0, spin_timeout_ms: int = 0):
+    def __init__(self, device: int = 0, spin_timeout_ms: int = 0, workspace_bytes: int = 0):
         self.lib = load()
         self.device = device
         h = _vp()
-        cfg = _Config(device, spin_timeout_ms, 0)
+        cfg = _Config(device, spin_timeout_ms, 0, workspace_bytes)
         self._check(self.lib.mk_create(ctypes.byref(h), ctypes.byref(cfg)), "mk_create", None)
         self.h = h
 
@@ -213,8 +214,8 @@ class Handle:
         m, k = a.shape
         n = bt.shape[0]
         ms = m // W
-        pp = [0 if q == rank else _ptr(peer_part[q], f"peer_part[{q}]", (torch.float32,), (ms, n))
-              for q in range(W)]
+        pp = [0 if q == rank or (peer_part[q] is None and flags & F_NO_PEERS)
+              else _ptr(peer_part[q], f"peer_part[{q}]", (torch.float32,), (ms, n)) for q in range(W)]
         ob = [0 if q == rank else _ptr(outbox[q], f"outbox[{q}]", _BF16, (ms, n)) for q in range(W)]
         st = self.lib.mk_gemm_rs(self.h, _vp(_stream(stream, self.device)), W, rank,
                                  _ptr(a, "a", _BF16), _ptr(bt, "bt", _BF16, (n, k)), _ptr_array(pp),
@@ -227,8 +228,8 @@ class Handle:
         W = len(peer_part)
         m, k = a.shape
         n = bt.shape[0]
-        pp = [0 if q == rank else _ptr(peer_part[q], f"peer_part[{q}]", (torch.float32,), (m, n))
-              for q in range(W)]
+        pp = [0 if q == rank or (peer_part[q] is None and flags & F_NO_PEERS)
+              else _ptr(peer_part[q], f"peer_part[{q}]", (torch.float32,), (m, n)) for q in range(W)]
         bc = [_ptr(b, f"bcast[{i}]", _BF16, (m, n)) for i, b in enumerate(bcast)]
         st = self.lib.mk_gemm_ar(self.h, _vp(_stream(stream, self.device)), W, rank,
                                  _ptr(a, "a", _BF16), _ptr(bt, "bt", _BF16, (n, k)), _ptr_array(pp),

@@ -21,9 +21,11 @@
  * caller's stream.  Each workgroup takes a ticket from a device counter and
  * becomes a LAND workgroup (copies incoming chunks, then release-stores a
  * per-chunk ready flag), a COMPUTE workgroup (bf16 MFMA GEMM tiles, started
- * as soon as the flags of their rows are seen with acquire semantics), or a
- * REDUCE workgroup (sums and forwards finished tiles).  Role counts are
- * tunable per operation (mk_set_roles).  Every in-kernel wait is bounded by
+ * as soon as the flags of their rows are seen with acquire semantics), or
+ * (GEMM+RS and GEMM+AR) a REDUCE workgroup (sums the peers' partials of a
+ * tile into the workspace and release-stores the tile's flag; the tile's
+ * epilogue adds that sum).  Role counts are tunable per operation
+ * (mk_set_roles).  Every in-kernel wait is bounded by
  * mk_config.spin_timeout_ms; on expiry the kernel records MK_ERR_TIMEOUT,
  * every workgroup leaves its loop and the launch completes.
  *
@@ -86,14 +88,36 @@ typedef enum {
 } mk_op;
 
 typedef struct {
-  int device;          /* HIP device ordinal the handle is bound to */
-  int spin_timeout_ms; /* bound on every in-kernel wait; <= 0 selects 2000 ms */
-  unsigned flags;      /* reserved, must be 0 */
+  int device;             /* HIP device ordinal the handle is bound to */
+  int spin_timeout_ms;    /* bound on every in-kernel wait; <= 0 selects 2000 ms */
+  unsigned flags;         /* reserved, must be 0 */
+  size_t workspace_bytes; /* device workspace the handle owns, allocated by mk_create and
+                             never grown by a call; 0 selects 128 MiB.  Users: the MoE
+                             dispatch (about 16 bytes per routed slot plus 8 per
+                             (token, k) pair), ring attention (66.5 KiB per (head,
+                             128-query tile) pair), the GEMM+RS reduce role ([m/W, n]
+                             fp32) and the GEMM+AR reduce role ([m, n] fp32).  A call
+                             that needs more returns MK_ERR_INVALID before launching. */
 } mk_config;
 
 /* Workgroup role counts of one persistent launch.  A negative value selects
  * the library's default for that role; n_compute = 0 runs only the data
- * movement (used to time transfer alone). */
+ * movement (transfer alone: the outputs then do not hold the operation's
+ * result).
+ *   n_land    AG+GEMM, MoE and ring attention: workgroups that copy incoming
+ *             chunks (the AG, MoE and ring attention launches also let
+ *             compute workgroups land while their rows are missing)
+ *   n_reduce  GEMM+RS and GEMM+AR only (MK_ERR_INVALID elsewhere):
+ *             workgroups that sum the peers' partials of the rows the tiles
+ *             reduce into the workspace, one tile-sized item at a time, each
+ *             released by a flag; a tile's epilogue then adds that sum
+ *             instead of reading every peer.  Reduce workgroups run tiles
+ *             once every item is claimed (not with MK_F_STATIC_ROLES).
+ *             Default 0: the tile epilogues read the peers themselves.
+ *             With n_compute = 0 the reduce workgroups (default: the whole
+ *             grid) move the reduce and scatter bytes alone: bf16 of the
+ *             peers' sum to c_own / c and the broadcast buffers, zeros to
+ *             the RS outboxes. */
 typedef struct {
   int n_land;
   int n_compute;
@@ -104,14 +128,20 @@ typedef struct {
 #define MK_F_PRELANDED 0x1u /* AG: a_gathered already holds the gathered A; ring attention: the
                                receive buffers hold every block; skip landing (compute alone) */
 #define MK_F_NO_GATE 0x2u   /* MoE: store x @ W_e without the gate factor */
-#define MK_F_STATIC_ROLES 0x4u /* AG: every workgroup keeps its ticket role for the whole launch
-                                 (by default compute workgroups land chunks while their rows
-                                 are missing, and land workgroups run tiles once landing is
-                                 done) */
+#define MK_F_STATIC_ROLES 0x4u /* AG, RS, AR: every workgroup keeps its ticket role for the whole
+                                 launch (by default AG compute workgroups land chunks while
+                                 their rows are missing, and land and reduce workgroups run
+                                 tiles once their queue is empty) */
+#define MK_F_NO_PEERS 0x8u     /* RS, AR: compute alone -- the epilogues leave out the peers'
+                                 partials (c_own = bf16 of this rank's own rows, c = bf16(A @ B));
+                                 peer_part is not read and may hold NULL entries.  For timing
+                                 the GEMM with its output traffic. */
 
 /* Create a handle on cfg->device: checks the device is gfx950, allocates the
- * control block (tickets, counters, per-chunk flags, error record).  No
- * kernel runs.  *out is set only on MK_OK. */
+ * control block (tickets, counters, per-chunk flags, error record) and the
+ * workspace (cfg->workspace_bytes).  No kernel runs.  This is the only call
+ * that allocates device memory (mk_destroy frees it).  *out is set only on
+ * MK_OK; MK_ERR_OOM if an allocation fails. */
 mk_status mk_create(mk_handle *out, const mk_config *cfg);
 
 /* Free everything mk_create allocated.  The caller must have synchronised
@@ -167,6 +197,8 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
  *   outbox     host array of W pointers; outbox[q] (q != rank) receives
  *              [ms, n] bf16; entry [rank] ignored
  *   m must be a multiple of W.
+ *   flags: MK_F_NO_PEERS (compute alone), MK_F_STATIC_ROLES.
+ *   Reduce role (mk_set_roles n_reduce > 0): needs [m/W, n] fp32 of workspace.
  */
 mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const mk_bf16 *a,
                      const mk_bf16 *bt, const float *const *peer_part, mk_bf16 *c_own,
@@ -180,6 +212,8 @@ mk_status mk_gemm_rs(mk_handle h, mk_stream stream, int world, int rank, const m
  *   peer_part  host array of W pointers, each [m, n] fp32; entry [rank] ignored
  *   c          output [m, n] bf16;  bcast: host array of n_bcast pointers,
  *              each [m, n] bf16;  0 <= n_bcast <= MK_MAX_WORLD
+ *   flags: MK_F_NO_PEERS (compute alone), MK_F_STATIC_ROLES.
+ *   Reduce role (mk_set_roles n_reduce > 0): needs [m, n] fp32 of workspace.
  */
 mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const mk_bf16 *a,
                      const mk_bf16 *bt, const float *const *peer_part, mk_bf16 *c,

@@ -234,3 +234,171 @@ def test_rs_ar_own_slice_pipelined_epilogue(mk, tile):
                 O.assert_bits_equal(b, c, f"bcast[{i}] vs c")
     finally:
         h.close()
+
+
+# ---------------------------------------------------------------- reduce role
+
+RED_SHAPES = [(8, 3, 2048, 520, 200), (4, 1, 1024, 264, 72), (3, 2, 1500, 776, 136), (2, 0, 512, 256, 64)]
+
+
+@pytest.mark.parametrize("shape", RED_SHAPES)
+@pytest.mark.parametrize("n_reduce", [1, 5, 64])
+@pytest.mark.parametrize("static", [False, True])
+def test_rs_reduce_role_integer_bit_exact(handle, mk, shape, n_reduce, static):
+    """Reduce workgroups sum the peers' partials of the own slice into the
+    workspace; the own tiles' epilogues add that sum.  Integer inputs: every
+    output bit-exact, whatever the role split (slices of 1500 / 3 = 500 rows
+    put own rows in tiles that straddle slices)."""
+    W, rank, m, n, k = shape
+    print(f"rs reduce role n_reduce={n_reduce} static={static} {shape}", flush=True)
+    d = I.gen_rs(W, m, n, k, rank=rank, variant=I.INTEGER, config=380 + W)
+    handle.set_roles(mk.OP_GEMM_RS, n_reduce=n_reduce)
+    try:
+        c_own, outbox = _run_rs_flags(handle, d, rank, mk.F_STATIC_ROLES if static else 0)
+        (_, n_compute, nr), grid = handle.last_launch(mk.OP_GEMM_RS)
+        assert nr == n_reduce and grid == n_reduce + n_compute
+    finally:
+        handle.set_roles(mk.OP_GEMM_RS)
+    check_rs(d, rank, c_own, outbox, exact=True)
+
+
+def _run_rs_flags(h, d, rank, flags):
+    W = len(d["peers"])
+    m, k = d["a"].shape
+    n = d["b"].shape[1]
+    ms = m // W
+    a = dev_bf16(d["a"])
+    bt = dev_bf16(I.transpose_bits(d["b"]))
+    peers = [None if p is None else dev_f32(p) for p in d["peers"]]
+    c_own = empty_bf16((ms, n))
+    outbox = [None if q == rank else empty_bf16((ms, n)) for q in range(W)]
+    h.gemm_rs(a, bt, peers, c_own, outbox, rank=rank, flags=flags)
+    h.sync()
+    return bits(c_own), [None if o is None else bits(o) for o in outbox]
+
+
+def _run_ar_flags(h, d, rank, n_bcast, flags):
+    m, k = d["a"].shape
+    n = d["b"].shape[1]
+    a = dev_bf16(d["a"])
+    bt = dev_bf16(I.transpose_bits(d["b"]))
+    peers = [None if p is None else dev_f32(p) for p in d["peers"]]
+    c = empty_bf16((m, n))
+    bc = [empty_bf16((m, n)) for _ in range(n_bcast)]
+    h.gemm_ar(a, bt, peers, c, bc, rank=rank, flags=flags)
+    h.sync()
+    return bits(c), [bits(b) for b in bc]
+
+
+@pytest.mark.parametrize("shape", RED_SHAPES)
+@pytest.mark.parametrize("n_reduce", [1, 7, 300])
+def test_ar_reduce_role_integer_bit_exact(handle, mk, shape, n_reduce):
+    W, rank, m, n, k = shape
+    print(f"ar reduce role n_reduce={n_reduce} {shape}", flush=True)
+    d = I.gen_ar(W, m, n, k, rank=rank, variant=I.INTEGER, config=390 + W)
+    handle.set_roles(mk.OP_GEMM_AR, n_reduce=n_reduce)
+    try:
+        c, bc = _run_ar_flags(handle, d, rank, 2, 0)
+        assert handle.last_launch(mk.OP_GEMM_AR)[0][2] == n_reduce
+    finally:
+        handle.set_roles(mk.OP_GEMM_AR)
+    O.assert_bits_equal(c, O.gemm_ar(d["a"], d["b"], d["peers"], rank=rank)["c"], "c")
+    for i, b in enumerate(bc):
+        O.assert_bits_equal(b, c, f"bcast[{i}] vs c")
+
+
+def test_rs_reduce_role_full_size(handle, mk):
+    """The full GEMM+ReduceScatter workload with 16 reduce workgroups: every
+    element of c_own and of the outboxes within the float rule."""
+    name = "gemm_rs_w8_8192x8192x3584"
+    print(f"{name} reduce role", flush=True)
+    d = I.gen_workload(name, I.FLOAT)
+    handle.set_roles(mk.OP_GEMM_RS, n_reduce=16)
+    try:
+        c_own, outbox = _run_rs_flags(handle, d, 0, 0)
+    finally:
+        handle.set_roles(mk.OP_GEMM_RS)
+    check_rs(d, 0, c_own, outbox, exact=False)
+
+
+@pytest.mark.parametrize("shape", [(8, 3, 2048, 520, 200), (3, 2, 1500, 776, 136)])
+def test_rs_ar_transfer_alone_moves_the_reduce_bytes(handle, mk, shape):
+    """n_compute = 0: the reduce workgroups alone write bf16 of the peers' sum
+    (the operation with A = 0) and zero outboxes; nothing is computed."""
+    W, rank, m, n, k = shape
+    print(f"rs/ar transfer alone {shape}", flush=True)
+    for nr in (-1, 3):
+        d = I.gen_rs(W, m, n, k, rank=rank, variant=I.INTEGER, config=395)
+        handle.set_roles(mk.OP_GEMM_RS, n_compute=0, n_reduce=nr)
+        try:
+            c_own, outbox = _run_rs_flags(handle, d, rank, 0)
+            (_, nc, got_nr), grid = handle.last_launch(mk.OP_GEMM_RS)
+            assert nc == 0 and got_nr == grid and (nr < 0 or got_nr == nr)
+        finally:
+            handle.set_roles(mk.OP_GEMM_RS)
+        ref = O.gemm_rs(np.zeros_like(d["a"]), d["b"], d["peers"], rank=rank)
+        O.assert_bits_equal(c_own, ref["c_own"], "c_own = bf16(sum of peers)")
+        for q in range(W):
+            if q != rank:
+                assert (outbox[q] == 0).all(), f"outbox[{q}] holds zeros"
+        d = I.gen_ar(W, m, n, k, rank=rank, variant=I.INTEGER, config=396)
+        handle.set_roles(mk.OP_GEMM_AR, n_compute=0, n_reduce=nr)
+        try:
+            c, bc = _run_ar_flags(handle, d, rank, 2, 0)
+        finally:
+            handle.set_roles(mk.OP_GEMM_AR)
+        O.assert_bits_equal(c, O.gemm_ar(np.zeros_like(d["a"]), d["b"], d["peers"], rank=rank)["c"],
+                            "c = bf16(sum of peers)")
+        for b in bc:
+            O.assert_bits_equal(b, c, "bcast vs c")
+
+
+@pytest.mark.parametrize("variant", [I.FLOAT, I.INTEGER])
+def test_rs_ar_compute_alone_leaves_out_the_peers(handle, mk, variant):
+    """MK_F_NO_PEERS: the operation with every peer partial zero; the peer
+    pointers are not read (None)."""
+    W, rank, m, n, k = 4, 1, 1024, 264, 136
+    d = I.gen_rs(W, m, n, k, rank=rank, variant=variant, config=397)
+    zero = [None if p is None else np.zeros_like(p) for p in d["peers"]]
+    ms = m // W
+    a, bt = dev_bf16(d["a"]), dev_bf16(I.transpose_bits(d["b"]))
+    c_own = empty_bf16((ms, n))
+    outbox = [None if q == rank else empty_bf16((ms, n)) for q in range(W)]
+    handle.gemm_rs(a, bt, [None] * W, c_own, outbox, rank=rank, flags=mk.F_NO_PEERS)
+    handle.sync()
+    d0 = dict(d, peers=zero)
+    check_rs(d0, rank, bits(c_own), [None if o is None else bits(o) for o in outbox],
+             exact=variant == I.INTEGER)
+    da = I.gen_ar(W, m, n, k, rank=rank, variant=variant, config=398)
+    c = empty_bf16((m, n))
+    handle.gemm_ar(dev_bf16(da["a"]), dev_bf16(I.transpose_bits(da["b"])), [None] * W, c, [],
+                   rank=rank, flags=mk.F_NO_PEERS)
+    handle.sync()
+    ref = O.gemm_ar(da["a"], da["b"], [None if p is None else np.zeros_like(p) for p in da["peers"]],
+                    rank=rank)["c"]
+    (O.assert_bits_equal if variant == I.INTEGER else O.assert_close_bf16)(bits(c), ref, "c")
+
+
+def test_reduce_role_argument_checks(mk):
+    """n_reduce only where a reduce role exists; a workspace too small for the
+    reduce role is refused before launching (no call allocates)."""
+    h = mk.Handle(0, spin_timeout_ms=10000, workspace_bytes=1 << 20)
+    try:
+        for op in (mk.OP_AG_GEMM, mk.OP_MOE, mk.OP_RING_ATTN):
+            with pytest.raises(mk.MkError) as e:
+                h.set_roles(op, n_reduce=2)
+            assert e.value.status == mk.MK_ERR_INVALID
+        d = I.gen_rs(8, 8192, 520, 64, rank=0, variant=I.INTEGER, config=399)  # own slice 1024 x 520 fp32 > 1 MiB
+        h.set_roles(mk.OP_GEMM_RS, n_reduce=4)
+        with pytest.raises(mk.MkError) as e:
+            _run_rs_flags(h, d, 0, 0)
+        assert e.value.status == mk.MK_ERR_INVALID and "workspace" in str(e.value)
+        h.set_roles(mk.OP_GEMM_RS, n_reduce=4, n_compute=0)
+        with pytest.raises(mk.MkError) as e:
+            _run_rs_flags(h, d, 0, mk.F_NO_PEERS)
+        assert e.value.status == mk.MK_ERR_INVALID
+        h.set_roles(mk.OP_GEMM_RS)
+        c_own, outbox = _run_rs_flags(h, d, 0, 0)      # without the reduce role: no workspace
+        check_rs(d, 0, c_own, outbox, exact=True)
+    finally:
+        h.close()
