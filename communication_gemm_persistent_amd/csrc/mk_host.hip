@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "mk_params.h"
@@ -46,6 +47,8 @@ struct mk_ctx {
   uint32_t *flags = nullptr;
   uint32_t *cnt = nullptr;
   uint32_t epoch = 0;
+  int max_flags = mk::kMaxFlags;  // flags (and arrival counters) the control memory holds
+  bool scratch = false;           // control memory is the library's per-device array (no handle)
   mk_roles roles[MK_OP_COUNT];
   mk_roles last[MK_OP_COUNT];
   int last_grid[MK_OP_COUNT] = {0, 0, 0, 0};
@@ -144,7 +147,10 @@ mk_status resolve(mk_ctx *h, const void *p, size_t bytes, bool allow_host, const
 }
 
 mk::Sync make_sync(mk_ctx *h, uint32_t n_flags) {
-  if (++h->epoch == 0) h->epoch = 1;
+  // the per-device array is cleared before every launch (which a captured
+  // graph replays too), so its launches all use epoch 1
+  if (h->scratch) h->epoch = 1;
+  else if (++h->epoch == 0) h->epoch = 1;
   mk::Sync s;
   s.ctrl = h->ctrl;
   s.flags = h->flags;
@@ -300,6 +306,116 @@ mk_status need_ws(mk_ctx *h, size_t bytes, const char *what) {
                                      " (mk_config.workspace_bytes)");
 }
 
+// ---------------------------------------------------------------- per-device control memory
+//
+// mk_ag_gemm_noalloc runs without a handle: its control block, ready flags
+// and arrival counters live in `scratch`, a fixed array that each GPU the
+// library runs on holds until the process ends.  In host code `scratch` is
+// a host-side stand-in; the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// ever passed to a kernel.  Every call clears the control block and its
+// flags first (with a kernel, so a captured graph replays the clear too) and
+// uses epoch 1; calls that overlap on one GPU share the array and race.
+
+constexpr int kScratchFlags = 2048;
+constexpr size_t kScratchCtrlBytes = (sizeof(mk::Ctrl) + 255) & ~(size_t)255;
+constexpr size_t kScratchFlagBytes = (size_t)kScratchFlags * mk::kFlagStride * sizeof(uint32_t);
+constexpr size_t kScratchBytes = kScratchCtrlBytes + 2 * kScratchFlagBytes;  // 260 KiB
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Zero the control block and the first n_flags flags and arrival counters.
+__global__ void scratch_clear_kernel(uint32_t *ctrl_words, uint32_t n_ctrl_words, uint32_t *flags,
+                                     uint32_t *cnt, uint32_t n_flags) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_ctrl_words) ctrl_words[i] = 0u;
+  if (i < n_flags) {
+    flags[(size_t)i * mk::kFlagStride] = 0u;
+    cnt[(size_t)i * mk::kFlagStride] = 0u;
+  }
+}
+
+// status[0] = the launch's error code (0 = MK_OK), status[1] = its detail.
+__global__ void scratch_report_kernel(const mk::Ctrl *ctrl, int32_t *status) {
+  if (threadIdx.x == 0) {
+    status[0] = (int32_t)(ctrl->err_code == mk::kErrInternal ? (uint32_t)MK_ERR_HIP : ctrl->err_code);
+    status[1] = (int32_t)ctrl->err_info;
+  }
+}
+
+hipError_t scratch_clear(mk_ctx *h, uint32_t n_flags, hipStream_t s) {
+  const uint32_t words = (uint32_t)(sizeof(mk::Ctrl) / sizeof(uint32_t));
+  const uint32_t n = std::max(words, n_flags);
+  hipLaunchKernelGGL(scratch_clear_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
+                     reinterpret_cast<uint32_t *>(h->ctrl), words, h->flags, h->cnt, n_flags);
+  return hipGetLastError();
+}
+
+hipError_t scratch_report(mk_ctx *h, int32_t *status, hipStream_t s) {
+  hipLaunchKernelGGL(scratch_report_kernel, dim3(1), dim3(64), 0, s, h->ctrl, status);
+  return hipGetLastError();
+}
+
+struct ScratchDevice {
+  std::once_flag once;
+  mk_ctx *ctx = nullptr;
+  mk_status st = MK_OK;
+};
+ScratchDevice g_scratch[kMaxDevices];
+
+// The per-device context of mk_ag_gemm_noalloc for the current device, set
+// up on the device's first call: gfx950 check, the array's device address,
+// the library's default schedule (no environment knobs).  Nothing is
+// allocated on the device.
+mk_status scratch_ctx(mk_ctx **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return MK_ERR_INVALID;
+  }
+  ScratchDevice &sd = g_scratch[dev];
+  std::call_once(sd.once, [&] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      sd.st = MK_ERR_HIP;
+      return;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      sd.st = MK_ERR_UNSUPPORTED;
+      return;
+    }
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      sd.st = MK_ERR_HIP;
+      return;
+    }
+    mk_ctx *h = new mk_ctx();
+    h->device = dev;
+    h->cu_count = prop.multiProcessorCount;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) khz = 100000;
+    h->timeout_ticks = (uint64_t)khz * (uint64_t)h->timeout_ms;
+    for (int i = 0; i < MK_OP_COUNT; ++i) h->roles[i] = mk_roles{-1, -1, -1};
+    char *base = static_cast<char *>(ptr);
+    h->ctrl = reinterpret_cast<mk::Ctrl *>(base);
+    h->flags = reinterpret_cast<uint32_t *>(base + kScratchCtrlBytes);
+    h->cnt = reinterpret_cast<uint32_t *>(base + kScratchCtrlBytes + kScratchFlagBytes);
+    h->max_flags = kScratchFlags;
+    h->scratch = true;
+    sd.ctx = h;
+  });
+  if (sd.st != MK_OK) return sd.st;
+  *out = sd.ctx;
+  return MK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -441,9 +557,13 @@ mk_status mk_sync(mk_handle h, mk_stream stream) {
 
 // ---------------------------------------------------------------- AllGather + GEMM
 
-mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
-                     const mk_bf16 *const *a_shards, const mk_bf16 *bt, mk_bf16 *c,
-                     mk_bf16 *a_gathered, int m_s, int n, int k, unsigned flags) {
+// mk_ag_gemm on a handle, or (h->scratch) on the per-device array of
+// mk_ag_gemm_noalloc, whose launch is bracketed by a clear of the array and
+// an optional status report.
+static mk_status ag_gemm_impl(mk_handle h, mk_stream stream, int world, int rank,
+                              const mk_bf16 *const *a_shards, const mk_bf16 *bt, mk_bf16 *c,
+                              mk_bf16 *a_gathered, int m_s, int n, int k, unsigned flags,
+                              int32_t *status) {
   mk_status st = check_common(h, world, rank);
   if (st != MK_OK) return st;
   if (flags & ~(MK_F_PRELANDED | MK_F_STATIC_ROLES)) return fail(h, MK_ERR_INVALID, "unknown flag bits");
@@ -499,7 +619,9 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   }
   p.slab_stages = p.n_slabs > 1 ? p.slab_k / 64 : 0;
   p.lb_rows = bm;
-  while ((long)world * cdiv(m_s, p.lb_rows) * p.n_slabs > mk::kMaxFlags) p.lb_rows *= 2;
+  while ((long)world * cdiv(m_s, p.lb_rows) * p.n_slabs > h->max_flags) p.lb_rows *= 2;
+  if ((long)world * cdiv(m_s, p.lb_rows) * p.n_slabs > h->max_flags)
+    return fail(h, MK_ERR_UNSUPPORTED, "more landing flags than the control memory holds");
   p.blocks_per_chunk = cdiv(m_s, p.lb_rows);
   p.item_rows = std::max(1, std::min(p.lb_rows, (h->item_kib * 1024) / (p.slab_k * 2)));
   p.items_per_block = cdiv(p.lb_rows, p.item_rows);
@@ -565,10 +687,36 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
   }
   const int grid = std::max(1, land + compute);
   p.sync = make_sync(h, (uint32_t)(world * p.blocks_per_chunk * p.n_slabs));
-  hipError_t e = mk::launch_ag(p, bm, bn, grid, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = hipSuccess;
+  if (h->scratch) e = scratch_clear(h, p.sync.n_flags, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(h, e, "launching the control-memory clear");
+  e = mk::launch_ag(p, bm, bn, grid, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(h, e, "launching the AllGather+GEMM kernel");
+  if (h->scratch && status) e = scratch_report(h, status, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(h, e, "launching the status report");
   record(h, MK_OP_AG_GEMM, land, compute, 0, grid);
   return MK_OK;
+}
+
+mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
+                     const mk_bf16 *const *a_shards, const mk_bf16 *bt, mk_bf16 *c,
+                     mk_bf16 *a_gathered, int m_s, int n, int k, unsigned flags) {
+  if (h && h->scratch) return MK_ERR_INVALID;
+  return ag_gemm_impl(h, stream, world, rank, a_shards, bt, c, a_gathered, m_s, n, k, flags, nullptr);
+}
+
+mk_status mk_ag_gemm_noalloc(mk_stream stream, int world, int rank, const mk_bf16 *const *a_shards,
+                             const mk_bf16 *bt, mk_bf16 *c, mk_bf16 *a_gathered, int m_s, int n, int k,
+                             unsigned flags, int32_t *status) {
+  mk_ctx *h = nullptr;
+  mk_status st = scratch_ctx(&h);
+  if (st != MK_OK) return st;
+  if (status) {
+    const void *dp;
+    if ((st = resolve(h, status, sizeof(int32_t) * 2, false, &dp, "status")) != MK_OK) return st;
+    status = static_cast<int32_t *>(const_cast<void *>(dp));
+  }
+  return ag_gemm_impl(h, stream, world, rank, a_shards, bt, c, a_gathered, m_s, n, k, flags, status);
 }
 
 // ---------------------------------------------------------------- GEMM + ReduceScatter

@@ -42,7 +42,7 @@ MAX_WORLD = 16
 EXPORTS = ("mk_create", "mk_destroy", "mk_set_roles", "mk_get_roles", "mk_last_launch",
            "mk_sync", "mk_status_string", "mk_last_error", "mk_ag_gemm", "mk_gemm_rs",
            "mk_gemm_ar", "mk_moe_dispatch_gemm", "mk_moe_dispatch_gemm_combine",
-           "mk_ring_attention", "mk_mfma_ceiling")
+           "mk_ring_attention", "mk_mfma_ceiling", "mk_ag_gemm_noalloc")
 
 
 class MkError(RuntimeError):
@@ -97,6 +97,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mk_mfma_ceiling.argtypes = [_vp, _vp, _i, _vp]
     lib.mk_ring_attention.argtypes = [_vp, _vp, _i, _i, _vp, _pp, _pp, _i, _i, _i, _i,
                                       ctypes.c_float, _vp, _vp, _vp, _vp, _u]
+    lib.mk_ag_gemm_noalloc.argtypes = [_vp, _i, _i, _pp, _vp, _vp, _vp, _i, _i, _i, _u, _vp]
     lib.mk_moe_dispatch_gemm_combine.argtypes = [
         _vp, _vp, _i, _i, _pp, _pp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
         _i, _vp, _pp, _vp, _u]
@@ -137,6 +138,30 @@ def _stream(stream, device: int) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def ag_gemm_noalloc(shards: Sequence[torch.Tensor], bt: torch.Tensor, c: torch.Tensor,
+                    a_gathered: torch.Tensor, rank: int = 0, flags: int = 0, stream=None,
+                    status: Optional[torch.Tensor] = None) -> None:
+    """mk_ag_gemm_noalloc: AllGather+GEMM on the current device with no handle
+    and no allocation (control memory in the library's per-device array).
+    status: optional int32 device tensor of >= 2 elements that receives the
+    launch's result code and detail.  Calls overlapping on one GPU race."""
+    lib = load()
+    W = len(shards)
+    m_s, k = shards[rank].shape
+    n = bt.shape[0]
+    sp = [0 if (s is None and q != rank and flags & F_PRELANDED)
+          else _ptr(s, f"shards[{q}]", _BF16, (m_s, k)) for q, s in enumerate(shards)]
+    if status is not None and (status.dtype != torch.int32 or status.numel() < 2):
+        raise ValueError("status must be an int32 tensor of at least 2 elements")
+    st = lib.mk_ag_gemm_noalloc(_vp(_stream(stream, torch.cuda.current_device())), W, rank,
+                                _ptr_array(sp), _ptr(bt, "bt", _BF16, (n, k)),
+                                _ptr(c, "c", _BF16, (W * m_s, n)),
+                                _ptr(a_gathered, "a_gathered", _BF16, (W * m_s, k)), m_s, n, k, flags,
+                                _ptr(status, "status", (torch.int32,)) if status is not None else None)
+    if st != MK_OK:
+        raise MkError(st, "mk_ag_gemm_noalloc: " + lib.mk_status_string(st).decode())
 
 
 class Handle:

@@ -185,6 +185,37 @@ mk_status mk_ag_gemm(mk_handle h, mk_stream stream, int world, int rank,
                      mk_bf16 *a_gathered, int m_s, int n, int k, unsigned flags);
 
 /*
+ * AllGather + GEMM that allocates nothing -- for callers that cannot call
+ * hipMalloc: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid device allocation.  Computes exactly what mk_ag_gemm computes
+ * (same arguments, same outputs, same kernels) with the library's default
+ * schedule, but needs no handle: the control block, ready flags and arrival
+ * counters live in one fixed array of the library on each device (260 KiB,
+ * held by every GPU the library runs on until the process ends; 2048 ready
+ * flags, the landing blocks are made coarser until they fit).  The caller
+ * passes inputs and outputs only.
+ *
+ *   Runs on the current device (hipSetDevice) and on `stream`: a small
+ *   kernel clears the array's control block and this call's flags, then the
+ *   fused kernel runs, then (status != NULL) a one-thread kernel writes
+ *   status[0] = the launch's result (MK_OK, or MK_ERR_TIMEOUT when an
+ *   in-kernel wait expired) and status[1] = its detail.  No call allocates
+ *   or frees memory or synchronises; the device's first call looks up the
+ *   array's address.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents: calls that overlap on one GPU (two streams, or two host
+ *   threads) race and give undefined results -- order them on one stream.
+ *   status   optional device memory, int32[2], 16-byte aligned
+ *   flags    MK_F_PRELANDED, MK_F_STATIC_ROLES
+ *   Errors as mk_ag_gemm (MK_ERR_INVALID / MK_ERR_UNSUPPORTED before
+ *   anything is launched; MK_ERR_UNSUPPORTED also for a device that is not
+ *   gfx950); there is no handle, so no error text.
+ */
+mk_status mk_ag_gemm_noalloc(mk_stream stream, int world, int rank, const mk_bf16 *const *a_shards,
+                             const mk_bf16 *bt, mk_bf16 *c, mk_bf16 *a_gathered, int m_s, int n, int k,
+                             unsigned flags, int32_t *status);
+
+/*
  * GEMM + ReduceScatter  [P1, row "GEMM + ReduceScatter"]:
  *   P = A @ B ([m, n] fp32); with slices of ms = m / W rows, this rank keeps
  *   c_own = bf16(P[slice rank] + sum over q != rank of peer_part[q]) and
