@@ -159,6 +159,22 @@ __device__ __forceinline__ void arrive(const Sync &s, uint32_t f, uint32_t targe
   }
 }
 
+// Arrival of one work item whose stores were written through to memory
+// (kStoreWriteThrough): every thread of the workgroup has waited for its
+// own stores (wait_stores) and passed a barrier, so the item's data is in
+// memory already and the count moves without the L2 write-back that
+// arrive() pays for (a write-back of the whole XCD's L2, whose cost grows
+// with every other workgroup's dirty lines).  The last arrival publishes the
+// flag as arrive() does.
+__device__ __forceinline__ void arrive_written_through(const Sync &s, uint32_t f, uint32_t target) {
+  const uint32_t old = add_relaxed(cnt_ptr(s, f), 1u);
+  if (old + 1 == target) {
+    fence_acquire();
+    st_relaxed(cnt_ptr(s, f), 0u);
+    st_release(flag_ptr(s, f), s.epoch);
+  }
+}
+
 // Wait for this thread's outstanding global stores (and loads).
 __device__ __forceinline__ void wait_stores() {
   __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0)
@@ -377,10 +393,11 @@ __device__ __forceinline__ void wg_copy16(void *__restrict__ dst, const void *__
 // loads of batch b + 1 issued before the stores of batch b, so a thread
 // always has loads in flight and never waits for its own stores.  Other
 // shapes take a plain loop.  The block spans less than 2 GiB.
-#ifndef MK_COPY_U
-#define MK_COPY_U 4
-#endif
-template <int U = MK_COPY_U>
+// U = 4 batches of 16-byte vectors per thread: deeper batches hold more
+// registers in the out-of-line copy, and an 8-deep build placed a spilled
+// descriptor's restore next to an LDS DMA of the fused kernels.  AUX: the
+// stores' cache-policy bits (kStoreWriteThrough for landing copies).
+template <int U = 4, int AUX = 0>
 __device__ __forceinline__ void wg_copy2d(void *__restrict__ dst, const void *__restrict__ src,
                                           int rows, int row_bytes, size_t pitch_bytes) {
   const int nt = blockDim.x, tid = threadIdx.x;
@@ -392,7 +409,7 @@ __device__ __forceinline__ void wg_copy2d(void *__restrict__ dst, const void *__
   if (!dense && nt % upr != 0) {
     for (int p = tid; p < n; p += nt) {
       const uint32_t o = (uint32_t)((size_t)(p / upr) * pitch_bytes + (size_t)(p % upr) * 16);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0), rd, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0), rd, o, 0, AUX);
     }
     return;
   }
@@ -408,7 +425,7 @@ __device__ __forceinline__ void wg_copy2d(void *__restrict__ dst, const void *__
   };
   auto store = [&](const u32x4_t (&v)[U], int b) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, o0, (b * U + u) * stride, 0);
+    for (int u = 0; u < U; ++u) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, o0, (b * U + u) * stride, AUX);
   };
   if (batches > 0) {
     load(v0, 0);
@@ -427,7 +444,7 @@ __device__ __forceinline__ void wg_copy2d(void *__restrict__ dst, const void *__
   // the rest: fewer than U + 1 vectors per thread
   for (int p = tid + batches * U * nt, j = batches * U; p < n; p += nt, ++j) {
     const uint32_t so = j * stride;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(rs, o0, so, 0), rd, o0, so, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(rs, o0, so, 0), rd, o0, so, AUX);
   }
 }
 
@@ -441,11 +458,18 @@ __device__ __forceinline__ const void *uniform_ptr(const void *p) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
   return reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo);
 }
+// Landing copies store with the system-coherence bits (sc0 sc1): the L2 of
+// the writer's XCD writes them through to memory, so once a thread's stores
+// are complete (vmcnt) they are visible to every XCD and the arrival needs
+// no write-back of the L2 (see arrive_written_through).
+constexpr int kStoreWriteThrough = 0x11;  // cache-policy bits sc0 | sc1
+
 __device__ __attribute__((noinline)) void wg_copy2d_call(void *dst, const void *src, int rows,
                                                          int row_bytes, size_t pitch_bytes) {
   const uint64_t pb = reinterpret_cast<uint64_t>(uniform_ptr(reinterpret_cast<const void *>(pitch_bytes)));
-  wg_copy2d(const_cast<void *>(uniform_ptr(dst)), uniform_ptr(src), __builtin_amdgcn_readfirstlane(rows),
-            __builtin_amdgcn_readfirstlane(row_bytes), (size_t)pb);
+  wg_copy2d<4, kStoreWriteThrough>(const_cast<void *>(uniform_ptr(dst)), uniform_ptr(src),
+                                   __builtin_amdgcn_readfirstlane(rows),
+                                   __builtin_amdgcn_readfirstlane(row_bytes), (size_t)pb);
 }
 
 // ---------------------------------------------------------------- GEMM tile engine
@@ -549,8 +573,10 @@ __device__ __forceinline__ void dma16(i32x4_t vdesc, uint32_t m0_base, uint32_t 
 }
 
 // One 4-byte-per-lane global->LDS DMA (lane l's word lands at m0_base + 4 l).
+// Issued once per K-slab, so it always carries the 5 wait states a
+// descriptor restored from a spill would need.
 __device__ __forceinline__ void dma4(i32x4_t vdesc, uint32_t m0_base, uint32_t voff) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(vdesc), "{m0}"(m0_base)
                : "memory");

@@ -40,6 +40,7 @@ struct mk_ctx {
   int ring_splits = 0;  // MK_RING_SPLITS=1: one task per (head, query tile) (0: library choice)
   int tile_map = -1;  // MK_TILE_MAP env: 0 global m-major order, 1 XCD blocks, 2 XCD strided, 3 XCD rounds (-1: per op)
   int item_kib = 512;  // MK_ITEM_KIB env: target size of one AllGather land item
+  int item_kib_first = 512;  // MK_ITEM_KIB_FIRST env: the same for the shards landed at the start
   int help_every = 0;  // MK_HELP_EVERY env: 1 in this many compute workgroups helps land (0: automatic)
   int help_eager = -1;  // MK_HELP_EAGER env: helpers land until the queue is empty (-1: automatic)
   int land_split = 1;  // MK_LAND_SPLIT env: land first-round chunks at the start, the rest between tiles
@@ -461,6 +462,7 @@ mk_status mk_create(mk_handle *out, const mk_config *cfg) {
   if (const char *t = std::getenv("MK_RING_SPLITS")) h->ring_splits = std::atoi(t) == 1 ? 1 : 0;
   if (const char *t = std::getenv("MK_TILE_MAP")) h->tile_map = std::min(3, std::max(0, std::atoi(t)));
   if (const char *t = std::getenv("MK_ITEM_KIB")) h->item_kib = std::min(4096, std::max(4, std::atoi(t)));
+  if (const char *t = std::getenv("MK_ITEM_KIB_FIRST")) h->item_kib_first = std::min(4096, std::max(4, std::atoi(t)));
   if (const char *t = std::getenv("MK_HELP_EVERY")) h->help_every = std::max(1, std::atoi(t));
   if (const char *t = std::getenv("MK_HELP_EAGER")) h->help_eager = std::atoi(t) != 0 ? 1 : 0;
   if (const char *t = std::getenv("MK_LAND_SPLIT")) h->land_split = std::atoi(t) != 0 ? 1 : 0;
@@ -673,10 +675,22 @@ static mk_status ag_gemm_impl(mk_handle h, mk_stream stream, int world, int rank
     // keeps the global order's rounds
     if (p.tile_map != mk::kMapGlobal && p.tile_map != mk::kMapRounds) p.first_peers = world - 1;
   }
+  // the first group's items: under the split schedule every workgroup lands
+  // them at once at the start, so they are cut small enough (item_kib_first)
+  // for all workgroups to take part; the later ones stay large
+  {
+    const int kib_first = split ? h->item_kib_first : h->item_kib;
+    p.item_rows_first = std::max(1, std::min(p.lb_rows, (kib_first * 1024) / (p.slab_k * 2)));
+    p.items_per_block_first = cdiv(p.lb_rows, p.item_rows_first);
+    const int items_per_chunk_first = p.blocks_per_chunk * p.n_slabs * p.items_per_block_first;
+    p.n_first_items = p.first_peers * items_per_chunk_first;
+    p.n_peer_items = p.n_first_items + (world - 1 - p.first_peers) * items_per_chunk;
+    p.n_items = p.n_peer_items + items_per_chunk;
+  }
   rounds_order(p.tiles_m, p.tiles_n, grid_all, bm, bn, &p.tile_group_m, &p.tile_split_m);
   if (split) {
     p.help_eager = 1;
-    p.eager_items = p.first_peers * items_per_chunk;
+    p.eager_items = p.n_first_items;
     p.land_between = (p.n_peer_items - p.eager_items + grid_all - 1) / grid_all;
     p.help_every = 1;
   } else {

@@ -29,42 +29,64 @@ __device__ __forceinline__ uint32_t ag_flag(const AgParams &p, int q, int j, int
   return (uint32_t)((q * p.blocks_per_chunk + j) * p.n_slabs + s);
 }
 
-// Land item `it` (numbering in AgParams).  Peers land in the order rank+1,
-// rank+2, ...; every thread copies its share, waits for its stores, and
-// thread 0 records the arrival after the barrier.
-__device__ __forceinline__ void ag_land_item(const AgParams &p, uint32_t it) {
-  const uint32_t per_block = (uint32_t)p.items_per_block;
-  const uint32_t per_chunk_slab = (uint32_t)p.blocks_per_chunk * per_block;
-  int q, s;
-  uint32_t rem;
+// Where land item `it` (numbering in AgParams) lives: shard q, land block j,
+// slab s; rows [r0, r1) of the shard, columns [c0, c1).
+struct AgItem {
+  int q, j, s, r0, r1, c0, c1;
+  int per_block;  // items per land block (and slab) of this item's shard: its flag's arrivals
+};
+
+__device__ __forceinline__ AgItem ag_item(const AgParams &p, uint32_t it) {
+  int q, s, item_rows;
+  uint32_t rem, per_block;
   if (it < (uint32_t)p.n_peer_items) {
-    // group of peers [pos0, pos0 + np) in landing order, slab-major
-    const uint32_t n_first = (uint32_t)p.first_peers * per_chunk_slab * p.n_slabs;
-    const bool first = it < n_first;
+    // two groups of peers in landing order, each slab-major: the first
+    // first_peers peers (items of item_rows_first rows), then the others
+    const bool first = it < (uint32_t)p.n_first_items;
+    per_block = (uint32_t)(first ? p.items_per_block_first : p.items_per_block);
+    item_rows = first ? p.item_rows_first : p.item_rows;
+    const uint32_t per_chunk_slab = (uint32_t)p.blocks_per_chunk * per_block;
     const int pos0 = first ? 0 : p.first_peers;
     const uint32_t np = (uint32_t)(first ? p.first_peers : p.world - 1 - p.first_peers);
-    const uint32_t ig = first ? it : it - n_first;
+    const uint32_t ig = first ? it : it - (uint32_t)p.n_first_items;
     const uint32_t per_slab = np * per_chunk_slab;
     s = (int)(ig / per_slab);
     rem = ig % per_slab;
     q = (p.rank + 1 + pos0 + (int)(rem / per_chunk_slab)) % p.world;
     rem %= per_chunk_slab;
   } else {
+    per_block = (uint32_t)p.items_per_block;
+    item_rows = p.item_rows;
+    const uint32_t per_chunk_slab = (uint32_t)p.blocks_per_chunk * per_block;
     const uint32_t il = it - (uint32_t)p.n_peer_items;
     s = (int)(il / per_chunk_slab);
     rem = il % per_chunk_slab;
     q = p.rank;
   }
-  const int j = (int)(rem / per_block), ii = (int)(rem % per_block);
-  const int r0 = j * p.lb_rows + ii * p.item_rows;
-  const int r1 = min(r0 + p.item_rows, min((j + 1) * p.lb_rows, p.m_s));
-  const int c0 = s * p.slab_k, c1 = min(c0 + p.slab_k, p.k);
-  if (r1 > r0)
-    wg_copy2d_call(p.ag + ((size_t)q * p.m_s + r0) * p.k + c0, p.shard[q] + (size_t)r0 * p.k + c0,
-                   r1 - r0, (c1 - c0) * 2, (size_t)p.k * 2);
+  AgItem r;
+  r.q = q;
+  r.s = s;
+  r.per_block = (int)per_block;
+  r.j = (int)(rem / per_block);
+  const int ii = (int)(rem % per_block);
+  r.r0 = r.j * p.lb_rows + ii * item_rows;
+  r.r1 = min(r.r0 + item_rows, min((r.j + 1) * p.lb_rows, p.m_s));
+  r.c0 = s * p.slab_k;
+  r.c1 = min(r.c0 + p.slab_k, p.k);
+  return r;
+}
+
+// Land item `it`.  Peers land in the order rank+1, rank+2, ...; every thread
+// copies its share, waits for its stores, and thread 0 records the arrival
+// after the barrier.
+__device__ __forceinline__ void ag_land_item(const AgParams &p, uint32_t it) {
+  const AgItem g = ag_item(p, it);
+  if (g.r1 > g.r0)
+    wg_copy2d_call(p.ag + ((size_t)g.q * p.m_s + g.r0) * p.k + g.c0, p.shard[g.q] + (size_t)g.r0 * p.k + g.c0,
+                   g.r1 - g.r0, (g.c1 - g.c0) * 2, (size_t)p.k * 2);
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) arrive(p.sync, ag_flag(p, q, j, s), per_block);
+  if (threadIdx.x == 0) arrive_written_through(p.sync, ag_flag(p, g.q, g.j, g.s), (uint32_t)g.per_block);
 }
 
 __device__ __forceinline__ void ag_land(const AgParams &p, uint32_t *s_word) {

@@ -10,12 +10,14 @@ namespace mk {
 
 // AllGather + GEMM.  Landing unit: a "land block" of lb_rows rows of one
 // shard and one K-slab of slab_k columns (one ready flag each), copied as
-// items_per_block items of item_rows rows.  Flag of block j of shard q,
-// slab s: (q * blocks_per_chunk + j) * n_slabs + s.  Items are numbered
-// peers first, in two groups: the first_peers peers (in landing order
-// rank+1, rank+2, ...) whose tiles run in the first round of tiles, then the
-// others; each group slab-major (every peer's slab 0, then slab 1, ...).
-// The local shard's items come last.
+// items_per_block items of item_rows rows (items_per_block_first items of
+// item_rows_first rows for the first group's shards, which every workgroup
+// lands at once at the start).  Flag of block j of shard q, slab s:
+// (q * blocks_per_chunk + j) * n_slabs + s.  Items are numbered peers first,
+// in two groups: the first_peers peers (in landing order rank+1, rank+2,
+// ...) whose tiles run in the first round of tiles (n_first_items items),
+// then the others; each group slab-major (every peer's slab 0, then slab 1,
+// ...).  The local shard's items come last.
 struct AgParams {
   Sync sync;
   const uint16_t *shard[MK_MAX_WORLD];
@@ -26,6 +28,7 @@ struct AgParams {
   int n_land, n_compute;
   int tiles_m, tiles_n, n_tiles, mb0, tile_map, tile_group_m, tile_split_m;
   int lb_rows, blocks_per_chunk, item_rows, items_per_block, n_items, n_peer_items;
+  int item_rows_first, items_per_block_first, n_first_items;
   int first_peers;
   int n_slabs, slab_k;
   int slab_stages;         // slab_k / 64 when tiles may start before their later slabs land, else 0

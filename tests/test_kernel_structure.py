@@ -92,3 +92,27 @@ def test_hazard_checker_sees_scalar_offsets(tmp_path):
     f.write_text("_Z1kv:\n\tv_readfirstlane_b32 s7, v3\n"
                  "\tbuffer_load_dwordx4 v32, s[8:11], s7 offen lds\n\ts_endpgm\n.Lfunc_end0:\n")
     assert check_hazards(str(f))
+
+
+def test_hazard_checker_follows_branches_and_m0(tmp_path):
+    """A descriptor written by v_readlane at the end of a block that branches
+    to the DMA's block (not its fall-through predecessor), and M0 written by
+    a VALU instruction right before the DMA, are both flagged; padded
+    versions are not."""
+    branch = ("_Z1kv:\n\tv_readlane_b32 s0, v250, 33\n\ts_branch .LBB0_2\n.LBB0_1:\n"
+              "\ts_add_i32 s6, s6, 1\n" * 1 + "{pad}.LBB0_2:\n"
+              "\tbuffer_load_dwordx4 v32, s[0:3], 0 offen lds\n\ts_endpgm\n.Lfunc_end0:\n")
+    f = tmp_path / "b.s"
+    f.write_text(branch.format(pad=""))
+    assert check_hazards(str(f)), "the branch source's v_readlane is 2 wait states away"
+    f.write_text(branch.replace("\ts_branch .LBB0_2\n", "\ts_nop 4\n\ts_branch .LBB0_2\n").format(pad=""))
+    assert not check_hazards(str(f))
+    m0 = "_Z1kv:\n\tv_readfirstlane_b32 m0, v3\n{pad}\tbuffer_load_dwordx4 v32, s[8:11], 0 offen lds\n\ts_endpgm\n.Lfunc_end0:\n"
+    f.write_text(m0.format(pad=""))
+    assert check_hazards(str(f))
+    f.write_text(m0.format(pad="\ts_nop 4\n"))
+    assert not check_hazards(str(f))
+    carry = ("_Z1kv:\n\tv_add_co_u32_e64 v1, s[8:9], v2, v3\n"
+             "\tbuffer_load_dwordx4 v32, s[8:11], 0 offen lds\n\ts_endpgm\n.Lfunc_end0:\n")
+    f.write_text(carry)
+    assert check_hazards(str(f)), "a carry-out written into the descriptor"
