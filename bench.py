@@ -91,7 +91,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--profile-run", choices=["fused", "gemm_alone", "transfer_alone", "copy"],
+    ap.add_argument("--profile-run", choices=["fused", "gemm_alone", "transfer_alone", "copy", "rs", "ar",
+                                              "moe", "moe_combine", "ring"],
                     help="only launch the named kernel a few times (for rocprofv3 counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -402,6 +403,8 @@ def profile_run(which, h, I, mk, to_dev, dev):
     that rocprofv3 wraps for counter passes.  "copy" is a plain device copy of
     COPY_BYTES that calibrates FETCH_SIZE / WRITE_SIZE."""
     import torch
+    if which in ("rs", "ar", "moe", "moe_combine", "ring"):
+        return profile_other(which, h, I, mk, to_dev, dev)
     if which == "copy":
         src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -431,6 +434,74 @@ def profile_run(which, h, I, mk, to_dev, dev):
     h.sync()
     print(json.dumps({"profile_run": which, "workload": WORKLOAD,
                       "roles": h.last_launch(mk.OP_AG_GEMM)}))
+    return 0
+
+
+def profile_other(which, h, I, mk, to_dev, dev):
+    """--profile-run for the other fused ops at their workload sizes: 7
+    launches of the default configuration."""
+    import torch
+
+    def f32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    if which in ("rs", "ar"):
+        name = "gemm_rs_w8_8192x8192x3584" if which == "rs" else "gemm_ar_w8_2048x8192x1024"
+        p = I.CONFIGS[name].params
+        d = I.gen_workload(name)
+        W, m, n = p["world"], p["m"], p["n"]
+        a, bt = to_dev(d["a"]), to_dev(I.transpose_bits(d["b"]))
+        peers = [None] + [f32(x) for x in d["peers"][1:]]
+        if which == "rs":
+            ms = m // W
+            c = torch.empty((ms, n), dtype=torch.bfloat16, device=dev)
+            ob = [None] + [torch.empty((ms, n), dtype=torch.bfloat16, device=dev) for _ in range(W - 1)]
+            call = lambda: h.gemm_rs(a, bt, peers, c, ob, rank=0)
+        else:
+            c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            bc = [torch.empty((m, n), dtype=torch.bfloat16, device=dev) for _ in range(p["n_bcast"])]
+            call = lambda: h.gemm_ar(a, bt, peers, c, bc, rank=0)
+    elif which in ("moe", "moe_combine"):
+        name = "moe_s8_t4096_h4096_n1536_e64"
+        p = I.CONFIGS[name].params
+        d = I.gen_workload(name)
+        S, T, H, N, E, E_loc, top_k = (p[x] for x in ("S", "T", "H", "N", "E", "E_loc", "top_k"))
+        cap = S * T * min(top_k, E_loc)
+        x = [to_dev(v) for v in d["x"]]
+        lg = [f32(v) for v in d["logits"]]
+        wt = to_dev(I.transpose_bits(d["w"]))
+        y = torch.empty((cap, N), dtype=torch.bfloat16, device=dev)
+        idx = torch.empty((S * T, top_k), dtype=torch.int32, device=dev)
+        gate = torch.empty((S * T, top_k), dtype=torch.float32, device=dev)
+        st = torch.empty((cap,), dtype=torch.int32, device=dev)
+        eo = torch.empty((E_loc + 1,), dtype=torch.int32, device=dev)
+        co = torch.empty((E_loc, S + 1), dtype=torch.int32, device=dev)
+        xs = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        if which == "moe":
+            call = lambda: h.moe_dispatch_gemm(x, lg, wt, E, top_k, y, idx, gate, st, eo, co, xs, rank=0)
+        else:
+            yp = to_dev(np.ascontiguousarray(d["y_peer"]).reshape(T * top_k, N))
+            ret = [None] + [torch.empty((T * top_k, N), dtype=torch.bfloat16, device=dev) for _ in range(S - 1)]
+            o = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+            call = lambda: h.moe_dispatch_gemm_combine(x, lg, wt, E, top_k, y, idx, gate, st, eo, co, xs,
+                                                       yp, ret, o, rank=0)
+    else:
+        name = "ring_attn_w8_h32_s4096_d128"
+        p = I.CONFIGS[name].params
+        d = I.gen_workload(name)
+        W, BH, S_q, S_kv, D = p["world"], p["B"] * p["H"], p["S_q"], p["S_kv"], p["D"]
+        q = to_dev(d["q"].reshape(BH, S_q, D))
+        ks = [to_dev(k.reshape(BH, S_kv, D)) for k in d["k"]]
+        vs = [to_dev(v.reshape(BH, S_kv, D)) for v in d["v"]]
+        o = torch.empty((BH, S_q, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((BH, S_q), dtype=torch.float32, device=dev)
+        kr = torch.empty((W, BH, S_kv, D), dtype=torch.bfloat16, device=dev)
+        vr = torch.empty((W, BH, D, S_kv), dtype=torch.bfloat16, device=dev)
+        call = lambda: h.ring_attention(q, ks, vs, o, lse, kr, vr, rank=p["rank"])
+    for _ in range(7):
+        call()
+    h.sync()
+    print(json.dumps({"profile_run": which, "workload": name}))
     return 0
 
 
