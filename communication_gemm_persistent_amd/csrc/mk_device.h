@@ -81,6 +81,13 @@ __device__ __forceinline__ uint32_t add_acq_rel(uint32_t *p, uint32_t v) {
 __device__ __forceinline__ uint32_t add_relaxed(uint32_t *p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A store that the writer's L2 writes through to memory (device scope, the
+// sc1 bit): once the thread's stores are complete it is visible to every
+// XCD, and publishing it needs no write-back of the L2.
+template <class T>
+__device__ __forceinline__ void st_through(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void fence_acquire() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }

@@ -23,6 +23,13 @@
 //                              (local experts from y, remote ones from what
 //                              their owners returned) into out
 // A route item is kRouteTokens consecutive tokens of one source rank.
+//
+// Everything one workgroup publishes to others (routing outputs, the scan,
+// slot metadata, landed rows) is stored write-through (device scope), so a
+// publish is: every thread waits for its stores, a barrier, then one
+// counter add or flag store -- no write-back of the XCD's L2, whose cost
+// grows with every other workgroup's dirty lines.  Readers acquire with an
+// L2 invalidate before they read.
 #include "mk_params.h"
 
 namespace mk {
@@ -35,6 +42,10 @@ struct MoeShared {
   int32_t tile_base[kMaxLocalExperts + 2];
   int32_t expert_off[kMaxLocalExperts + 1];
   int32_t expert_tot[kMaxLocalExperts];
+  float tile_gate[256];      // gate of each row of the current tile
+  int32_t tile_ret_src[256]; // source its row returns to (combine), -1: none
+  uint32_t tile_ret_row[256];
+  uint16_t *ret_ptr[MK_MAX_WORLD];
 };
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -117,8 +128,8 @@ __device__ __forceinline__ void moe_route_item(const MoeParams &p, int item, Moe
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j >= p.top_k) continue;
-      p.topk_idx[o + j] = sel[j];
-      p.topk_gate[o + j] = expf(selv[j] - mx) / sum;
+      st_through(&p.topk_idx[o + j], (int32_t)sel[j]);
+      st_through(&p.topk_gate[o + j], expf(selv[j] - mx) / sum);
     }
   }
   // per local expert: count and rank of this item's tokens (token order)
@@ -149,12 +160,12 @@ __device__ __forceinline__ void moe_route_item(const MoeParams &p, int item, Moe
     const size_t o = ((size_t)s * p.T + t) * p.top_k;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (j < p.top_k) p.tok_rank[o + j] = my_rank[j];
+      if (j < p.top_k) st_through(&p.tok_rank[o + j], (int32_t)my_rank[j]);
   }
   if (threadIdx.x < (unsigned)p.E_loc) {
     int tot = 0;
     for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += sh.wave_cnt[w][threadIdx.x];
-    p.item_cnt[(size_t)item * p.E_loc + threadIdx.x] = tot;
+    st_through(&p.item_cnt[(size_t)item * p.E_loc + threadIdx.x], (int32_t)tot);
   }
   __syncthreads();
 }
@@ -190,12 +201,12 @@ __device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
     int32_t running = 0;
     for (int e = 0; e < p.E_loc; ++e) {
       sh.expert_off[e] = running;
-      p.expert_offsets[e] = running;
+      st_through(&p.expert_offsets[e], running);
       running += sh.expert_tot[e];
     }
     sh.expert_off[p.E_loc] = running;
-    p.expert_offsets[p.E_loc] = running;
-    p.tile_base[1] = running;
+    st_through(&p.expert_offsets[p.E_loc], running);
+    st_through(&p.tile_base[1], running);
   }
   __syncthreads();
   for (int e = wave; e < p.E_loc; e += nw) {
@@ -206,12 +217,12 @@ __device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
       const int32_t incl = wave_inclusive_scan(v);
       const int32_t base = carry + incl - v;
       if (i < p.n_items) {
-        p.item_base[(size_t)i * p.E_loc + e] = base;
-        if (i % p.items_per_src == 0) p.chunk_offsets[e * (p.S + 1) + i / p.items_per_src] = base;
+        st_through(&p.item_base[(size_t)i * p.E_loc + e], base);
+        if (i % p.items_per_src == 0) st_through(&p.chunk_offsets[e * (p.S + 1) + i / p.items_per_src], base);
       }
       carry += __shfl(incl, 63, 64);
     }
-    if (lane == 0) p.chunk_offsets[e * (p.S + 1) + p.S] = carry;
+    if (lane == 0) st_through(&p.chunk_offsets[e * (p.S + 1) + p.S], carry);
   }
   __syncthreads();
   // grouped-GEMM row tiles in m-tile-major order across experts (tokens of
@@ -224,20 +235,23 @@ __device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
     for (int mt = 0; mt < max_mt; ++mt)
       for (int e = 0; e < p.E_loc; ++e)
         if (mt * BM < sh.expert_off[e + 1] - sh.expert_off[e])
-          p.tile_base[2 + ntile_rows++] = (e << 16) | mt;
-    p.tile_base[0] = ntile_rows;
+          st_through(&p.tile_base[2 + ntile_rows++], (int32_t)((e << 16) | mt));
+    st_through(&p.tile_base[0], (int32_t)ntile_rows);
   }
 }
 
 // ---------------------------------------------------------------- land
 
-__device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, MoeShared &sh) {
+// Land part `part` of route item `item`: the item's tokens t with
+// t % kLandParts == part that chose local experts.  Their slot metadata and
+// rows are stored write-through.
+__device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, int part, MoeShared &sh) {
   const int s = item / p.items_per_src, b = item % p.items_per_src;
   const int t = b * kRouteTokens + (int)threadIdx.x;
   const int e_lo = p.rank * p.E_loc;
   if (threadIdx.x == 0) sh.n_list = 0;
   __syncthreads();
-  if (threadIdx.x < (unsigned)kRouteTokens && t < p.T) {
+  if (threadIdx.x < (unsigned)kRouteTokens && t < p.T && (int)threadIdx.x % kLandParts == part) {
     const size_t o = ((size_t)s * p.T + t) * p.top_k;
     for (int j = 0; j < p.top_k; ++j) {
       const int e = p.topk_idx[o + j] - e_lo;
@@ -247,9 +261,9 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, MoeS
           raise_error(p.sync, kErrInternal, (uint32_t)item);
           continue;
         }
-        p.slot_token[slot] = s * p.T + t;
-        p.slot_gate[slot] = p.topk_gate[o + j];
-        if (p.combine) p.slot_ret[slot] = (int32_t)((size_t)(s * p.T + t) * p.top_k + j);
+        st_through(&p.slot_token[slot], (int32_t)(s * p.T + t));
+        st_through(&p.slot_gate[slot], p.topk_gate[o + j]);
+        if (p.combine) st_through(&p.slot_ret[slot], (int32_t)((size_t)(s * p.T + t) * p.top_k + j));
         const int k = atomicAdd(&sh.n_list, 1);
         sh.list_tok[k] = (slot << 8) | (int)threadIdx.x;
       }
@@ -258,42 +272,48 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, MoeS
   __syncthreads();
   const int n = (int)uniform((uint32_t)sh.n_list);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const size_t row_vec = (size_t)p.H / 8;   // 16-byte vectors per token row
+  const uint32_t row_bytes = (uint32_t)p.H * 2;
+  const int row_vec = p.H / 8;   // 16-byte vectors per token row
   const int nw = blockDim.x >> 6;
-  auto row = [&](int r, const u32x4_t *&src, u32x4_t *&dst) {
+  // buffer descriptors of a row's source and slot (the stores write through)
+  auto row = [&](int r, __amdgpu_buffer_rsrc_t &src, __amdgpu_buffer_rsrc_t &dst) {
     const int v = sh.list_tok[r];
     const int slot = v >> 8, tt = b * kRouteTokens + (v & 255);
-    src = reinterpret_cast<const u32x4_t *>(p.x[s] + (size_t)tt * p.H);
-    dst = reinterpret_cast<u32x4_t *>(p.x_slots + (size_t)slot * p.H);
+    src = make_rsrc(p.x[s] + (size_t)tt * p.H, row_bytes);
+    dst = make_rsrc(p.x_slots + (size_t)slot * p.H, row_bytes);
   };
   // two rows per wave at a time, 8 loads per lane and row in flight before
   // the stores (two whole 8 KiB rows per wave for H = 4096)
   for (int r = wave; r < n; r += 2 * nw) {
     const bool two = r + nw < n;
-    const u32x4_t *src0, *src1;
-    u32x4_t *dst0, *dst1;
+    __amdgpu_buffer_rsrc_t src0, src1, dst0, dst1;
     row(r, src0, dst0);
     if (two) row(r + nw, src1, dst1);
     else { src1 = src0; dst1 = dst0; }
-    size_t i = lane;
+    int i = lane;
     for (; i + 7 * 64 < row_vec; i += 8 * 64) {
       u32x4_t a0[8], a1[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a0[u] = src0[i + u * 64];
+      for (int u = 0; u < 8; ++u) a0[u] = __builtin_amdgcn_raw_buffer_load_b128(src0, (uint32_t)(i + u * 64) * 16u, 0, 0);
       if (two) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) a1[u] = src1[i + u * 64];
+        for (int u = 0; u < 8; ++u) a1[u] = __builtin_amdgcn_raw_buffer_load_b128(src1, (uint32_t)(i + u * 64) * 16u, 0, 0);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) dst0[i + u * 64] = a0[u];
+      for (int u = 0; u < 8; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(a0[u], dst0, (uint32_t)(i + u * 64) * 16u, 0, kStoreWriteThrough);
       if (two) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) dst1[i + u * 64] = a1[u];
+        for (int u = 0; u < 8; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(a1[u], dst1, (uint32_t)(i + u * 64) * 16u, 0, kStoreWriteThrough);
       }
     }
     for (; i < row_vec; i += 64) {
-      dst0[i] = src0[i];
-      if (two) dst1[i] = src1[i];
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(src0, (uint32_t)i * 16u, 0, 0),
+                                             dst0, (uint32_t)i * 16u, 0, kStoreWriteThrough);
+      if (two)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(src1, (uint32_t)i * 16u, 0, 0),
+                                               dst1, (uint32_t)i * 16u, 0, kStoreWriteThrough);
     }
   }
 }
@@ -331,13 +351,16 @@ __device__ __forceinline__ bool moe_rows_ready(const MoeParams &p, int e, int sl
   return true;
 }
 
-// Land route item it and release its flag (every thread waits for its own
-// stores; after the barrier one release store publishes the item).
-__device__ __forceinline__ void moe_land_and_release(const MoeParams &p, uint32_t it, MoeShared &sh) {
-  moe_land_item(p, (int)it, sh);
+// Land unit w of the land queue (route item w / kLandParts, part
+// w % kLandParts) and record its arrival: every thread waits for its own
+// (write-through) stores, then after the barrier one counter add; the last
+// part of the item publishes its flag.
+__device__ __forceinline__ void moe_land_and_release(const MoeParams &p, uint32_t w, MoeShared &sh) {
+  const uint32_t it = w / kLandParts;
+  moe_land_item(p, (int)it, (int)(w % kLandParts), sh);
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) st_release(flag_ptr(p.sync, it), p.sync.epoch);
+  if (threadIdx.x == 0) arrive_written_through(p.sync, it, (uint32_t)kLandParts);
 }
 
 template <int BM, int BN>
@@ -345,6 +368,7 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
   using C = TileCfg<BM, BN>;
   if (threadIdx.x <= (unsigned)p.E_loc) sh.expert_off[threadIdx.x] = p.expert_offsets[threadIdx.x];
   if (threadIdx.x == 0) sh.tile_base[0] = p.tile_base[0];
+  if (threadIdx.x < (unsigned)MK_MAX_WORLD) sh.ret_ptr[threadIdx.x] = p.ret[threadIdx.x];
   __syncthreads();
   const int n_row_tiles = (int)uniform((uint32_t)sh.tile_base[0]);
   const int n_tiles = n_row_tiles * p.tiles_n;
@@ -371,7 +395,7 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
       if (threadIdx.x == 0) ready = moe_rows_ready(p, e, slot0, slot1);
       if (wg_broadcast(ready, &sh.word)) break;
       const uint32_t it = next_index(&p.sync.ctrl->land_ctr, &sh.word);
-      if (it >= (uint32_t)p.n_items) break;
+      if (it >= (uint32_t)(p.n_items * kLandParts)) break;
       moe_land_and_release(p, it, sh);
     }
     bool ok0 = true;
@@ -380,36 +404,41 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
     const int valid_n = min(BN, p.N - n0);
     const i32x4_t ra = make_vdesc(p.x_slots + (size_t)slot0 * p.H, (uint32_t)((slot1 - slot0) * ld));
     const i32x4_t rb = make_vdesc(p.wt + ((size_t)e * p.N + n0) * p.H, (uint32_t)(valid_n * ld));
+    // the tile's row gates and return positions, for the epilogue
+    if (threadIdx.x < (unsigned)BM) {
+      const int slot = slot0 + (int)threadIdx.x;
+      float g = 1.f;
+      int src = -1;
+      uint32_t rrow = 0;
+      if (slot < slot1) {
+        if (!p.no_gate) g = p.slot_gate[slot];
+        if (p.combine) {
+          const size_t rp = (size_t)p.slot_ret[slot];
+          const size_t per_src = (size_t)p.T * p.top_k;
+          src = (int)(rp / per_src);
+          rrow = (uint32_t)(rp - (size_t)src * per_src);
+          if (src == p.rank) src = -1;  // this rank's own tokens stay in y
+        }
+      }
+      sh.tile_gate[threadIdx.x] = g;
+      sh.tile_ret_src[threadIdx.x] = src;
+      sh.tile_ret_row[threadIdx.x] = rrow;
+    }
     AccTile<BM, BN> acc;
     gemm_tile<BM, BN>(smem, ra, ld, rb, ld, p.H, acc);
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-      const AccPos<BM, BN> p0 = acc_pos<BM, BN>(i, 0, 0);
-      const int slot = slot0 + p0.row;
-      if (slot >= slot1) continue;
-      const float gt = p.no_gate ? 1.f : p.slot_gate[slot];
-      // the row's return position in its source's combine buffer (none for this rank's tokens)
-      uint16_t *ret_row = nullptr;
-      if (p.combine) {
-        const size_t rp = (size_t)p.slot_ret[slot];
-        const size_t per_src = (size_t)p.T * p.top_k;
-        const int src = (int)(rp / per_src);
-        if (src != p.rank) ret_row = p.ret[src] + (rp - (size_t)src * per_src) * p.N;
-      }
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int g = 0; g < C::GROUPS; ++g) {
-          const int col = n0 + acc_pos<BM, BN>(i, j, g).col;
-          if (col >= p.N) continue;
-          const f32x4_t v = acc_group(acc[i][j], g);
-          float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
-          if (!p.no_gate) { x0 *= gt; x1 *= gt; x2 *= gt; x3 *= gt; }
-          const uint2 o = pack_bf16x4(x0, x1, x2, x3);
-          *reinterpret_cast<uint2 *>(p.y + (size_t)slot * p.N + col) = o;
-          if (ret_row) *reinterpret_cast<uint2 *>(ret_row + col) = o;
-        }
-    }
+    // y = bf16(gate * acc) row by row through LDS (whole-row stores); a row
+    // of a remote token is also stored to its source's return buffer
+    const int rows = slot1 - slot0;
+    staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
+      const int col = n0 + cc;
+      if (r >= rows || col >= p.N) return;
+      const float g = sh.tile_gate[r];
+      const uint2 o = p.no_gate ? pack_bf16x4(v[0], v[1], v[2], v[3])
+                                : pack_bf16x4(v[0] * g, v[1] * g, v[2] * g, v[3] * g);
+      *reinterpret_cast<uint2 *>(p.y + (size_t)(slot0 + r) * p.N + col) = o;
+      const int src = sh.tile_ret_src[r];
+      if (src >= 0) *reinterpret_cast<uint2 *>(sh.ret_ptr[src] + (size_t)sh.tile_ret_row[r] * p.N + col) = o;
+    });
     if (p.combine) {  // count the finished tile for the combine (release of its rows)
       wait_stores();
       __syncthreads();
@@ -514,10 +543,7 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeP
     moe_route_item(p, (int)it, sh);
     wait_stores();
     __syncthreads();
-    if (threadIdx.x == 0) {
-      fence_release();
-      add_relaxed(&ctrl->route_done, 1u);
-    }
+    if (threadIdx.x == 0) add_relaxed(&ctrl->route_done, 1u);  // the outputs were written through
   }
 
   bool ok = true;
@@ -529,7 +555,7 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeP
       moe_scan<BM>(p, sh);
       wait_stores();
       __syncthreads();
-      if (threadIdx.x == 0) st_release(&ctrl->scan_ready, p.sync.epoch);
+      if (threadIdx.x == 0) st_through(&ctrl->scan_ready, p.sync.epoch);
     }
   }
   if (ok && ticket < (uint32_t)(p.n_land + p.n_compute)) {
@@ -541,7 +567,7 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeP
     if (ticket < (uint32_t)p.n_land) {
       for (;;) {
         const uint32_t it = next_index(&ctrl->land_ctr, &sh.word);
-        if (it >= (uint32_t)p.n_items) break;
+        if (it >= (uint32_t)(p.n_items * kLandParts)) break;
         moe_land_and_release(p, it, sh);
       }
     } else if (ticket < (uint32_t)(p.n_land + p.n_compute)) {

@@ -117,7 +117,11 @@ struct AttnParams {
 
 // MoE dispatch + grouped GEMM.  Route items are blocks of kRouteTokens
 // tokens of one source; an item's flag says all of its local tokens landed.
+// An item lands as kLandParts parts (the item's tokens t with t % kLandParts
+// == part), each a unit of the land queue; the item's flag completes after
+// kLandParts arrivals.
 constexpr int kRouteTokens = 256;
+constexpr int kLandParts = 2;
 constexpr int kMaxLocalExperts = 32;
 
 struct MoeParams {
