@@ -887,13 +887,16 @@ __device__ __forceinline__ void gemm_tile_pingpong(
   // which A rows of stage u are first fetched (group 0, COMPUTE(u-2)); if
   // the flag is not yet set there it waits for it.  Slabs span at least
   // four stages, so the slot is never refilled before it is read.
-  const int S = gate.stages;  // 0: no gate
+  // (gate values are uniform; readfirstlane keeps them scalar even when the
+  // caller read them from memory into vector registers)
+  const int S = __builtin_amdgcn_readfirstlane(gate.stages);  // 0: no gate
+  const uint32_t flag0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)gate.flag0);
   const bool gated = S > 0 && wave == 0;
   i32x4_t fdesc{};
   uint32_t epoch = 0;
   if (gated) {
     fdesc = make_vdesc(gate.sync->flags, gate.sync->n_flags * kFlagStride * 4u);
-    epoch = gate.sync->epoch;
+    epoch = (uint32_t)__builtin_amdgcn_readfirstlane((int)gate.sync->epoch);
   }
   // prologue, in the order the loop's waits expect: own 0, other 0, own 1
 #pragma unroll
@@ -906,6 +909,8 @@ __device__ __forceinline__ void gemm_tile_pingpong(
   phase_barrier();
   if (!g0) phase_barrier();           // group 1 starts one phase late
   Frags<BM, BN> f[C::SUBSTEPS];
+  int chk_t = S - 2, pf_t = S - 3;  // first stages t with (t + 2) % S == 0, (t + 3) % S == 0
+  uint32_t chk_slab = 1, pf_slab = 1;
   for (int t = 0; t < nk; ++t) {
     // MEMORY(t): fragments of stage t, then the other operand of stage t+1
     const char *st = smem + (t & 1) * C::STAGE_BYTES;
@@ -914,19 +919,28 @@ __device__ __forceinline__ void gemm_tile_pingpong(
 #pragma unroll
     for (int d = 0; d < R; ++d) fetch(false, t + 1, d);
     if (gated) {
-      if ((t + 2) % S == 0 && t + 2 < nk) {
-        const uint32_t seen = uniform(*reinterpret_cast<volatile uint32_t *>(smem + C::FLAG_SLOT));
-        if (seen != epoch && lane == 0) {
-          const uint32_t slab = (uint32_t)((t + 2) / S);
-          // on timeout or abort the error is recorded; the tile completes with
-          // undefined values and the caller stops at its next wait
-          (void)spin_until_eq(*gate.sync, flag_ptr(*gate.sync, gate.flag0 + slab), epoch,
-                              0x51000000u | (gate.flag0 + slab));
+      // stage t + 2 starts slab chk_slab when t == chk_t; stage t + 3 starts
+      // slab pf_slab when t == pf_t (counters, not a division per stage)
+      if (t == chk_t) {
+        chk_t += S;
+        if (t + 2 < nk) {
+          const uint32_t seen = uniform(*reinterpret_cast<volatile uint32_t *>(smem + C::FLAG_SLOT));
+          if (seen != epoch && lane == 0) {
+            // on timeout or abort the error is recorded; the tile completes
+            // with undefined values and the caller stops at its next wait
+            (void)spin_until_eq(*gate.sync, flag_ptr(*gate.sync, flag0 + chk_slab), epoch,
+                                0x51000000u | (flag0 + chk_slab));
+          }
         }
+        ++chk_slab;
       }
-      if ((t + 3) % S == 0 && t + 3 < nk)
-        dma4(fdesc, __builtin_amdgcn_readfirstlane(lds_addr(smem + C::FLAG_SLOT)),
-             (gate.flag0 + (uint32_t)((t + 3) / S)) * kFlagStride * 4u);
+      if (t == pf_t) {
+        pf_t += S;
+        if (t + 3 < nk)
+          dma4(fdesc, __builtin_amdgcn_readfirstlane(lds_addr(smem + C::FLAG_SLOT)),
+               (flag0 + pf_slab) * kFlagStride * 4u);
+        ++pf_slab;
+      }
     }
     if (g0)
       __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)

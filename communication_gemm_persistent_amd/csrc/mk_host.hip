@@ -982,6 +982,7 @@ static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
   const long exp_rows = (long)n_src * T * top_k * E_loc / E;
   const int bm = pick_tile(h, (long)(cdiv((int)std::max(1L, exp_rows), 256) + E_loc) * cdiv(N, 256));
   p.tiles_n = cdiv(N, bm);
+  p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapBlocks;
   const long max_row_tiles = cdiv(cap, bm) + E_loc;
 
   // workspace: item_cnt, item_base, tok_rank, slot_gate, slot_ret, tile list

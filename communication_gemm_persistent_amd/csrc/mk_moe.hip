@@ -12,8 +12,10 @@
 //                              (expert, source, token) order -> slot offsets,
 //                              then the grouped-GEMM tile list; publishes
 //                              scan_ready
-//   land   (land workgroups)   copies each routed token row straight into its
+//   land   (every workgroup)   copies each routed token row straight into its
 //                              expert slot and releases that route item's flag
+//                              (a workgroup copies at a few tens of GB/s, so
+//                              landing needs the whole grid)
 //   compute (compute workgroups) grouped-GEMM tiles over the expert slots; a
 //                              tile waits for the flags of the route items whose
 //                              tokens fill its rows; y = bf16(gate * acc)
@@ -35,9 +37,14 @@
 namespace mk {
 
 struct MoeShared {
+  // a copy of the parameters that the tile loop reads: LDS reads are
+  // reloaded where they are used (the K loop's asm may write memory), so no
+  // parameter stays live in scalar registers across the K loop, where
+  // spilled registers would be restored right before its DMAs
+  MoeParams prm;
   uint32_t word;
   int32_t wave_cnt[kMaxWaves][kMaxLocalExperts];
-  int32_t list_tok[kRouteTokens * 8];   // (slot << 8 | token-in-item) of the item's local rows
+  int32_t list_tok[kRouteTokens * 8];  // (slot << 8 | token in item) of the unit's rows
   int32_t n_list;
   int32_t tile_base[kMaxLocalExperts + 2];
   int32_t expert_off[kMaxLocalExperts + 1];
@@ -225,26 +232,102 @@ __device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
     if (lane == 0) st_through(&p.chunk_offsets[e * (p.S + 1) + p.S], carry);
   }
   __syncthreads();
-  // grouped-GEMM row tiles in m-tile-major order across experts (tokens of
-  // the first sources land first and fill every expert's first rows); the
-  // offsets are read from LDS (one thread, many dependent reads)
+  // grouped-GEMM row tiles, expert by expert (the XCD tile map hands each
+  // XCD a contiguous block of them, so the tiles one XCD runs share their
+  // expert's weights and their m-blocks' rows in its L2); the offsets are
+  // read from LDS (one thread, many dependent reads)
   if (threadIdx.x == 0) {
-    int ntile_rows = 0, max_mt = 0;
+    int ntile_rows = 0;
     for (int e = 0; e < p.E_loc; ++e)
-      max_mt = max(max_mt, (sh.expert_off[e + 1] - sh.expert_off[e] + BM - 1) / BM);
-    for (int mt = 0; mt < max_mt; ++mt)
-      for (int e = 0; e < p.E_loc; ++e)
-        if (mt * BM < sh.expert_off[e + 1] - sh.expert_off[e])
-          st_through(&p.tile_base[2 + ntile_rows++], (int32_t)((e << 16) | mt));
+      for (int mt = 0; mt * BM < sh.expert_off[e + 1] - sh.expert_off[e]; ++mt)
+        st_through(&p.tile_base[2 + ntile_rows++], (int32_t)((e << 16) | mt));
     st_through(&p.tile_base[0], (int32_t)ntile_rows);
   }
 }
 
 // ---------------------------------------------------------------- land
 
-// Land part `part` of route item `item`: the item's tokens t with
-// t % kLandParts == part that chose local experts.  Their slot metadata and
-// rows are stored write-through.
+// Copy every listed row (n rows in sh.list_tok, of route item `item`) from
+// its token's row of x to its slot's row of x_slots.  The stores are
+// device-scope 8-byte stores, which write through the L2.
+//
+// A step is 8 rows x 128 8-byte units per row of one wave (two units per
+// lane and row); a wave's steps run in a two-deep pipeline: the loads of
+// step i + 1 are issued before the stores of step i, so a wait for them
+// leaves the stores in flight (a wait for a load also waits for every store
+// issued before it).  Row addresses stay in vector registers.  Steps have no
+// branches, so the compiler's waits count exactly: the rows past the last
+// of a partial group repeat the last row and units past a row's end repeat
+// its last unit (the same bytes stored twice to the same place).
+__device__ __forceinline__ void moe_copy_rows(const MoeParams &p, const MoeShared &sh, int n, int item) {
+  constexpr int RB = 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int sr = item / p.items_per_src;
+  const uint64_t *xs = reinterpret_cast<const uint64_t *>(p.x[sr]);
+  uint64_t *xd = reinterpret_cast<uint64_t *>(p.x_slots);
+  const int t0 = (item - sr * p.items_per_src) * kRouteTokens;
+  const int nu = p.H / 4;                     // 8-byte units per row
+  const int chunks = (nu + 127) / 128;        // steps per row group
+  const int groups = (n + RB - 1) / RB;
+  const int steps = groups * chunks;
+  const size_t rw = (size_t)p.H / 4;          // units per row
+  struct Step {
+    const uint64_t *src[RB];
+    uint64_t *dst[RB];
+    uint64_t a[RB][2];
+    int u0, u1;
+  };
+  auto issue = [&](int st, Step &q) {
+    const int g = st / chunks, c = st - g * chunks;
+    const int r0 = g * RB;
+    q.u0 = min(c * 128 + lane, nu - 1);
+    q.u1 = min(c * 128 + 64 + lane, nu - 1);
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const int r = min(r0 + j, n - 1);
+      const int v = sh.list_tok[r];
+      q.src[j] = xs + (size_t)(t0 + (v & 255)) * rw;
+      q.dst[j] = xd + (size_t)(v >> 8) * rw;
+    }
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      q.a[j][0] = q.src[j][q.u0];
+      q.a[j][1] = q.src[j][q.u1];
+    }
+  };
+  auto drain = [&](const Step &q) {
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      st_through(q.dst[j] + q.u0, q.a[j][0]);
+      st_through(q.dst[j] + q.u1, q.a[j][1]);
+    }
+  };
+  // this wave's steps are wave + k * nw, k < my; the loop body has no
+  // branches (the compiler's waits then leave one step's loads and the
+  // previous step's stores in flight), the last one or two steps follow it
+  const int my = wave < steps ? (steps - wave + nw - 1) / nw : 0;
+  if (my == 0) return;
+  Step qa, qb;
+  issue(wave, qa);
+  int k = 0;
+  for (; k + 2 < my; k += 2) {
+    issue(wave + (k + 1) * nw, qb);
+    drain(qa);
+    issue(wave + (k + 2) * nw, qa);
+    drain(qb);
+  }
+  if (k + 1 < my) {
+    issue(wave + (k + 1) * nw, qb);
+    drain(qa);
+    drain(qb);
+  } else {
+    drain(qa);
+  }
+}
+
+// Land part `part` of route item `item`: the rows of the item's tokens t
+// with t % kLandParts == part that chose local experts and their slot
+// metadata, all stored write-through.
 __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, int part, MoeShared &sh) {
   const int s = item / p.items_per_src, b = item % p.items_per_src;
   const int t = b * kRouteTokens + (int)threadIdx.x;
@@ -271,51 +354,7 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, int 
   }
   __syncthreads();
   const int n = (int)uniform((uint32_t)sh.n_list);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t row_bytes = (uint32_t)p.H * 2;
-  const int row_vec = p.H / 8;   // 16-byte vectors per token row
-  const int nw = blockDim.x >> 6;
-  // buffer descriptors of a row's source and slot (the stores write through)
-  auto row = [&](int r, __amdgpu_buffer_rsrc_t &src, __amdgpu_buffer_rsrc_t &dst) {
-    const int v = sh.list_tok[r];
-    const int slot = v >> 8, tt = b * kRouteTokens + (v & 255);
-    src = make_rsrc(p.x[s] + (size_t)tt * p.H, row_bytes);
-    dst = make_rsrc(p.x_slots + (size_t)slot * p.H, row_bytes);
-  };
-  // two rows per wave at a time, 8 loads per lane and row in flight before
-  // the stores (two whole 8 KiB rows per wave for H = 4096)
-  for (int r = wave; r < n; r += 2 * nw) {
-    const bool two = r + nw < n;
-    __amdgpu_buffer_rsrc_t src0, src1, dst0, dst1;
-    row(r, src0, dst0);
-    if (two) row(r + nw, src1, dst1);
-    else { src1 = src0; dst1 = dst0; }
-    int i = lane;
-    for (; i + 7 * 64 < row_vec; i += 8 * 64) {
-      u32x4_t a0[8], a1[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) a0[u] = __builtin_amdgcn_raw_buffer_load_b128(src0, (uint32_t)(i + u * 64) * 16u, 0, 0);
-      if (two) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) a1[u] = __builtin_amdgcn_raw_buffer_load_b128(src1, (uint32_t)(i + u * 64) * 16u, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        __builtin_amdgcn_raw_buffer_store_b128(a0[u], dst0, (uint32_t)(i + u * 64) * 16u, 0, kStoreWriteThrough);
-      if (two) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          __builtin_amdgcn_raw_buffer_store_b128(a1[u], dst1, (uint32_t)(i + u * 64) * 16u, 0, kStoreWriteThrough);
-      }
-    }
-    for (; i < row_vec; i += 64) {
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(src0, (uint32_t)i * 16u, 0, 0),
-                                             dst0, (uint32_t)i * 16u, 0, kStoreWriteThrough);
-      if (two)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(src1, (uint32_t)i * 16u, 0, 0),
-                                               dst1, (uint32_t)i * 16u, 0, kStoreWriteThrough);
-    }
-  }
+  moe_copy_rows(p, sh, n, item);
 }
 
 // ---------------------------------------------------------------- compute
@@ -342,15 +381,6 @@ __device__ __forceinline__ bool moe_wait_rows(const MoeParams &p, int e, int slo
   return true;
 }
 
-// Thread 0: have those route items landed?  (moe_wait_rows without waiting)
-__device__ __forceinline__ bool moe_rows_ready(const MoeParams &p, int e, int slot0, int slot1) {
-  for (int i = moe_first_item(p, e, slot0); i < p.n_items; ++i) {
-    if (p.item_base[(size_t)i * p.E_loc + e] >= slot1) break;
-    if (ld_relaxed(flag_ptr(p.sync, (uint32_t)i)) != p.sync.epoch) return false;
-  }
-  return true;
-}
-
 // Land unit w of the land queue (route item w / kLandParts, part
 // w % kLandParts) and record its arrival: every thread waits for its own
 // (write-through) stores, then after the barrier one counter add; the last
@@ -363,6 +393,15 @@ __device__ __forceinline__ void moe_land_and_release(const MoeParams &p, uint32_
   if (threadIdx.x == 0) arrive_written_through(p.sync, it, (uint32_t)kLandParts);
 }
 
+// Land units of the land queue until none is left.
+__device__ __forceinline__ void moe_land_queue(const MoeParams &p, MoeShared &sh) {
+  for (;;) {
+    const uint32_t it = next_index(&p.sync.ctrl->land_ctr, &sh.word);
+    if (it >= (uint32_t)(p.n_items * kLandParts)) break;
+    moe_land_and_release(p, it, sh);
+  }
+}
+
 template <int BM, int BN>
 __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeShared &sh) {
   using C = TileCfg<BM, BN>;
@@ -371,11 +410,11 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
   if (threadIdx.x < (unsigned)MK_MAX_WORLD) sh.ret_ptr[threadIdx.x] = p.ret[threadIdx.x];
   __syncthreads();
   const int n_row_tiles = (int)uniform((uint32_t)sh.tile_base[0]);
-  const int n_tiles = n_row_tiles * p.tiles_n;
   const int ld = p.H * 2;
+  const int xcd = xcd_id();
   for (;;) {
-    const uint32_t t = next_index(&p.sync.ctrl->tile_ctr, &sh.word);
-    if (t >= (uint32_t)n_tiles) break;
+    const int t = next_tile(p.sync, n_row_tiles, p.tiles_n, xcd, TileOrder{p.tile_map, 1, 1}, &sh.word);
+    if (t < 0) break;
     const int rt = (int)t / p.tiles_n, nb = (int)t % p.tiles_n;
     const int code = (int)uniform((uint32_t)p.tile_base[2 + rt]);
     const int e = code >> 16, mt = code & 0xFFFF;
@@ -386,18 +425,6 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
       break;
     }
     const int n0 = nb * BN;
-    // while the tile's rows are missing, land queued route items (landing
-    // then runs on every workgroup, not only on the land role's)
-    for (;;) {
-      // the barrier closes the previous item's single-thread release
-      __syncthreads();
-      bool ready = false;
-      if (threadIdx.x == 0) ready = moe_rows_ready(p, e, slot0, slot1);
-      if (wg_broadcast(ready, &sh.word)) break;
-      const uint32_t it = next_index(&p.sync.ctrl->land_ctr, &sh.word);
-      if (it >= (uint32_t)(p.n_items * kLandParts)) break;
-      moe_land_and_release(p, it, sh);
-    }
     bool ok0 = true;
     if (threadIdx.x == 0) ok0 = moe_wait_rows(p, e, slot0, slot1);
     if (!wg_sync_ok(ok0, &sh.word)) break;
@@ -535,6 +562,9 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeP
   __shared__ MoeShared sh;
   const uint32_t ticket = take_ticket(p.sync, &sh.word);
   Ctrl *ctrl = p.sync.ctrl;
+  static_assert(sizeof(MoeParams) % 4 == 0, "parameters copy as words");
+  for (int i = (int)threadIdx.x; i < (int)(sizeof(MoeParams) / 4); i += (int)blockDim.x)
+    reinterpret_cast<uint32_t *>(&sh.prm)[i] = reinterpret_cast<const uint32_t *>(&p)[i];
 
   // route: every workgroup takes route items until none are left
   for (;;) {
@@ -563,17 +593,12 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeP
     if (threadIdx.x == 0) ok0 = spin_until_eq(p.sync, &ctrl->scan_ready, p.sync.epoch, 0xFFFF0002u);
     ok = wg_sync_ok(ok0, &sh.word);
   }
-  if (ok) {
-    if (ticket < (uint32_t)p.n_land) {
-      for (;;) {
-        const uint32_t it = next_index(&ctrl->land_ctr, &sh.word);
-        if (it >= (uint32_t)(p.n_items * kLandParts)) break;
-        moe_land_and_release(p, it, sh);
-      }
-    } else if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
-      moe_compute<BM, BN>(p, smem, sh);
-    }
-    if (p.combine && ticket < (uint32_t)(p.n_land + p.n_compute)) moe_combine(p, sh, smem);
+  if (ok && ticket < (uint32_t)(p.n_land + p.n_compute)) {
+    // Every workgroup lands route items until none is left; then compute
+    // workgroups run their tiles
+    moe_land_queue(p, sh);
+    if (ticket >= (uint32_t)p.n_land) moe_compute<BM, BN>(sh.prm, smem, sh);
+    if (p.combine) moe_combine(p, sh, smem);
   }
   finish_launch(p.sync);
 }

@@ -154,6 +154,7 @@ struct MoeParams {
   int items_per_src, n_items;
   int n_land, n_compute;
   int tiles_n;
+  int tile_map;         // kMapBlocks: XCD x takes a contiguous block of row tiles (about one expert)
   int no_gate;
 };
 
