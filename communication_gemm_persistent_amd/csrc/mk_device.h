@@ -208,6 +208,15 @@ __device__ __forceinline__ uint32_t take_ticket(const Sync &s, uint32_t *lds_wor
   return uniform(*lds_word);
 }
 
+// Copy a kernel's parameter block to LDS, one word per thread (the caller's
+// next barrier publishes it).
+template <class P>
+__device__ __forceinline__ void copy_params(P *dst, const P &src) {
+  static_assert(sizeof(P) % 4 == 0, "parameters copy as words");
+  for (int i = (int)threadIdx.x; i < (int)(sizeof(P) / 4); i += (int)blockDim.x)
+    reinterpret_cast<uint32_t *>(dst)[i] = reinterpret_cast<const uint32_t *>(&src)[i];
+}
+
 // Fetch the next index from a device counter (all threads get the value).
 __device__ __forceinline__ uint32_t next_index(uint32_t *ctr, uint32_t *lds_word) {
   __syncthreads();

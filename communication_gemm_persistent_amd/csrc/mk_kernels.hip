@@ -224,16 +224,26 @@ template <int BM, int BN, int MODE>
 __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void ag_gemm_kernel(AgParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
+  // The 4-wave tile's loop reads its parameters from an LDS copy: LDS reads
+  // are reloaded where they are used (the K loop's asm may write memory), so
+  // no parameter stays live in scalar registers across its K loop, where
+  // spilled ones were restored with v_readlane every iteration.  (The 8-wave
+  // tile's fused loop measured slower that way and keeps the kernel
+  // arguments.)
+  __shared__ AgParams s_prm;
+  constexpr bool kLdsParams = TileCfg<BM, BN>::WAVES == 4;
+  if (kLdsParams) copy_params(&s_prm, p);  // take_ticket's barrier publishes the copy
+  const AgParams &q = kLdsParams ? s_prm : p;
   const uint32_t ticket = take_ticket(p.sync, &s_word);
   if (MODE == kAgLandOnly) {
     if (ticket < (uint32_t)p.n_land) ag_land(p, &s_word);
   } else if (MODE == kAgGemmOnly) {
-    if (ticket < (uint32_t)p.n_compute) ag_compute<BM, BN, true>(p, smem, &s_word, ticket);
+    if (ticket < (uint32_t)p.n_compute) ag_compute<BM, BN, true>(q, smem, &s_word, ticket);
   } else if (ticket < (uint32_t)p.n_land) {
     ag_land(p, &s_word);
-    if (p.land_joins_compute) ag_compute<BM, BN, false>(p, smem, &s_word, ticket);
+    if (p.land_joins_compute) ag_compute<BM, BN, false>(q, smem, &s_word, ticket);
   } else if (ticket < (uint32_t)(p.n_land + p.n_compute)) {
-    ag_compute<BM, BN, false>(p, smem, &s_word, ticket);
+    ag_compute<BM, BN, false>(q, smem, &s_word, ticket);
     // with dynamic roles nobody may have been assigned the items no tile
     // waits for (the local shard's copy is landed last): drain the queue
     if (p.help_land) ag_land(p, &s_word);
@@ -576,6 +586,11 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_rs_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
   __shared__ PtrTable s_tab;
+  // the tile loop reads its parameters from an LDS copy: LDS reads are
+  // reloaded where they are used (the K loop's asm may write memory), so
+  // fewer parameters stay live in (spilled) scalar registers around it
+  __shared__ RsParams s_prm;
+  copy_params(&s_prm, p);  // take_ticket's barrier publishes the copy
   fill_table(&s_tab, p.peer_c, p.outbox, p.red.ws,
              p.red.n_items > 0 && !p.red.xfer_only ? kEpiWs : p.no_peers ? kEpiNone : kEpiPeers);
   // reduce workgroups take the first tickets: every item a tile waits for
@@ -585,9 +600,9 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_rs_kernel(
   if (ticket < nr) {
     red_loop(p.sync, p.red.n_items, !p.red.xfer_only, [&](int it) { rs_reduce_item<BM, BN>(p, s_tab, it); },
              &s_word);
-    if (p.red.joins_compute) rs_compute<BM, BN>(p, s_tab, smem, &s_word);
+    if (p.red.joins_compute) rs_compute<BM, BN>(s_prm, s_tab, smem, &s_word);
   } else if (ticket < nr + (uint32_t)p.n_compute) {
-    rs_compute<BM, BN>(p, s_tab, smem, &s_word);
+    rs_compute<BM, BN>(s_prm, s_tab, smem, &s_word);
   }
   finish_launch(p.sync);
 }
@@ -673,6 +688,11 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_ar_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[TileCfg<BM, BN>::LDS_BYTES];
   __shared__ uint32_t s_word;
   __shared__ PtrTable s_tab;
+  // the tile loop reads its parameters from an LDS copy: LDS reads are
+  // reloaded where they are used (the K loop's asm may write memory), so
+  // fewer parameters stay live in (spilled) scalar registers around it
+  __shared__ ArParams s_prm;
+  copy_params(&s_prm, p);  // take_ticket's barrier publishes the copy
   fill_table(&s_tab, p.peer_c, p.bcast, p.red.ws,
              p.red.n_items > 0 && !p.red.xfer_only ? kEpiWs : p.no_peers ? kEpiNone : kEpiPeers);
   const uint32_t ticket = take_ticket(p.sync, &s_word);
@@ -680,9 +700,9 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void gemm_ar_kernel(
   if (ticket < nr) {
     red_loop(p.sync, p.red.n_items, !p.red.xfer_only, [&](int it) { ar_reduce_item<BM, BN>(p, s_tab, it); },
              &s_word);
-    if (p.red.joins_compute) ar_compute<BM, BN>(p, s_tab, smem, &s_word);
+    if (p.red.joins_compute) ar_compute<BM, BN>(s_prm, s_tab, smem, &s_word);
   } else if (ticket < nr + (uint32_t)p.n_compute) {
-    ar_compute<BM, BN>(p, s_tab, smem, &s_word);
+    ar_compute<BM, BN>(s_prm, s_tab, smem, &s_word);
   }
   finish_launch(p.sync);
 }

@@ -562,9 +562,7 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeP
   __shared__ MoeShared sh;
   const uint32_t ticket = take_ticket(p.sync, &sh.word);
   Ctrl *ctrl = p.sync.ctrl;
-  static_assert(sizeof(MoeParams) % 4 == 0, "parameters copy as words");
-  for (int i = (int)threadIdx.x; i < (int)(sizeof(MoeParams) / 4); i += (int)blockDim.x)
-    reinterpret_cast<uint32_t *>(&sh.prm)[i] = reinterpret_cast<const uint32_t *>(&p)[i];
+  copy_params(&sh.prm, p);
 
   // route: every workgroup takes route items until none are left
   for (;;) {

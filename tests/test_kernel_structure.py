@@ -4,7 +4,8 @@ Every workgroup-wide barrier must execute in control flow that all lanes
 follow together; a barrier inside a loop whose exit is exec-masked deadlocks
 the workgroup.  No global->LDS DMA (inline assembly, outside the compiler's
 hazard checks) may read a descriptor SGPR that a VALU instruction wrote
-fewer than 5 wait states before.  Each checker must also flag known-bad
+fewer than 5 wait states before.  No K loop (innermost MFMA loop) may move
+spilled registers in its hot blocks.  Each checker must also flag known-bad
 input, so a silent checker cannot pass.
 """
 import os
@@ -15,6 +16,7 @@ import pytest
 
 from tests.asm_barrier_check import check_file
 from tests.asm_hazard_check import check_file as check_hazards
+from tests.asm_loop_check import mfma_loops, spill_counts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "communication_gemm_persistent_amd", "csrc")
@@ -32,9 +34,16 @@ def _asm(src_dir, name, out_dir):
     return out
 
 
+@pytest.fixture(scope="module")
+def built(tmp_path_factory):
+    """The library's sources compiled once per test session: name -> .s path."""
+    d = str(tmp_path_factory.mktemp("asm"))
+    return {n: _asm(CSRC, n, d) for n in ("mk_kernels.hip", "mk_moe.hip", "mk_attn.hip")}
+
+
 @pytest.mark.parametrize("name", ["mk_kernels.hip", "mk_moe.hip", "mk_attn.hip"])
-def test_no_barrier_in_divergent_loop(tmp_path, name):
-    bad = check_file(_asm(CSRC, name, str(tmp_path)))
+def test_no_barrier_in_divergent_loop(built, name):
+    bad = check_file(built[name])
     assert not bad, f"barriers inside divergent loops: {bad}"
 
 
@@ -57,8 +66,8 @@ def test_checker_flags_merged_single_thread_regions(tmp_path):
 
 
 @pytest.mark.parametrize("name", ["mk_kernels.hip", "mk_moe.hip", "mk_attn.hip"])
-def test_no_sgpr_hazard_at_lds_dma(tmp_path, name):
-    bad = check_hazards(_asm(CSRC, name, str(tmp_path)))
+def test_no_sgpr_hazard_at_lds_dma(built, name):
+    bad = check_hazards(built[name])
     assert not bad, f"LDS DMAs reading a VALU-written SGPR too early: {bad[:5]}"
 
 
@@ -116,3 +125,55 @@ def test_hazard_checker_follows_branches_and_m0(tmp_path):
              "\tbuffer_load_dwordx4 v32, s[8:11], 0 offen lds\n\ts_endpgm\n.Lfunc_end0:\n")
     f.write_text(carry)
     assert check_hazards(str(f)), "a carry-out written into the descriptor"
+
+
+@pytest.mark.parametrize("name", ["mk_kernels.hip", "mk_moe.hip", "mk_attn.hip"])
+def test_no_spill_traffic_in_k_loops(built, name):
+    """Scratch accesses and v_readlane / v_writelane in a K loop's hot blocks
+    cost every iteration (a scratch load's wait also waits for the DMAs in
+    flight); the error paths of the loop's bounded waits may spill."""
+    loops = mfma_loops(built[name])
+    assert loops, "no MFMA loop found"
+    bad = [(f, n, sp[:3]) for f, n, sp in loops if sp]
+    assert not bad, f"spill traffic in K loops: {bad[:4]}"
+
+
+_LOOP_ASM = """_Z1kv:
+.LBB0_1:
+\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]
+{hot}\ts_cbranch_scc0 .LBB0_3
+.LBB0_2:
+{cold}\ts_branch .LBB0_1
+.LBB0_3:
+\ts_cbranch_scc1 .LBB0_1
+\ts_endpgm
+.Lfunc_end0:
+"""
+
+
+@pytest.mark.parametrize("hot,cold,flagged", [
+    ("", "", False),
+    ("\tscratch_load_dword v30, off, off offset:4\n", "", True),
+    ("\tv_readlane_b32 s12, v78, 37\n", "", True),
+    ("", "\tscratch_load_dword v30, off, off offset:4\n", False),  # a block without MFMAs or DMAs
+])
+def test_loop_checker_on_known_loops(tmp_path, hot, cold, flagged):
+    f = tmp_path / "k.s"
+    f.write_text(_LOOP_ASM.format(hot=hot, cold=cold))
+    loops = mfma_loops(str(f))
+    assert loops and bool(any(sp for _, _, sp in loops)) == flagged
+
+
+def test_spill_counts_bounded(built):
+    """A regression guard on the register budget: the 8-wave tiles sit at the
+    256-VGPR cap, and the few values they spill live outside the K loop
+    (checked above); the GEMM-alone and transfer-alone AllGather variants
+    spill nothing."""
+    counts = {}
+    for path in built.values():
+        counts.update(spill_counts(path))
+    assert len(counts) >= 10
+    for k, (v, s_) in counts.items():
+        assert v <= 32, (k, v)
+        if "ag_gemm_kernel" in k and not k.endswith("Li0EEEvNS_8AgParamsE"):
+            assert v == 0 and s_ == 0, (k, v, s_)
