@@ -793,12 +793,15 @@ __device__ __forceinline__ int dma_chunk(int lane, int par) { return (lane & 7) 
 // operand's region of a stage plus 1024 g).  lane_off is the lane's offset
 // for g's parity; chunks at or past K and rows past the descriptor's range
 // read as zero.  k0 >= K fetches zeros only (no memory is touched).
+__device__ __forceinline__ uint32_t dma_row_offset(uint32_t lane_off, int lane_c8, int ld_bytes, int k0, int K,
+                                                   int g) {
+  const uint32_t uni = (uint32_t)__builtin_amdgcn_readfirstlane(g * 8 * ld_bytes + k0 * 2);
+  return lane_c8 < K - k0 ? lane_off + uni : kOOB;
+}
 template <bool PAD = false>
 __device__ __forceinline__ void dma_row_group(i32x4_t vdesc, uint32_t lds_rows, uint32_t lane_off,
                                               int lane_c8, int ld_bytes, int k0, int K, int g) {
-  const uint32_t uni = (uint32_t)__builtin_amdgcn_readfirstlane(g * 8 * ld_bytes + k0 * 2);
-  const uint32_t off = lane_c8 < K - k0 ? lane_off + uni : kOOB;
-  dma16<PAD>(vdesc, __builtin_amdgcn_readfirstlane(lds_rows), off);
+  dma16<PAD>(vdesc, __builtin_amdgcn_readfirstlane(lds_rows), dma_row_offset(lane_off, lane_c8, ld_bytes, k0, K, g));
 }
 
 // Gate of a tile whose A rows arrive during the K loop in K-slabs of
@@ -885,6 +888,15 @@ __device__ __forceinline__ void gemm_tile_pingpong(
                   (own ? lds_own : lds_oth) + (stage & 1) * C::STAGE_BYTES + d * 1024,
                   lane_off[d & 1], lane_c8[d & 1], ld, stage * kBK, K, rg + d);
   };
+  // the own operand's offsets for stage t+2 are computed in MEMORY(t), which
+  // has time to spare, so COMPUTE(t) issues its refills without address
+  // arithmetic between the MFMAs
+  auto own_offset = [&](int stage, int d) {
+    return dma_row_offset(lane_off[d & 1], lane_c8[d & 1], ld, stage * kBK, K, rg + d);
+  };
+  auto fetch_own = [&](int stage, int d, uint32_t off) {
+    dma16(v_own, __builtin_amdgcn_readfirstlane(lds_own + (stage & 1) * C::STAGE_BYTES + d * 1024), off);
+  };
   auto fetch_padded = [&](bool own, int stage, int d) {  // prologue: see dma16
     dma_row_group<true>(own ? v_own : v_oth,
                         (own ? lds_own : lds_oth) + (stage & 1) * C::STAGE_BYTES + d * 1024,
@@ -927,6 +939,9 @@ __device__ __forceinline__ void gemm_tile_pingpong(
     for (int ks = 0; ks < C::SUBSTEPS; ++ks) load_frags<BM, BN>(f[ks], st, ks, wm, wn, lane);
 #pragma unroll
     for (int d = 0; d < R; ++d) fetch(false, t + 1, d);
+    uint32_t own_off[R];
+#pragma unroll
+    for (int d = 0; d < R; ++d) own_off[d] = own_offset(t + 2, d);
     if (gated) {
       // stage t + 2 starts slab chk_slab when t == chk_t; stage t + 3 starts
       // slab pf_slab when t == pf_t (counters, not a division per stage)
@@ -962,7 +977,7 @@ __device__ __forceinline__ void gemm_tile_pingpong(
     for (int m = 0; m < MFMAS; ++m) {
       const int ks = m / (C::FM * C::FN), i = (m / C::FN) % C::FM, j = m % C::FN;
       acc[i][j] = mma<BM, BN>(f[ks].b[j], f[ks].a[i], acc[i][j]);
-      if (m % DMA_EVERY == 0 && m / DMA_EVERY < R) fetch(true, t + 2, m / DMA_EVERY);
+      if (m % DMA_EVERY == 0 && m / DMA_EVERY < R) fetch_own(t + 2, m / DMA_EVERY, own_off[m / DMA_EVERY]);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmcnt<R>();  // G0: B rows 0..127 and A rows 0..127 of t+1; G1: A rows 128..255 of t+1

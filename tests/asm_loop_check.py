@@ -7,8 +7,9 @@ every DMA in flight; a v_readlane / v_writelane there moves a spilled scalar
 register (and a descriptor restored that way right before an inline-asm DMA
 is the hazard asm_hazard_check looks for).  Loops are found from the
 assembly's backward branches; the hot blocks are the loop's basic blocks
-that issue MFMAs or LDS DMAs (the error paths of its bounded waits are
-cold).
+that issue MFMAs or 16-byte LDS DMAs (the operand refills).  The error paths
+of its bounded waits and the once-per-slab flag fetch (a 4-byte DMA) are
+cold.
 """
 import re
 from typing import Dict, List, Tuple
@@ -49,7 +50,8 @@ def mfma_loops(path: str) -> List[Tuple[str, int, List[str]]]:
                 if re.match(r"^\.L\w+:$", x) or x.startswith(("s_branch", "s_cbranch")):
                     if not x.startswith(".L"):
                         block.append(x)
-                    if any(y.startswith("v_mfma") or y.endswith(" lds") for y in block):
+                    if any(y.startswith("v_mfma") or (y.startswith("buffer_load_dwordx4") and y.endswith(" lds"))
+                           for y in block):
                         spills += [y for y in block if y.startswith(SPILL_OPS) and not y.endswith(" lds")]
                     block = []
                 else:
