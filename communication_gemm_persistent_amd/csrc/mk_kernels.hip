@@ -180,6 +180,7 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
     const int m1 = min(m0 + BM, M);
     const uint16_t *abase;
     SlabGate gate{&p.sync, 0u, 0};
+    bool gated = false;
     if (!PRE && m0 >= loc0 && m1 <= loc1) {
       abase = p.shard[p.rank] + (size_t)(m0 - loc0) * p.k;
     } else {
@@ -192,13 +193,19 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
         const bool in_loop = C::WAVES == 8 && p.slab_stages > 0 && q0 == q1 && j0 == j1;
         if (!ag_acquire_rows(p, m0, m1, 0, in_loop ? 1 : p.n_slabs, helper, s_word)) break;
         if (in_loop) gate = SlabGate{&p.sync, ag_flag(p, q0, j0, 0), p.slab_stages};
+        gated = in_loop;
       }
     }
     const int valid_n = min(BN, p.n - n0);
     const i32x4_t ra = make_vdesc(abase, (uint32_t)((m1 - m0) * ldb));
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * ldb));
     AccTile<BM, BN> acc;
-    gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc, gate);
+    // two instantiations of the K loop: with a gate it is longer and holds
+    // more registers, so tiles that need no in-loop check run the plain one
+    if (gated)
+      gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc, gate);
+    else
+      gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc);
     staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
       const int row = m0 + r, col = n0 + cc;
       if (row < m1 && col < p.n) store_nt(p.c + (size_t)row * p.n + col, pack_bf16x4(v[0], v[1], v[2], v[3]));
