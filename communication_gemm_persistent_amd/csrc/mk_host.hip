@@ -906,7 +906,7 @@ static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
   if (!h) return MK_ERR_INVALID;
   h->err.clear();
   if (n_src < 1 || n_src > MK_MAX_WORLD) return fail(h, MK_ERR_INVALID, "n_src out of range");
-  if (flags & ~MK_F_NO_GATE) return fail(h, MK_ERR_INVALID, "unknown flag bits");
+  if (flags & ~(MK_F_NO_GATE | MK_F_STATIC_ROLES)) return fail(h, MK_ERR_INVALID, "unknown flag bits");
   if (!x_src || !logits_src) return fail(h, MK_ERR_INVALID, "x_src / logits_src is NULL");
   if (T < 1 || H < 8 || N < 8 || H % 8 || N % 8) return fail(h, MK_ERR_INVALID, "bad T / H / N");
   if (top_k < 1 || top_k > 8 || E < top_k || E > 256) return fail(h, MK_ERR_INVALID, "bad E / top_k");
@@ -977,6 +977,7 @@ static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
   p.n_items = n_src * p.items_per_src;
   if (p.n_items > mk::kMaxFlags) return fail(h, MK_ERR_UNSUPPORTED, "too many route items");
   p.no_gate = (flags & MK_F_NO_GATE) ? 1 : 0;
+  p.static_roles = (flags & MK_F_STATIC_ROLES) ? 1 : 0;
 
   // expected routed rows decide the tile edge
   const long exp_rows = (long)n_src * T * top_k * E_loc / E;
@@ -1014,9 +1015,10 @@ static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
   land = std::max(1, std::min(land, 4 * gmax));  // landing cannot be switched off: compute depends on it
   int compute = r.n_compute >= 0 ? std::min(r.n_compute, 4 * gmax)
                                  : (int)std::max(1L, std::min(max_row_tiles * p.tiles_n, (long)gmax - land));
-  if (combine) {
-    // Land workgroups wait for the last tile before they combine, so every
-    // workgroup must be resident at once or they could hold every slot.
+  if (combine && p.static_roles) {
+    // With static roles the land workgroups wait for the last tile before
+    // they combine without taking tiles, so at least one compute workgroup
+    // must be resident besides them: keep the grid within one residency.
     land = std::min(land, std::max(1, gmax - 1));
     compute = std::max(1, std::min(compute, gmax - land));
   }

@@ -592,10 +592,13 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeP
     ok = wg_sync_ok(ok0, &sh.word);
   }
   if (ok && ticket < (uint32_t)(p.n_land + p.n_compute)) {
-    // Every workgroup lands route items until none is left; then compute
-    // workgroups run their tiles
+    // Every workgroup lands route items until none is left, then takes
+    // tiles until none is left (land workgroups too, unless the roles are
+    // static), then combines.  A workgroup waiting in the combine has seen
+    // the tile queue empty, so every tile belongs to a running workgroup:
+    // the combine's wait needs no co-residency.
     moe_land_queue(p, sh);
-    if (ticket >= (uint32_t)p.n_land) moe_compute<BM, BN>(sh.prm, smem, sh);
+    if (ticket >= (uint32_t)p.n_land || !p.static_roles) moe_compute<BM, BN>(sh.prm, smem, sh);
     if (p.combine) moe_combine(p, sh, smem);
   }
   finish_launch(p.sync);

@@ -156,6 +156,7 @@ struct MoeParams {
   int tiles_n;
   int tile_map;         // kMapBlocks: XCD x takes a contiguous block of row tiles (about one expert)
   int no_gate;
+  int static_roles;     // land workgroups do not take tiles
 };
 
 }  // namespace mk

@@ -128,8 +128,8 @@ typedef struct {
 #define MK_F_PRELANDED 0x1u /* AG: a_gathered already holds the gathered A; ring attention: the
                                receive buffers hold every block; skip landing (compute alone) */
 #define MK_F_NO_GATE 0x2u   /* MoE: store x @ W_e without the gate factor */
-#define MK_F_STATIC_ROLES 0x4u /* AG, RS, AR: every workgroup keeps its ticket role for the whole
-                                 launch (by default AG compute workgroups land chunks while
+#define MK_F_STATIC_ROLES 0x4u /* AG, RS, AR, MoE: every workgroup keeps its ticket role for the
+                                 whole launch (by default AG compute workgroups land chunks while
                                  their rows are missing, and land and reduce workgroups run
                                  tiles once their queue is empty) */
 #define MK_F_NO_PEERS 0x8u     /* RS, AR: compute alone -- the epilogues leave out the peers'
@@ -278,6 +278,8 @@ mk_status mk_gemm_ar(mk_handle h, mk_stream stream, int world, int rank, const m
  *              expert e; chunk_offsets[e][S] = expert_offsets[e+1]
  *   x_slots    output [cap, H] bf16 device memory: the landed token rows
  *   cap        rows of y, slot_token and x_slots; must be >= S*T*min(top_k, E_loc)
+ *   flags      MK_F_NO_GATE, MK_F_STATIC_ROLES (land workgroups do not take
+ *              tiles; by default every workgroup lands, then takes tiles)
  *   1 <= top_k <= 8, top_k <= E <= 256, E_loc >= 1, rank*E_loc + E_loc <= E,
  *   H and N multiples of 8.
  */

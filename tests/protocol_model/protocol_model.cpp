@@ -25,9 +25,9 @@
 //          n_compute = 0 is the transfer-alone mode
 //   moe    every workgroup routes items, ticket 0 scans once all are routed
 //          and publishes scan_ready, every workgroup lands route items, then
-//          compute workgroups run tiles that wait for the flags of the items
-//          filling their rows; with --combine every workgroup then waits for
-//          the last tile before it combines
+//          runs tiles that wait for the flags of the items filling their rows
+//          (with --static only compute workgroups run tiles); with --combine
+//          every workgroup then waits for the last tile before it combines
 //   ring   land workgroups land key/value blocks; a task waits for the blocks
 //          it reads; the two halves of a pair combine through a counter and a
 //          flag (the first to finish publishes, the second waits and merges)
@@ -36,6 +36,7 @@
 //   --launches K --timeout-ms M --seed X --late-us U (random start delay per
 //   workgroup) --withhold I (land skips unit I: the waiters must time out)
 //   --permute (units are landed in a shuffled order) --no-help --combine
+//   --static (MoE: land workgroups keep their role)
 //
 // Output: one JSON line {"ok": ..., "err": ..., "mismatch": ..., "late":
 // ..., "ms": ...}.  err is 0 or 2 (timeout); mismatch counts data a waiter
@@ -63,7 +64,7 @@ struct Opts {
   int grid = 16, slots = 16, land = 2, compute = -1, items = 32, tiles = 48, launches = 3;
   int timeout_ms = 2000, late_us = 0, withhold = -1;
   unsigned seed = 1;
-  bool permute = false, help = true, combine = false;
+  bool permute = false, help = true, combine = false, static_roles = false;
 };
 
 // Control memory that outlives a launch (flags and arrival counters, as the
@@ -259,7 +260,7 @@ struct Launch {
     if (!wait_until([&] { return c.scan_ready.load(std::memory_order_acquire) == epoch; })) return;
     // every workgroup lands, then compute workgroups run tiles
     land_queue();
-    if (tk >= (uint32_t)o.land && tk < (uint32_t)(o.land + n_compute())) {
+    if ((tk >= (uint32_t)o.land || !o.static_roles) && tk < (uint32_t)(o.land + n_compute())) {
       for (;;) {
         const uint32_t t = c.tile_ctr.fetch_add(1);
         if (t >= (uint32_t)o.tiles) break;
@@ -317,6 +318,7 @@ void parse(int argc, char **argv, Opts &o) {
     else if (a == "--permute") o.permute = true;
     else if (a == "--no-help") o.help = false;
     else if (a == "--combine") o.combine = true;
+    else if (a == "--static") o.static_roles = true;
     else { std::fprintf(stderr, "unknown option %s\n", a.c_str()); std::exit(2); }
   }
 }

@@ -130,18 +130,19 @@ def test_moe_e64_routing_with_ties(handle, top_k):
     check_moe(d, out, top_k, 0, I.FLOAT)
 
 
-@pytest.mark.parametrize("roles", [(1, -1), (1, 3), (4, 60)])
-def test_moe_role_splits_bit_identical(handle, mk, roles):
-    """Landing is shared by the land role and by compute workgroups whose rows
-    are missing; every split of the roles gives the same bits."""
+@pytest.mark.parametrize("roles,static", [((1, -1), False), ((1, 3), False), ((4, 60), False),
+                                          ((4, 60), True), ((1, 3), True)])
+def test_moe_role_splits_bit_identical(handle, mk, roles, static):
+    """Every workgroup lands, then takes tiles (land workgroups too, unless
+    the roles are static); every split of the roles gives the same bits."""
     S, T, H, N, E, E_loc, top_k = 4, 700, 128, 136, 64, 8, 2
-    print(f"moe role split {roles}", flush=True)
+    print(f"moe role split {roles} static {static}", flush=True)
     d = I.gen_moe(S, T, H, N, E, E_loc, I.INTEGER, config=450)
     ref = run_moe(handle, d, E, top_k, rank=1)
     check_moe(d, ref, top_k, 1, I.INTEGER)
     handle.set_roles(mk.OP_MOE, n_land=roles[0], n_compute=roles[1])
     try:
-        out = run_moe(handle, d, E, top_k, rank=1)
+        out = run_moe(handle, d, E, top_k, rank=1, flags=mk.F_STATIC_ROLES if static else 0)
     finally:
         handle.set_roles(mk.OP_MOE)
     for key in ref:

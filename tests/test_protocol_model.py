@@ -15,8 +15,9 @@ how many run at once (the GPU's residency).  These tests check, on the CPU:
   (land and reduce tickets come first and never wait on compute);
 * a unit that never lands makes the waiters time out and every workgroup
   exit, instead of hanging;
-* the waits that need other workgroups to be resident (the MoE combine's
-  wait for the last tile) hang without them, which is why the library caps
+* the MoE combine's wait for the last tile needs no co-residency while land
+  workgroups take tiles too (the library's default), and hangs without it
+  when they keep their role (static roles), which is why the library caps
   that launch's grid at the residency.
 """
 import json
@@ -95,12 +96,19 @@ def test_moe_route_scan_land_compute(model):
     assert r["ok"], r
 
 
-def test_moe_combine_needs_a_resident_compute_workgroup(model):
-    # all resident: fine
-    r = model("moe", "--combine", "--grid", 24, "--slots", 24, "--land", 4, "--late-us", 1000)
+def test_moe_combine_residency(model):
+    # all resident: fine either way
+    for extra in ([], ["--static"]):
+        r = model("moe", "--combine", "--grid", 24, "--slots", 24, "--land", 4, "--late-us", 1000, *extra)
+        assert r["ok"], r
+    # land workgroups that take tiles too: a workgroup in the combine has seen
+    # the tile queue empty, so any number of slots suffices
+    r = model("moe", "--combine", "--grid", 24, "--slots", 4, "--land", 4, "--late-us", 1000)
     assert r["ok"], r
-    # the land workgroups fill every slot and wait for tiles nobody runs
-    r = model("moe", "--combine", "--grid", 24, "--slots", 4, "--land", 4, "--timeout-ms", 200, "--launches", 1)
+    # static roles: the land workgroups fill every slot and wait for tiles
+    # nobody runs (why the library keeps that launch within one residency)
+    r = model("moe", "--combine", "--static", "--grid", 24, "--slots", 4, "--land", 4, "--timeout-ms", 200,
+              "--launches", 1)
     assert not r["ok"] and r["err"] == 2, r
 
 
