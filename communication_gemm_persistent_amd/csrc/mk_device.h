@@ -150,6 +150,27 @@ __device__ __forceinline__ bool spin_until_ge(const Sync &s, const uint32_t *p, 
   }
 }
 
+// Every lane of one wave: spin until *p == want in every lane whose `need`
+// is set (lanes may watch different words).  The exit conditions are
+// wave-uniform (a ballot, the scalar clock, lane 0's view of the abort word),
+// so the wave leaves together.  Returns false on timeout or abort.
+__device__ __forceinline__ bool wave_spin_all_eq(const Sync &s, const uint32_t *p, bool need, uint32_t want,
+                                                 uint32_t info) {
+  bool pending = need && ld_relaxed(p) != want;
+  if (__ballot(pending) == 0) return true;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    __builtin_amdgcn_s_sleep(2);
+    if (pending) pending = ld_relaxed(p) != want;
+    if (__ballot(pending) == 0) return true;
+    if (__builtin_amdgcn_readfirstlane((int)aborted(s))) return false;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > s.timeout_ticks) {
+      if ((threadIdx.x & 63) == 0) raise_error(s, kErrTimeout, info);
+      return false;
+    }
+  }
+}
+
 // Arrival of one work item of flag `f`, which completes after `target` items.
 // Called by one thread after every thread of the workgroup has waited for
 // its own stores (wait_stores) and the workgroup has passed a barrier: the

@@ -18,7 +18,8 @@
 //                              landing needs the whole grid)
 //   compute (compute workgroups) grouped-GEMM tiles over the expert slots; a
 //                              tile waits for the flags of the route items whose
-//                              tokens fill its rows; y = bf16(gate * acc)
+//                              tokens fill its rows (one wave checks them in
+//                              parallel); y = bf16(gate * acc)
 //   combine (every workgroup, when requested) each finished row also returns
 //                              to its source (ret[s] at (token, k)); once every
 //                              tile is done, this rank's tokens sum their k rows
@@ -359,24 +360,23 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, int 
 
 // ---------------------------------------------------------------- compute
 
-// First route item whose range of slots of local expert e ends after slot0
-// (item_base[i][e] is non-decreasing in i).
-__device__ __forceinline__ int moe_first_item(const MoeParams &p, int e, int slot0) {
-  int lo = 0, hi = p.n_items;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    const int end = p.item_base[(size_t)mid * p.E_loc + e] + p.item_cnt[(size_t)mid * p.E_loc + e];
-    if (end > slot0) hi = mid; else lo = mid + 1;
-  }
-  return lo;
-}
-
-// Thread 0: wait for every route item whose tokens of local expert e fall in
-// slots [slot0, slot1).
+// Wave 0, every lane: wait for every route item that holds tokens of local
+// expert e in slots [slot0, slot1).  Lane l takes items l, l + 64, ...: it
+// reads the item's slot range of e and, where that range overlaps the tile's
+// rows, the item's flag; the wave loops until no lane has an item pending, so
+// a wait costs one round trip per 64 items rather than one per item.
 __device__ __forceinline__ bool moe_wait_rows(const MoeParams &p, int e, int slot0, int slot1) {
-  for (int i = moe_first_item(p, e, slot0); i < p.n_items; ++i) {
-    if (p.item_base[(size_t)i * p.E_loc + e] >= slot1) break;
-    if (!spin_until_eq(p.sync, flag_ptr(p.sync, (uint32_t)i), p.sync.epoch, (uint32_t)i)) return false;
+  const int lane = threadIdx.x & 63;
+  for (int i0 = 0; i0 < p.n_items; i0 += 64) {
+    const int i = i0 + lane;
+    bool need = false;
+    if (i < p.n_items) {
+      const int base = p.item_base[(size_t)i * p.E_loc + e];
+      const int cnt = p.item_cnt[(size_t)i * p.E_loc + e];
+      need = cnt > 0 && base < slot1 && base + cnt > slot0;
+    }
+    const uint32_t *f = flag_ptr(p.sync, (uint32_t)(need ? i : 0));
+    if (!wave_spin_all_eq(p.sync, f, need, p.sync.epoch, (uint32_t)i0)) return false;
   }
   return true;
 }
@@ -426,7 +426,7 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
     }
     const int n0 = nb * BN;
     bool ok0 = true;
-    if (threadIdx.x == 0) ok0 = moe_wait_rows(p, e, slot0, slot1);
+    if (threadIdx.x < 64) ok0 = moe_wait_rows(p, e, slot0, slot1);
     if (!wg_sync_ok(ok0, &sh.word)) break;
     const int valid_n = min(BN, p.N - n0);
     const i32x4_t ra = make_vdesc(p.x_slots + (size_t)slot0 * p.H, (uint32_t)((slot1 - slot0) * ld));
