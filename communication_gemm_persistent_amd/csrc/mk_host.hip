@@ -986,13 +986,12 @@ static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
   p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapBlocks;
   const long max_row_tiles = cdiv(cap, bm) + E_loc;
 
-  // workspace: item_cnt, item_base, tok_rank, slot_gate, slot_ret, tile list
+  // workspace: item_cnt, item_base, tok_rank, slot_gate, slot_ret
   const size_t sz_items = (size_t)p.n_items * E_loc * sizeof(int32_t);
   const size_t sz_rank = (size_t)n_src * T * top_k * sizeof(int32_t);
   const size_t sz_gate = (size_t)cap * sizeof(float);
-  const size_t sz_tiles = (size_t)(max_row_tiles + 2) * sizeof(int32_t);
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  const size_t total = al(sz_items) * 2 + al(sz_rank) + al(sz_gate) * 2 + al(sz_tiles);
+  const size_t total = al(sz_items) * 2 + al(sz_rank) + al(sz_gate) * 2;
   if ((st = need_ws(h, total, "the MoE dispatch")) != MK_OK) return st;
   char *w = static_cast<char *>(h->ws);
   p.item_cnt = reinterpret_cast<int32_t *>(w);
@@ -1004,8 +1003,6 @@ static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
   p.slot_gate = reinterpret_cast<float *>(w);
   w += al(sz_gate);
   p.slot_ret = reinterpret_cast<int32_t *>(w);
-  w += al(sz_gate);
-  p.tile_base = reinterpret_cast<int32_t *>(w);
 
   const int gmax = max_grid(h, MK_OP_MOE, bm);
   const mk_roles &r = h->roles[MK_OP_MOE];

@@ -8,10 +8,14 @@
 // Phases inside one launch, chained by flags:
 //   route  (every workgroup)   top-k over the logits, softmax gates, and per
 //                              (route item, local expert) counts and ranks
-//   scan   (ticket-0 workgroup) exclusive scan of the counts in
-//                              (expert, source, token) order -> slot offsets,
-//                              then the grouped-GEMM tile list; publishes
-//                              scan_ready
+//   offsets (every workgroup)  once every item is routed: each workgroup sums
+//                              the counts itself into its LDS (expert totals
+//                              and offsets, first row tile of each expert;
+//                              a route item's slot bases when it needs them),
+//                              so no workgroup waits for another's scan
+//   scan   (ticket-0 workgroup) the slot offsets as outputs (expert_offsets,
+//                              chunk_offsets) and the per-item bases the
+//                              combine reads; publishes scan_ready
 //   land   (every workgroup)   copies each routed token row straight into its
 //                              expert slot and releases that route item's flag
 //                              (a workgroup copies at a few tens of GB/s, so
@@ -47,9 +51,10 @@ struct MoeShared {
   int32_t wave_cnt[kMaxWaves][kMaxLocalExperts];
   int32_t list_tok[kRouteTokens * 8];  // (slot << 8 | token in item) of the unit's rows
   int32_t n_list;
-  int32_t tile_base[kMaxLocalExperts + 2];
-  int32_t expert_off[kMaxLocalExperts + 1];
+  int32_t tile_base[kMaxLocalExperts + 1];   // first row tile of each expert; [E_loc]: row tiles
+  int32_t expert_off[kMaxLocalExperts + 1];   // first slot of each expert; [E_loc]: slots
   int32_t expert_tot[kMaxLocalExperts];
+  int32_t unit_base[kMaxLocalExperts];        // first slot of (land item, expert)
   float tile_gate[256];      // gate of each row of the current tile
   int32_t tile_ret_src[256]; // source its row returns to (combine), -1: none
   uint32_t tile_ret_row[256];
@@ -191,12 +196,13 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
   return v;
 }
 
-// Slot offsets in (expert, source, token) order.  Each wave takes whole
-// experts, so the experts are scanned in parallel: (1) every expert's total,
-// (2) expert offsets, (3) each item's base = its expert's offset plus the
-// counts of the expert's earlier items.
+// Every workgroup, once every route item is counted: slots are ordered
+// (expert, source, token), so expert e's slots start at the sum of the
+// earlier experts' totals and its row tiles after theirs.  Each wave sums
+// whole experts; integer sums are exact in any order, so every workgroup gets
+// the same offsets.
 template <int BM>
-__device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
+__device__ __forceinline__ void moe_offsets(const MoeParams &p, MoeShared &sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   for (int e = wave; e < p.E_loc; e += nw) {
     int32_t tot = 0;
@@ -206,17 +212,38 @@ __device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int32_t running = 0;
+    int32_t off = 0, tiles = 0;
     for (int e = 0; e < p.E_loc; ++e) {
-      sh.expert_off[e] = running;
-      st_through(&p.expert_offsets[e], running);
-      running += sh.expert_tot[e];
+      sh.expert_off[e] = off;
+      sh.tile_base[e] = tiles;
+      off += sh.expert_tot[e];
+      tiles += (sh.expert_tot[e] + BM - 1) / BM;
     }
-    sh.expert_off[p.E_loc] = running;
-    st_through(&p.expert_offsets[p.E_loc], running);
-    st_through(&p.tile_base[1], running);
+    sh.expert_off[p.E_loc] = off;
+    sh.tile_base[p.E_loc] = tiles;
   }
   __syncthreads();
+}
+
+// First slot of every local expert's tokens of route item `item`
+// (sh.unit_base): the expert's offset plus its counts in the earlier items.
+__device__ __forceinline__ void moe_unit_bases(const MoeParams &p, int item, MoeShared &sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int e = wave; e < p.E_loc; e += nw) {
+    int32_t before = 0;
+    for (int i = lane; i < item; i += 64) before += p.item_cnt[(size_t)i * p.E_loc + e];
+    before = wave_inclusive_scan(before);
+    if (lane == 63) sh.unit_base[e] = sh.expert_off[e] + before;
+  }
+  __syncthreads();
+}
+
+// The ticket-0 workgroup: the slot offsets as outputs -- expert_offsets, each
+// source's first slot per expert (chunk_offsets) and, for the combine, each
+// item's base (item_base).  Each wave scans whole experts over the items.
+__device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (threadIdx.x <= (unsigned)p.E_loc) st_through(&p.expert_offsets[threadIdx.x], sh.expert_off[threadIdx.x]);
   for (int e = wave; e < p.E_loc; e += nw) {
     int32_t carry = sh.expert_off[e];
     for (int i0 = 0; i0 < p.n_items; i0 += 64) {
@@ -225,24 +252,12 @@ __device__ __forceinline__ void moe_scan(const MoeParams &p, MoeShared &sh) {
       const int32_t incl = wave_inclusive_scan(v);
       const int32_t base = carry + incl - v;
       if (i < p.n_items) {
-        st_through(&p.item_base[(size_t)i * p.E_loc + e], base);
+        if (p.combine) st_through(&p.item_base[(size_t)i * p.E_loc + e], base);
         if (i % p.items_per_src == 0) st_through(&p.chunk_offsets[e * (p.S + 1) + i / p.items_per_src], base);
       }
       carry += __shfl(incl, 63, 64);
     }
     if (lane == 0) st_through(&p.chunk_offsets[e * (p.S + 1) + p.S], carry);
-  }
-  __syncthreads();
-  // grouped-GEMM row tiles, expert by expert (the XCD tile map hands each
-  // XCD a contiguous block of them, so the tiles one XCD runs share their
-  // expert's weights and their m-blocks' rows in its L2); the offsets are
-  // read from LDS (one thread, many dependent reads)
-  if (threadIdx.x == 0) {
-    int ntile_rows = 0;
-    for (int e = 0; e < p.E_loc; ++e)
-      for (int mt = 0; mt * BM < sh.expert_off[e + 1] - sh.expert_off[e]; ++mt)
-        st_through(&p.tile_base[2 + ntile_rows++], (int32_t)((e << 16) | mt));
-    st_through(&p.tile_base[0], (int32_t)ntile_rows);
   }
 }
 
@@ -334,13 +349,13 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, int 
   const int t = b * kRouteTokens + (int)threadIdx.x;
   const int e_lo = p.rank * p.E_loc;
   if (threadIdx.x == 0) sh.n_list = 0;
-  __syncthreads();
+  moe_unit_bases(p, item, sh);  // ends with a barrier
   if (threadIdx.x < (unsigned)kRouteTokens && t < p.T && (int)threadIdx.x % kLandParts == part) {
     const size_t o = ((size_t)s * p.T + t) * p.top_k;
     for (int j = 0; j < p.top_k; ++j) {
       const int e = p.topk_idx[o + j] - e_lo;
       if (e >= 0 && e < p.E_loc) {
-        const int slot = p.item_base[(size_t)item * p.E_loc + e] + p.tok_rank[o + j];
+        const int slot = sh.unit_base[e] + p.tok_rank[o + j];
         if (slot < 0 || slot >= p.cap) {  // cannot happen when routing and scan agree
           raise_error(p.sync, kErrInternal, (uint32_t)item);
           continue;
@@ -361,20 +376,22 @@ __device__ __forceinline__ void moe_land_item(const MoeParams &p, int item, int 
 // ---------------------------------------------------------------- compute
 
 // Wave 0, every lane: wait for every route item that holds tokens of local
-// expert e in slots [slot0, slot1).  Lane l takes items l, l + 64, ...: it
-// reads the item's slot range of e and, where that range overlaps the tile's
-// rows, the item's flag; the wave loops until no lane has an item pending, so
-// a wait costs one round trip per 64 items rather than one per item.
-__device__ __forceinline__ bool moe_wait_rows(const MoeParams &p, int e, int slot0, int slot1) {
+// expert e in slots [slot0, slot1) (expert e's slots start at e_off).  Lane l
+// takes items l, l + 64, ...: the wave scans the items' counts of e into
+// their slot ranges and each lane whose item's range overlaps the tile's rows
+// watches that item's flag; the wave loops until no lane has an item
+// pending, so a wait costs one round trip per 64 items rather than one per
+// item.
+__device__ __forceinline__ bool moe_wait_rows(const MoeParams &p, int e, int e_off, int slot0, int slot1) {
   const int lane = threadIdx.x & 63;
+  int32_t carry = e_off;
   for (int i0 = 0; i0 < p.n_items; i0 += 64) {
     const int i = i0 + lane;
-    bool need = false;
-    if (i < p.n_items) {
-      const int base = p.item_base[(size_t)i * p.E_loc + e];
-      const int cnt = p.item_cnt[(size_t)i * p.E_loc + e];
-      need = cnt > 0 && base < slot1 && base + cnt > slot0;
-    }
+    const int32_t cnt = i < p.n_items ? p.item_cnt[(size_t)i * p.E_loc + e] : 0;
+    const int32_t incl = wave_inclusive_scan(cnt);
+    const int32_t base = carry + incl - cnt;
+    carry += __shfl(incl, 63, 64);
+    const bool need = cnt > 0 && base < slot1 && base + cnt > slot0;
     const uint32_t *f = flag_ptr(p.sync, (uint32_t)(need ? i : 0));
     if (!wave_spin_all_eq(p.sync, f, need, p.sync.epoch, (uint32_t)i0)) return false;
   }
@@ -405,19 +422,20 @@ __device__ __forceinline__ void moe_land_queue(const MoeParams &p, MoeShared &sh
 template <int BM, int BN>
 __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeShared &sh) {
   using C = TileCfg<BM, BN>;
-  if (threadIdx.x <= (unsigned)p.E_loc) sh.expert_off[threadIdx.x] = p.expert_offsets[threadIdx.x];
-  if (threadIdx.x == 0) sh.tile_base[0] = p.tile_base[0];
   if (threadIdx.x < (unsigned)MK_MAX_WORLD) sh.ret_ptr[threadIdx.x] = p.ret[threadIdx.x];
   __syncthreads();
-  const int n_row_tiles = (int)uniform((uint32_t)sh.tile_base[0]);
+  const int n_row_tiles = (int)uniform((uint32_t)sh.tile_base[p.E_loc]);
   const int ld = p.H * 2;
   const int xcd = xcd_id();
   for (;;) {
     const int t = next_tile(p.sync, n_row_tiles, p.tiles_n, xcd, TileOrder{p.tile_map, 1, 1}, &sh.word);
     if (t < 0) break;
     const int rt = (int)t / p.tiles_n, nb = (int)t % p.tiles_n;
-    const int code = (int)uniform((uint32_t)p.tile_base[2 + rt]);
-    const int e = code >> 16, mt = code & 0xFFFF;
+    // row tile rt is tile mt of the last expert e whose first row tile is <= rt
+    int e = 0;
+    for (int x = 1; x < p.E_loc; ++x)
+      if ((int)uniform((uint32_t)sh.tile_base[x]) <= rt) e = x;
+    const int mt = rt - (int)uniform((uint32_t)sh.tile_base[e]);
     const int slot0 = (int)uniform((uint32_t)sh.expert_off[e]) + mt * BM;
     const int slot1 = min(slot0 + BM, (int)uniform((uint32_t)sh.expert_off[e + 1]));
     if (e >= p.E_loc || slot0 < 0 || slot1 > p.cap || slot1 <= slot0) {
@@ -426,7 +444,7 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
     }
     const int n0 = nb * BN;
     bool ok0 = true;
-    if (threadIdx.x < 64) ok0 = moe_wait_rows(p, e, slot0, slot1);
+    if (threadIdx.x < 64) ok0 = moe_wait_rows(p, e, (int)uniform((uint32_t)sh.expert_off[e]), slot0, slot1);
     if (!wg_sync_ok(ok0, &sh.word)) break;
     const int valid_n = min(BN, p.N - n0);
     const i32x4_t ra = make_vdesc(p.x_slots + (size_t)slot0 * p.H, (uint32_t)((slot1 - slot0) * ld));
@@ -544,8 +562,10 @@ __device__ __forceinline__ void moe_combine(const MoeParams &p, MoeShared &sh, c
     if (!waited) {
       bool ok0 = true;
       if (threadIdx.x == 0) {
-        const uint32_t n_tiles = (uint32_t)p.tile_base[0] * (uint32_t)p.tiles_n;
-        ok0 = spin_until_ge(p.sync, &ctrl->tiles_done, n_tiles, 0xFFFF0003u);
+        // every tile's rows, and the ticket-0 workgroup's item bases
+        const uint32_t n_tiles = (uint32_t)sh.tile_base[p.E_loc] * (uint32_t)p.tiles_n;
+        ok0 = spin_until_ge(p.sync, &ctrl->tiles_done, n_tiles, 0xFFFF0003u) &&
+              spin_until_eq(p.sync, &ctrl->scan_ready, p.sync.epoch, 0xFFFF0002u);
       }
       if (!wg_sync_ok(ok0, &sh.word)) break;  // full acquire: rows of every tile are visible
       waited = true;
@@ -574,22 +594,17 @@ __global__ __launch_bounds__((TileCfg<BM, BN>::THREADS), 1) void moe_kernel(MoeP
     if (threadIdx.x == 0) add_relaxed(&ctrl->route_done, 1u);  // the outputs were written through
   }
 
-  bool ok = true;
-  if (ticket == 0) {
-    bool ok0 = true;
-    if (threadIdx.x == 0) ok0 = spin_until_ge(p.sync, &ctrl->route_done, (uint32_t)p.n_items, 0xFFFF0001u);
-    ok = wg_sync_ok(ok0, &sh.word);
-    if (ok) {
-      moe_scan<BM>(p, sh);
-      wait_stores();
-      __syncthreads();
-      if (threadIdx.x == 0) st_through(&ctrl->scan_ready, p.sync.epoch);
-    }
-  }
-  if (ok && ticket < (uint32_t)(p.n_land + p.n_compute)) {
-    bool ok0 = true;
-    if (threadIdx.x == 0) ok0 = spin_until_eq(p.sync, &ctrl->scan_ready, p.sync.epoch, 0xFFFF0002u);
-    ok = wg_sync_ok(ok0, &sh.word);
+  // every workgroup: wait until every route item is counted, then the
+  // offsets into LDS
+  bool ok0 = true;
+  if (threadIdx.x == 0) ok0 = spin_until_ge(p.sync, &ctrl->route_done, (uint32_t)p.n_items, 0xFFFF0001u);
+  const bool ok = wg_sync_ok(ok0, &sh.word);
+  if (ok) moe_offsets<BM>(p, sh);
+  if (ok && ticket == 0) {
+    moe_scan(p, sh);
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) st_through(&ctrl->scan_ready, p.sync.epoch);
   }
   if (ok && ticket < (uint32_t)(p.n_land + p.n_compute)) {
     // Every workgroup lands route items until none is left, then takes

@@ -138,10 +138,9 @@ struct MoeParams {
   uint16_t *x_slots;
   // workspace
   int32_t *item_cnt;    // [n_items, E_loc] tokens of item routed to local expert e
-  int32_t *item_base;   // [n_items, E_loc] first slot of (item, e)
+  int32_t *item_base;   // [n_items, E_loc] first slot of (item, e) (written for the combine)
   int32_t *tok_rank;    // [S*T, top_k] rank of the token within (item, e); -1 if not local
   float *slot_gate;     // [cap]
-  int32_t *tile_base;   // [E_loc + 1] first GEMM tile of each expert
   int32_t *slot_ret;    // [cap] return position (s*T + t)*top_k + k of every slot (combine)
   // combine (when `combine`): rows of this rank's experts return to ret[s]
   // ([T, top_k, N] per source s != rank); this rank's tokens sum their rows

@@ -23,11 +23,14 @@
 //   rs     reduce workgroups sum peers' partials per item and release the
 //          item's flag; compute tiles wait for it in their epilogue;
 //          n_compute = 0 is the transfer-alone mode
-//   moe    every workgroup routes items, ticket 0 scans once all are routed
-//          and publishes scan_ready, every workgroup lands route items, then
-//          runs tiles that wait for the flags of the items filling their rows
+//   moe    every workgroup routes items, then waits until all are routed and
+//          reads every item's counts itself (its own copy of the offsets);
+//          ticket 0 also writes the per-item bases for the combine and
+//          publishes scan_ready; every workgroup lands route items, then runs
+//          tiles that wait for the flags of the items filling their rows
 //          (with --static only compute workgroups run tiles); with --combine
-//          every workgroup then waits for the last tile before it combines
+//          every workgroup then waits for the last tile and scan_ready before
+//          it combines
 //   ring   land workgroups land key/value blocks; a task waits for the blocks
 //          it reads; the two halves of a pair combine through a counter and a
 //          flag (the first to finish publishes, the second waits and merges)
@@ -110,6 +113,7 @@ struct Launch {
   std::vector<std::atomic<uint64_t>> &ws;     // reduce / merge workspace
   std::vector<int> order;                     // landing order of the units
   std::atomic<int> mismatch{0};
+  std::atomic<uint64_t> bases{0};             // MoE: the item bases ticket 0 writes for the combine
   std::vector<std::vector<int>> needs;        // units each tile waits for
 
   bool aborted() const { return c.abort_epoch.load(std::memory_order_relaxed) == epoch; }
@@ -251,13 +255,14 @@ struct Launch {
       ws[i].store(stamp(i, epoch), std::memory_order_relaxed);  // the item's counts
       c.route_done.fetch_add(1, std::memory_order_release);
     }
-    if (tk == 0) {
-      if (!wait_until([&] { return c.route_done.load(std::memory_order_acquire) >= (uint32_t)o.items; })) return;
-      for (int i = 0; i < o.items; ++i)
-        if (ws[i].load(std::memory_order_relaxed) != stamp(i, epoch)) mismatch.fetch_add(1);
+    // every workgroup: all items routed, then their counts (the offsets)
+    if (!wait_until([&] { return c.route_done.load(std::memory_order_acquire) >= (uint32_t)o.items; })) return;
+    for (int i = 0; i < o.items; ++i)
+      if (ws[i].load(std::memory_order_relaxed) != stamp(i, epoch)) mismatch.fetch_add(1);
+    if (tk == 0) {  // the combine's item bases
+      bases.store(stamp(7777777, epoch), std::memory_order_relaxed);
       c.scan_ready.store(epoch, std::memory_order_release);
     }
-    if (!wait_until([&] { return c.scan_ready.load(std::memory_order_acquire) == epoch; })) return;
     // every workgroup lands, then compute workgroups run tiles
     land_queue();
     if ((tk >= (uint32_t)o.land || !o.static_roles) && tk < (uint32_t)(o.land + n_compute())) {
@@ -268,8 +273,11 @@ struct Launch {
         c.tiles_done.fetch_add(1, std::memory_order_release);
       }
     }
-    if (o.combine)  // every tile's rows must be final before the combine
-      (void)wait_until([&] { return c.tiles_done.load(std::memory_order_acquire) >= (uint32_t)o.tiles; });
+    if (o.combine) {  // every tile's rows and ticket 0's bases must be final before the combine
+      if (!wait_until([&] { return c.tiles_done.load(std::memory_order_acquire) >= (uint32_t)o.tiles; })) return;
+      if (!wait_until([&] { return c.scan_ready.load(std::memory_order_acquire) == epoch; })) return;
+      if (bases.load(std::memory_order_relaxed) != stamp(7777777, epoch)) mismatch.fetch_add(1);
+    }
   }
 
   // ring: units are key/value blocks; tiles are tasks, task t of pair t % P,
