@@ -23,10 +23,13 @@
 //
 // Every wave owns 32 query rows (two 16-row blocks) and all 128 columns of
 // the head.  S comes out of the 16x16x32 MFMA with each lane holding 4
-// consecutive keys of one query row; the P V product takes P from those
-// registers directly: within every 32-key step, lane group g supplies keys
-// 4g..4g+3 and 16+4g..16+4g+3 as its 8 K slots, and V^T is read from LDS in
-// the same slot order, so the sum over K slots is the sum over keys.
+// S columns of one query row (LDS K rows 16 kb + 4 g .. +3); the P V product
+// takes P from those registers directly: within every 32-row step, lane
+// group g supplies LDS rows 4g..4g+3 and 16+4g..16+4g+3 as its 8 K slots.
+// The K tile is staged with its keys permuted so that those 8 rows hold 8
+// consecutive keys (LDS row 32 kk + 16 h + 4 g + s holds key
+// 32 kk + 8 g + 4 h + s): the matching V^T values are then one 16-byte LDS
+// read, and the sum over K slots is the sum over keys.
 #include "mk_params.h"
 
 namespace mk {
@@ -48,7 +51,6 @@ constexpr int kAttnSlot = kAttnQ * kAttnD + 2 * kAttnQ;
 static_assert(kAttnD * kAttnTPitch <= kAttnLds, "transpose tile fits the staging area");
 static_assert(kAttnD == 128, "the task layout assumes 128-wide heads");
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- land
 
@@ -116,13 +118,6 @@ __device__ __forceinline__ float xor_max(float v, int m) {
 }
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
 
-// Two 8-byte LDS reads as one 8-value fragment (K slots 0..3, 4..7).
-__device__ __forceinline__ bf16x8_t lds_pair(const char *a, const char *b) {
-  const bf16x4_t lo = *reinterpret_cast<const bf16x4_t *>(a);
-  const bf16x4_t hi = *reinterpret_cast<const bf16x4_t *>(b);
-  return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 __device__ __forceinline__ bf16x8_t pack_p(const f32x4_t &a, const f32x4_t &b) {
   const uint2 lo = pack_bf16x4(a[0], a[1], a[2], a[3]);
   const uint2 hi = pack_bf16x4(b[0], b[1], b[2], b[3]);
@@ -171,9 +166,13 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
   float mrow[2] = {-INFINITY, -INFINITY};  // running row max (log2 domain)
   float lpart[2] = {0.f, 0.f};             // this lane's part of the row sum
 
-  // DMA lane offsets (8-row groups, 64-wide rows, swizzled as the GEMM tiles)
-  const uint32_t lane_off_k[2] = {(uint32_t)((lane >> 3) * ldk + dma_chunk(lane, 0) * 16),
-                                  (uint32_t)((lane >> 3) * ldk + dma_chunk(lane, 1) * 16)};
+  // DMA lane offsets (8-row groups, 64-wide rows, swizzled as the GEMM tiles).
+  // K: LDS row 8 gl + rs (rs = lane >> 3) holds key kperm(gl) + 8 (rs >> 2) + (rs & 3)
+  // (the permutation above); the swizzle follows the LDS row
+  const int rs = lane >> 3;
+  const uint32_t lane_off_k[2] = {(uint32_t)((8 * (rs >> 2) + (rs & 3)) * ldk + dma_chunk(lane, 0) * 16),
+                                  (uint32_t)((8 * (rs >> 2) + (rs & 3)) * ldk + dma_chunk(lane, 1) * 16)};
+  auto kperm = [](int gl) { return 32 * (gl >> 2) + 16 * (gl & 1) + 4 * ((gl >> 1) & 1); };
   const uint32_t lane_off_v[2] = {(uint32_t)((lane >> 3) * ldv + dma_chunk(lane, 0) * 16),
                                   (uint32_t)((lane >> 3) * ldv + dma_chunk(lane, 1) * 16)};
   const int lane_c8[2] = {dma_chunk(lane, 0) * 8, dma_chunk(lane, 1) * 8};
@@ -190,8 +189,8 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int gl = 4 * (wave & 1) + d;  // row group within the tile
-      dma_row_group(vk, st + half * kAttnKHalf + gl * 1024, lane_off_k[gl & 1], lane_c8[gl & 1], ldk,
-                    half * 64, kAttnD, kt * (kAttnKT / 8) + gl);
+      const uint32_t uni = (uint32_t)__builtin_amdgcn_readfirstlane((kt * kAttnKT + kperm(gl)) * ldk + half * 128);
+      dma16(vk, __builtin_amdgcn_readfirstlane(st + half * kAttnKHalf + gl * 1024), lane_off_k[gl & 1] + uni);
     }
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -283,18 +282,16 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
       pf[mb][0] = pack_p(sacc[mb][0], sacc[mb][1]);
       pf[mb][1] = pack_p(sacc[mb][2], sacc[mb][3]);
     }
-    // O += P V: V^T row d = 16 db + r16, K slots = keys 32 kk + 4 g .. +3 and
-    // 32 kk + 16 + 4 g .. +3 (8-byte halves of 16-byte chunks 4 kk + g / 2
-    // and 4 kk + 2 + g / 2)
+    // O += P V: V^T row d = 16 db + r16, K slots = keys 32 kk + 8 g .. +7
+    // (16-byte chunk 4 kk + g of the row)
     const char *vt = st + kAttnVOff;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const char *vrow = vt + (db * 16 + r16) * 128 + (g & 1) * 8;
+      const char *vrow = vt + (db * 16 + r16) * 128;
       const int swz = (lane >> 1) & 7;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int c1 = 4 * kk + (g >> 1), c2 = 4 * kk + 2 + (g >> 1);
-        const bf16x8_t vf = lds_pair(vrow + ((c1 ^ swz) << 4), vrow + ((c2 ^ swz) << 4));
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(vrow + (((4 * kk + g) ^ swz) << 4));
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) oacc[mb][db] = mfma16(vf, pf[mb][kk], oacc[mb][db]);
       }
