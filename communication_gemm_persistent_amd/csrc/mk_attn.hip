@@ -177,13 +177,15 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
                                   (uint32_t)((lane >> 3) * ldv + dma_chunk(lane, 1) * 16)};
   const int lane_c8[2] = {dma_chunk(lane, 0) * 8, dma_chunk(lane, 1) * 8};
   // this wave's DMAs of a tile: K half (wave >> 1), row groups 4 (wave & 1) ..
-  // +3; V^T row groups 4 wave .. +3
-  auto stage_tile = [&](int j, int buf) {
-    const int step = j / tpb, kt = j % tpb;
-    const int src = (p.rank - step + p.world) % p.world;
-    const size_t blk = (size_t)src * p.BH + bh;
-    const i32x4_t vk = make_vdesc(p.k_recv + blk * p.S_kv * kAttnD, (uint32_t)(p.S_kv * ldk));
-    const i32x4_t vv = make_vdesc(p.vt_recv + blk * kAttnD * p.S_kv, (uint32_t)(kAttnD * ldv));
+  // +3; V^T row groups 4 wave .. +3.  K and V^T of tile t go to the K and V
+  // parts of stage t & 1, K one tile ahead of V (see the loop below).
+  auto block_of = [&](int j) {
+    const int src = (p.rank - j / tpb + p.world) % p.world;
+    return (size_t)src * p.BH + bh;
+  };
+  auto stage_k = [&](int j, int buf) {
+    const int kt = j % tpb;
+    const i32x4_t vk = make_vdesc(p.k_recv + block_of(j) * p.S_kv * kAttnD, (uint32_t)(p.S_kv * ldk));
     const uint32_t st = base + buf * kAttnStage;
     const int half = wave >> 1;
 #pragma unroll
@@ -192,6 +194,11 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
       const uint32_t uni = (uint32_t)__builtin_amdgcn_readfirstlane((kt * kAttnKT + kperm(gl)) * ldk + half * 128);
       dma16(vk, __builtin_amdgcn_readfirstlane(st + half * kAttnKHalf + gl * 1024), lane_off_k[gl & 1] + uni);
     }
+  };
+  auto stage_v = [&](int j, int buf) {
+    const int kt = j % tpb;
+    const i32x4_t vv = make_vdesc(p.vt_recv + block_of(j) * kAttnD * p.S_kv, (uint32_t)(kAttnD * ldv));
+    const uint32_t st = base + buf * kAttnStage;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int gl = 4 * wave + d;
@@ -213,23 +220,14 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
     if (threadIdx.x == 0) ok0 = spin_until_eq(p.sync, flag_ptr(p.sync, f), p.sync.epoch, f);
     return wg_sync_ok(ok0, s_word, !p.light_acquire);
   };
-
-  if (!acquire(j0)) return false;
-  stage_tile(j0, j0 & 1);
-  for (int j = j0; j < j1; ++j) {
-    wait_vmcnt<0>();
-    wg_barrier();  // tile j landed; every wave is done with the other buffer
-    if (j + 1 < j1) {
-      if (!acquire(j + 1)) return false;  // timeout or abort: nothing is in flight here
-      stage_tile(j + 1, (j + 1) & 1);
-    }
-    const char *st = smem + (j & 1) * kAttnStage;
-    // S = Q K^T: sacc[mb][kb] lane (g, r16): query 16 mb + r16, keys 16 kb + 4 g + 0..3
-    f32x4_t sacc[2][4];
+  // S = Q K^T of the K tile in stage buf: s[mb][kb] lane (g, r16): query
+  // 16 mb + r16, LDS K rows 16 kb + 4 g + 0..3
+  auto qk = [&](f32x4_t (&s)[2][4], int buf) {
+    const char *st = smem + buf * kAttnStage;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sacc[mb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb) s[mb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c = (ks & 1) * 4 + g;  // logical chunk of the 128-byte row
@@ -240,37 +238,61 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) sacc[mb][kb] = mfma16(kf[kb], qf[mb][ks], sacc[mb][kb]);
+        for (int mb = 0; mb < 2; ++mb) s[mb][kb] = mfma16(kf[kb], qf[mb][ks], s[mb][kb]);
     }
-    // online softmax (log2 domain)
-    bf16x8_t pf[2][2];
-    // The scale is positive, so the row max is taken over the raw scores
-    // and scaled once; exp2(s scale_log2 - m) is one fma and one exp2.  When
-    // no row's max grows, alpha is exactly 1 for every row of the wave and
-    // the rescale of O is skipped (the same bits).
-    const float c = p.scale_log2;
+  };
+
+  // row max of S (log2 domain) over the wave's 4 lane groups: the scale is
+  // positive, so the max is taken over the raw scores and scaled once
+  const float c = p.scale_log2;
+  auto row_max = [&](const f32x4_t (&s)[2][4], float (&m)[2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[mb][kb][r]);
-      mx = xor_max(xor_max(mx, 16), 32) * c;
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[mb][kb][r]);
+      m[mb] = xor_max(xor_max(mx, 16), 32) * c;
+    }
+  };
+
+  // Software pipeline: iteration j computes S of tile j + 1 while it runs
+  // the exponentials of tile j (the MFMAs of one and the vector instructions
+  // of the other interleave), then O += P V of tile j while it takes the row
+  // max of tile j + 1.  LDS holds K(j+1) and V(j) during iteration j, while
+  // K(j+2) and V(j+1) land.  The acquires come before any DMA of the
+  // iteration is issued, so a failed wait returns with nothing in flight.
+  if (!acquire(j0)) return false;
+  if (j0 + 1 < j1 && !acquire(j0 + 1)) return false;
+  stage_k(j0, j0 & 1);
+  stage_v(j0, j0 & 1);
+  if (j0 + 1 < j1) stage_k(j0 + 1, (j0 + 1) & 1);
+  wait_vmcnt<0>();
+  wg_barrier();
+  f32x4_t sacc[2][4];
+  float tmax[2];  // row max of the tile in sacc
+  qk(sacc, j0 & 1);
+  row_max(sacc, tmax);
+  for (int j = j0; j < j1; ++j) {
+    // every wave is done with K(j) (read for S(j)) and V(j - 1); this wave's
+    // DMAs of K(j+1) and V(j) have landed (waited for below, or in the prologue)
+    wg_barrier();
+    if (j + 2 < j1) {
+      if (!acquire(j + 2)) return false;
+      stage_k(j + 2, j & 1);
+    }
+    if (j + 1 < j1) stage_v(j + 1, (j + 1) & 1);
+    // the running max; when no row's max grows, alpha is exactly 1 for every
+    // row of the wave and the rescale of O is skipped (the same bits)
+    float mnew[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
       const float mold = mrow[mb];
-      const float mnew = fmaxf(mold, mx);
-      mrow[mb] = mnew;
-      float sum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][kb][r], c, -mnew));
-          sacc[mb][kb][r] = e;
-          sum += e;
-        }
-      if (__any(mnew > mold)) {
-        const float alpha = __builtin_amdgcn_exp2f(mold - mnew);
+      mnew[mb] = fmaxf(mold, tmax[mb]);
+      mrow[mb] = mnew[mb];
+      if (__any(mnew[mb] > mold)) {
+        const float alpha = __builtin_amdgcn_exp2f(mold - mnew[mb]);
         lpart[mb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
@@ -278,13 +300,31 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
           oacc[mb][db][2] *= alpha; oacc[mb][db][3] *= alpha;
         }
       }
+    }
+    // S of tile j + 1 (in the last iteration a product of stale LDS data,
+    // never used: the stage is in-bounds and nothing is landing in it) and
+    // P = exp2(s scale_log2 - m) of tile j: one fma and one exp2 per score
+    f32x4_t snext[2][4];
+    qk(snext, (j + 1) & 1);
+    bf16x8_t pf[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float sum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][kb][r], c, -mnew[mb]));
+          sacc[mb][kb][r] = e;
+          sum += e;
+        }
       lpart[mb] += sum;
       pf[mb][0] = pack_p(sacc[mb][0], sacc[mb][1]);
       pf[mb][1] = pack_p(sacc[mb][2], sacc[mb][3]);
     }
     // O += P V: V^T row d = 16 db + r16, K slots = keys 32 kk + 8 g .. +7
-    // (16-byte chunk 4 kk + g of the row)
-    const char *vt = st + kAttnVOff;
+    // (16-byte chunk 4 kk + g of the row); then the row max of tile j + 1
+    const char *vt = smem + (j & 1) * kAttnStage + kAttnVOff;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const char *vrow = vt + (db * 16 + r16) * 128;
@@ -296,6 +336,12 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
         for (int mb = 0; mb < 2; ++mb) oacc[mb][db] = mfma16(vf, pf[mb][kk], oacc[mb][db]);
       }
     }
+    row_max(snext, tmax);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) sacc[mb][kb] = snext[mb][kb];
+    wait_vmcnt<0>();  // this wave's DMAs of K(j+2) and V(j+1)
   }
   wg_barrier();  // both buffers are free for the next task
   // row sums over the 4 lane groups; then store, or combine with the other half
