@@ -44,6 +44,7 @@ struct mk_ctx {
   int help_every = 0;  // MK_HELP_EVERY env: 1 in this many compute workgroups helps land (0: automatic)
   int help_eager = -1;  // MK_HELP_EAGER env: helpers land until the queue is empty (-1: automatic)
   int land_split = 1;  // MK_LAND_SPLIT env: land first-round chunks at the start, the rest between tiles
+  int moe_withhold = -1;  // MK_TEST_MOE_WITHHOLD env (failure tests only): the MoE land queue skips this unit
   mk::Ctrl *ctrl = nullptr;
   uint32_t *flags = nullptr;
   uint32_t *cnt = nullptr;
@@ -466,6 +467,7 @@ mk_status mk_create(mk_handle *out, const mk_config *cfg) {
   if (const char *t = std::getenv("MK_HELP_EVERY")) h->help_every = std::max(1, std::atoi(t));
   if (const char *t = std::getenv("MK_HELP_EAGER")) h->help_eager = std::atoi(t) != 0 ? 1 : 0;
   if (const char *t = std::getenv("MK_LAND_SPLIT")) h->land_split = std::atoi(t) != 0 ? 1 : 0;
+  if (const char *t = std::getenv("MK_TEST_MOE_WITHHOLD")) h->moe_withhold = std::atoi(t);
   for (int i = 0; i < MK_OP_COUNT; ++i) h->roles[i] = mk_roles{-1, -1, -1};
   if (const char *r = std::getenv("MK_ROLES")) {
     int l = -1, c = -1, d = -1;
@@ -978,6 +980,7 @@ static mk_status moe_launch(mk_handle h, mk_stream stream, int n_src, int rank,
   if (p.n_items > mk::kMaxFlags) return fail(h, MK_ERR_UNSUPPORTED, "too many route items");
   p.no_gate = (flags & MK_F_NO_GATE) ? 1 : 0;
   p.static_roles = (flags & MK_F_STATIC_ROLES) ? 1 : 0;
+  p.withhold = h->moe_withhold;
 
   // expected routed rows decide the tile edge
   const long exp_rows = (long)n_src * T * top_k * E_loc / E;

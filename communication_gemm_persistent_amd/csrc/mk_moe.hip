@@ -421,6 +421,7 @@ __device__ __forceinline__ void moe_land_queue(const MoeParams &p, MoeShared &sh
   for (;;) {
     const uint32_t it = next_index(&p.sync.ctrl->land_ctr, &sh.word);
     if (it >= (uint32_t)(p.n_items * kLandParts)) break;
+    if ((int)it == p.withhold) continue;  // failure tests only
     moe_land_and_release(p, it, sh);
   }
 }

@@ -156,6 +156,7 @@ struct MoeParams {
   int tile_map;         // kMapBlocks: XCD x takes a contiguous block of row tiles (about one expert)
   int no_gate;
   int static_roles;     // land workgroups do not take tiles
+  int withhold;         // failure tests: land unit never landed (-1: none), so its waiters time out
 };
 
 }  // namespace mk

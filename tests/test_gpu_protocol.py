@@ -43,6 +43,33 @@ def test_withheld_chunks_time_out_and_handle_recovers(mk):
         O.assert_bits_equal(bits(c), O.ag_gemm(d["shards"], d["b"])["c"], "after recovery")
 
 
+@pytest.mark.parametrize("combine", [False, True])
+def test_moe_withheld_unit_times_out_and_handle_recovers(mk, monkeypatch, combine):
+    """A MoE land unit that never lands (MK_TEST_MOE_WITHHOLD, a test-only
+    knob read when the handle is created) leaves its route item's flag unset:
+    the wave that checks a tile's item flags gives up at the spin limit, so
+    does the combine's wait for the last tile, and the launch completes with
+    MK_ERR_TIMEOUT recorded.  A second call on the handle reports it again;
+    a handle without the knob then computes the right result."""
+    from tests.test_gpu_moe import check_moe, run_moe
+    from tests.test_gpu_moe_combine import run_combine
+    S, T, H, N, E, E_loc, top_k = 2, 256, 64, 64, 8, 8, 2
+    print(f"moe withheld unit, combine={combine}", flush=True)
+    d = I.gen_moe(S, T, H, N, E, E_loc, I.INTEGER, config=470)
+    run = run_combine if combine else run_moe
+    monkeypatch.setenv("MK_TEST_MOE_WITHHOLD", "1")   # route item 0, second token part
+    with mk.Handle(0, spin_timeout_ms=50) as h:
+        for _ in range(2):
+            with pytest.raises(mk.MkError) as ei:
+                run(h, d, E, top_k, rank=0)
+            assert ei.value.status == mk.MK_ERR_TIMEOUT
+            h.sync()                                  # the error record was cleared
+    monkeypatch.delenv("MK_TEST_MOE_WITHHOLD")
+    with mk.Handle(0) as h:
+        out = run_moe(h, d, E, top_k, rank=0)
+        check_moe(d, out, top_k, 0, I.INTEGER)
+
+
 def test_invalid_arguments_launch_nothing(mk):
     d = I.gen_ag(2, 64, 64, 64, I.FLOAT, config=501)
     shards, bt, c, ag = _ag_buffers(d)
