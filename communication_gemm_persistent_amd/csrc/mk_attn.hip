@@ -116,7 +116,6 @@ __device__ __forceinline__ void attn_land_item(const AttnParams &p, int item, ch
 __device__ __forceinline__ float xor_max(float v, int m) {
   return fmaxf(v, __shfl_xor(v, m, 64));
 }
-__device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m, 64); }
 
 __device__ __forceinline__ bf16x8_t pack_p(const f32x4_t &a, const f32x4_t &b) {
   const uint2 lo = pack_bf16x4(a[0], a[1], a[2], a[3]);
@@ -158,13 +157,18 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
       qf[mb][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-  f32x4_t oacc[2][8];
+  // O in oacc[mb][0..7]; oacc[mb][8] is the P row sum: the P V product's
+  // ninth d-block multiplies P by a block of ones, so the sum comes out of the
+  // matrix core (of the bf16 P the O rows are built from), is rescaled with
+  // O, and every lane holds its query row's sum
+  f32x4_t oacc[2][9];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int db = 0; db < 8; ++db) oacc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < 9; ++db) oacc[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mrow[2] = {-INFINITY, -INFINITY};  // running row max (log2 domain)
-  float lpart[2] = {0.f, 0.f};             // this lane's part of the row sum
+  const bf16x8_t ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
   // DMA lane offsets (8-row groups, 64-wide rows, swizzled as the GEMM tiles).
   // K: LDS row 8 gl + rs (rs = lane >> 3) holds key kperm(gl) + 8 (rs >> 2) + (rs & 3)
@@ -293,9 +297,8 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
       mrow[mb] = mnew[mb];
       if (__any(mnew[mb] > mold)) {
         const float alpha = __builtin_amdgcn_exp2f(mold - mnew[mb]);
-        lpart[mb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
+        for (int db = 0; db < 9; ++db) {
           oacc[mb][db][0] *= alpha; oacc[mb][db][1] *= alpha;
           oacc[mb][db][2] *= alpha; oacc[mb][db][3] *= alpha;
         }
@@ -309,16 +312,10 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
     bf16x8_t pf[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      float sum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][kb][r], c, -mnew[mb]));
-          sacc[mb][kb][r] = e;
-          sum += e;
-        }
-      lpart[mb] += sum;
+        for (int r = 0; r < 4; ++r) sacc[mb][kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][kb][r], c, -mnew[mb]));
       pf[mb][0] = pack_p(sacc[mb][0], sacc[mb][1]);
       pf[mb][1] = pack_p(sacc[mb][2], sacc[mb][3]);
     }
@@ -336,6 +333,10 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
         for (int mb = 0; mb < 2; ++mb) oacc[mb][db] = mfma16(vf, pf[mb][kk], oacc[mb][db]);
       }
     }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) oacc[mb][8] = mfma16(ones, pf[mb][kk], oacc[mb][8]);
     row_max(snext, tmax);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -344,10 +345,11 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
     wait_vmcnt<0>();  // this wave's DMAs of K(j+2) and V(j+1)
   }
   wg_barrier();  // both buffers are free for the next task
-  // row sums over the 4 lane groups; then store, or combine with the other half
+  // the row sums (every lane holds its row's); then store, or combine with
+  // the other half
   float lrow[2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) lrow[mb] = xor_sum(xor_sum(lpart[mb], 16), 32);
+  for (int mb = 0; mb < 2; ++mb) lrow[mb] = oacc[mb][8][0];
   if (p.splits == 2) {
     // (bh, qt) pair: the first half to finish writes its unnormalised O, row
     // max and row sum and releases the pair's flag; the second combines.
