@@ -434,6 +434,11 @@ template <int DUMMY>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kAttnLds];
   __shared__ uint32_t s_word;
+  // the task loop reads its parameters from an LDS copy: LDS reads are
+  // reloaded where they are used, so no parameter stays live in (spilled)
+  // scalar registers around the tile loop's DMAs
+  __shared__ AttnParams s_prm;
+  copy_params(&s_prm, p);  // take_ticket's barrier publishes the copy
   const uint32_t ticket = take_ticket(p.sync, &s_word);
   Ctrl *ctrl = p.sync.ctrl;
   if (ticket < (uint32_t)p.n_land) {
@@ -444,18 +449,35 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnParams p) {
     }
   }
   // land workgroups join once landing is done, unless the launch lands only
-  if (ticket < (uint32_t)p.n_compute + (p.n_compute > 0 ? (uint32_t)p.n_land : 0u)) {
+  const AttnParams &q = s_prm;
+  if (ticket < (uint32_t)q.n_compute + (q.n_compute > 0 ? (uint32_t)q.n_land : 0u)) {
     for (;;) {
-      // query-tile-major: the tasks running together cover every head and
-      // consume the ring's blocks in the order they land
-      const uint32_t t = next_index(&ctrl->tile_ctr, &s_word);
-      if (t >= (uint32_t)p.n_tasks) break;
-      // every first half before any second half: the first round covers the
-      // early ring steps, and the late steps have longer to land
-      const int half = (int)(t / (uint32_t)p.n_pairs), pair = (int)(t % (uint32_t)p.n_pairs);
-      const int n_tiles = p.world * (p.S_kv / kAttnKT);
-      const int j0 = half * n_tiles / p.splits, j1 = (half + 1) * n_tiles / p.splits;
-      if (!attn_task(p, pair % p.BH, pair / p.BH, j0, j1, smem, &s_word)) break;
+      // Every first half before any second half: the first round covers the
+      // early ring steps, and the late steps have longer to land.  Within a
+      // half, the tasks running together cover every head and consume the
+      // ring's blocks in the order they land.  With an XCD map (the default)
+      // each XCD takes a block of heads, so the query tiles of one head that
+      // run at once stream the same K and V^T tiles through one L2; the
+      // global order runs query tiles head by head over the whole chip.
+      int bh, qt, half;
+      if (q.tile_map == kMapGlobal) {
+        const uint32_t t = next_index(&q.sync.ctrl->tile_ctr, &s_word);
+        if (t >= (uint32_t)q.n_tasks) break;
+        half = (int)(t / (uint32_t)q.n_pairs);
+        const int pair = (int)(t % (uint32_t)q.n_pairs);
+        bh = pair % q.BH;
+        qt = pair / q.BH;
+      } else {
+        const int tn = q.splits * q.q_tiles;  // tasks per head: (half, query tile)
+        const int t = next_tile(q.sync, q.BH, tn, xcd_id(), TileOrder{q.tile_map, 1, 1}, &s_word);
+        if (t < 0) break;
+        bh = t / tn;
+        half = (t % tn) / q.q_tiles;
+        qt = (t % tn) % q.q_tiles;
+      }
+      const int n_tiles = q.world * (q.S_kv / kAttnKT);
+      const int j0 = half * n_tiles / q.splits, j1 = (half + 1) * n_tiles / q.splits;
+      if (!attn_task(p, bh, qt, j0, j1, smem, &s_word)) break;
     }
   }
   finish_launch(p.sync);

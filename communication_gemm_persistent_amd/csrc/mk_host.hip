@@ -1122,6 +1122,8 @@ mk_status mk_ring_attention(mk_handle h, mk_stream stream, int world, int rank, 
   const long n_tiles = (long)world * (S_kv / 64);
   p.splits = (h->ring_splits != 1 && n_tiles >= 2 && (long)p.n_items + p.n_pairs <= mk::kMaxFlags) ? 2 : 1;
   p.n_tasks = p.splits * p.n_pairs;
+  p.tile_map = h->tile_map >= 0 ? h->tile_map : mk::kMapBlocks;
+  if (p.tile_map == mk::kMapRounds) p.tile_map = mk::kMapBlocks;  // no rounds order for tasks
   p.merge_flag0 = (uint32_t)p.n_items;
   if (p.splits == 2) {
     const size_t slot = (size_t)(128 * 128 + 2 * 128) * sizeof(float);

@@ -113,6 +113,7 @@ struct AttnParams {
   int splits, n_pairs;                    // tasks per (bh, q-tile) pair: 1, or 2 ring halves
   uint32_t merge_flag0;                   // flag / counter of pair i: merge_flag0 + i
   float *ws;                              // splits == 2: one combine slot per pair
+  int tile_map;                           // task order: kMapGlobal, or an XCD map over heads
 };
 
 // MoE dispatch + grouped GEMM.  Route items are blocks of kRouteTokens
