@@ -430,6 +430,41 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
   return true;
 }
 
+// Next task of the XCD-blocked order as (bh, half, qt), or bh = -1 when none
+// is left (all threads get the value).  XCD x owns heads [x BH / 8,
+// (x+1) BH / 8); its queue runs half by half, and within a half head by
+// head with the query tiles of a head consecutive, so the tasks an XCD runs
+// at once share the fewest K and V^T streams in its L2.  A workgroup drains
+// its own XCD's queue first, then the others in turn.
+__device__ __forceinline__ int attn_next_task(const AttnParams &q, int xcd, uint32_t *lds_word, int *half,
+                                              int *qt) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int r = -1;
+    for (int k = 0; k < kXcds && r < 0; ++k) {
+      const int x = (xcd + k) & (kXcds - 1);
+      const int lo = x * q.BH / kXcds, mc = (x + 1) * q.BH / kXcds - lo;
+      const uint32_t size = (uint32_t)(mc * q.splits * q.q_tiles);
+      uint32_t *ctr = &q.sync.ctrl->xq[x * 16];
+      if (size == 0 || ld_relaxed(ctr) >= size) continue;
+      const uint32_t i = add_relaxed(ctr, 1u);
+      if (i < size) {
+        const int per_half = mc * q.q_tiles;
+        const int hf = (int)i / per_half, rem = (int)i % per_half;
+        r = ((lo + rem / q.q_tiles) * q.splits + hf) * q.q_tiles + rem % q.q_tiles;
+      }
+    }
+    *lds_word = (uint32_t)r;
+  }
+  __syncthreads();
+  const int r = (int)uniform(*lds_word);
+  if (r >= 0) {
+    *qt = r % q.q_tiles;
+    *half = (r / q.q_tiles) % q.splits;
+  }
+  return r < 0 ? -1 : r / (q.q_tiles * q.splits);
+}
+
 template <int DUMMY>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kAttnLds];
@@ -453,12 +488,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnParams p) {
   if (ticket < (uint32_t)q.n_compute + (q.n_compute > 0 ? (uint32_t)q.n_land : 0u)) {
     for (;;) {
       // Every first half before any second half: the first round covers the
-      // early ring steps, and the late steps have longer to land.  Within a
-      // half, the tasks running together cover every head and consume the
-      // ring's blocks in the order they land.  With an XCD map (the default)
-      // each XCD takes a block of heads, so the query tiles of one head that
-      // run at once stream the same K and V^T tiles through one L2; the
-      // global order runs query tiles head by head over the whole chip.
+      // early ring steps, and the late steps have longer to land; the tasks
+      // running together consume the ring's blocks in the order they land.
+      // By default each XCD takes a block of heads and runs a head's query
+      // tiles together (attn_next_task), so they stream the same K and V^T
+      // tiles through one L2; the global order (MK_TILE_MAP=0) runs the
+      // query tiles of every head at once over the whole chip.
       int bh, qt, half;
       if (q.tile_map == kMapGlobal) {
         const uint32_t t = next_index(&q.sync.ctrl->tile_ctr, &s_word);
@@ -468,12 +503,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnParams p) {
         bh = pair % q.BH;
         qt = pair / q.BH;
       } else {
-        const int tn = q.splits * q.q_tiles;  // tasks per head: (half, query tile)
-        const int t = next_tile(q.sync, q.BH, tn, xcd_id(), TileOrder{q.tile_map, 1, 1}, &s_word);
-        if (t < 0) break;
-        bh = t / tn;
-        half = (t % tn) / q.q_tiles;
-        qt = (t % tn) % q.q_tiles;
+        bh = attn_next_task(q, xcd_id(), &s_word, &half, &qt);
+        if (bh < 0) break;
       }
       const int n_tiles = q.world * (q.S_kv / kAttnKT);
       const int j0 = half * n_tiles / q.splits, j1 = (half + 1) * n_tiles / q.splits;
