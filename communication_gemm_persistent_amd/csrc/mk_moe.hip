@@ -426,6 +426,31 @@ __device__ __forceinline__ void moe_land_queue(const MoeParams &p, MoeShared &sh
   }
 }
 
+// Next grouped-GEMM tile as rt * tiles_n + nb, or -1 when none is left (all
+// threads get the value).  XCD x owns the row tiles of local experts
+// [x E_loc / 8, (x+1) E_loc / 8), so the tiles one XCD runs at once share
+// their expert's weights in its L2; within an XCD every owned row tile of
+// n-block 0 comes first, then n-block 1, ...  A workgroup drains its own
+// XCD's queue first, then the others in turn.
+__device__ __forceinline__ int moe_next_tile(const MoeParams &p, const MoeShared &sh, int xcd, uint32_t *lds_word) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int r = -1;
+    for (int k = 0; k < kXcds && r < 0; ++k) {
+      const int x = (xcd + k) & (kXcds - 1);
+      const int lo = sh.tile_base[x * p.E_loc / kXcds], mc = sh.tile_base[(x + 1) * p.E_loc / kXcds] - lo;
+      const uint32_t size = (uint32_t)(mc * p.tiles_n);
+      uint32_t *ctr = &p.sync.ctrl->xq[x * 16];
+      if (size == 0 || ld_relaxed(ctr) >= size) continue;
+      const uint32_t i = add_relaxed(ctr, 1u);
+      if (i < size) r = (lo + (int)(i % (uint32_t)mc)) * p.tiles_n + (int)(i / (uint32_t)mc);
+    }
+    *lds_word = (uint32_t)r;
+  }
+  __syncthreads();
+  return (int)uniform(*lds_word);
+}
+
 template <int BM, int BN>
 __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeShared &sh) {
   using C = TileCfg<BM, BN>;
@@ -435,7 +460,8 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
   const int ld = p.H * 2;
   const int xcd = xcd_id();
   for (;;) {
-    const int t = next_tile(p.sync, n_row_tiles, p.tiles_n, xcd, TileOrder{p.tile_map, 1, 1}, &sh.word);
+    const int t = p.tile_map == kMapBlocks ? moe_next_tile(p, sh, xcd, &sh.word)
+                                           : next_tile(p.sync, n_row_tiles, p.tiles_n, xcd, TileOrder{p.tile_map, 1, 1}, &sh.word);
     if (t < 0) break;
     const int rt = (int)t / p.tiles_n, nb = (int)t % p.tiles_n;
     // row tile rt is tile mt of the last expert e whose first row tile is <= rt

@@ -154,7 +154,7 @@ struct MoeParams {
   int items_per_src, n_items;
   int n_land, n_compute;
   int tiles_n;
-  int tile_map;         // kMapBlocks: XCD x takes a contiguous block of row tiles (about one expert)
+  int tile_map;         // kMapBlocks: XCD x takes the row tiles of a block of local experts
   int no_gate;
   int static_roles;     // land workgroups do not take tiles
   int withhold;         // failure tests: land unit never landed (-1: none), so its waiters time out
