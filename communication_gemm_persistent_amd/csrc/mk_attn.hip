@@ -44,11 +44,8 @@ constexpr int kAttnKHalf = kAttnKT * 128;
 constexpr int kAttnVOff = 2 * kAttnKHalf;
 constexpr int kAttnStage = kAttnVOff + kAttnD * 128;
 constexpr int kAttnLds = 2 * kAttnStage;
-// land transpose tile: [128 d][64 keys] with a 132-byte pitch
-constexpr int kAttnTPitch = 132;
 // workspace slot of a (bh, qt) pair: unnormalised O [128][128], row max, row sum
 constexpr int kAttnSlot = kAttnQ * kAttnD + 2 * kAttnQ;
-static_assert(kAttnD * kAttnTPitch <= kAttnLds, "transpose tile fits the staging area");
 static_assert(kAttnD == 128, "the task layout assumes 128-wide heads");
 
 
@@ -60,7 +57,7 @@ __device__ __forceinline__ uint32_t attn_flag(const AttnParams &p, int src, int 
   return (uint32_t)((src * p.BH + bh) * p.chunks + c);
 }
 
-__device__ __forceinline__ void attn_land_item(const AttnParams &p, int item, char *smem) {
+__device__ __forceinline__ void attn_land_item(const AttnParams &p, int item) {
   const int per_step = p.BH * p.chunks;
   const int s = item / per_step, rem = item % per_step;
   const int src = (p.rank - s + p.world) % p.world;
@@ -80,31 +77,32 @@ __device__ __forceinline__ void attn_land_item(const AttnParams &p, int item, ch
     }
     for (; i < n16; i += kAttnThreads) dp[i] = sp[i];
   }
-  // V: transposed through LDS, 64 keys at a time
-  const uint16_t *vsrc = p.v_src[src] + (size_t)bh * p.S_kv * kAttnD;
-  uint16_t *vdst = p.vt_recv + ((size_t)src * p.BH + bh) * kAttnD * p.S_kv;
-  for (int k0 = key0; k0 < key0 + nk; k0 += kAttnKT) {
-    // read: 16 lanes per key row (coalesced), 8 d values each
-    for (int i = tid; i < kAttnKT * 16; i += kAttnThreads) {
-      const int key = i >> 4, dc = i & 15;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(vsrc + (size_t)(k0 + key) * kAttnD + dc * 8);
+  // V: transposed in registers, one 8-key x 8-d block per thread and step:
+  // eight 16-byte loads (one key's 8 d values each, 16 threads per 256-byte
+  // key row) become eight 16-byte rows of V^T (8 keys each) by byte
+  // permutes -- the low halves of two keys' words form one d row, the high
+  // halves the next
+  const uint16_t *vsrc = p.v_src[src] + ((size_t)bh * p.S_kv + key0) * kAttnD;
+  uint16_t *vdst = p.vt_recv + ((size_t)src * p.BH + bh) * kAttnD * p.S_kv + key0;
+  const int nblk = (nk / 8) * (kAttnD / 8);
+#pragma unroll 2
+  for (int b = tid; b < nblk; b += kAttnThreads) {
+    const int kg = b / (kAttnD / 8), dg = b % (kAttnD / 8);
+    u32x4_t in[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      in[i] = *reinterpret_cast<const u32x4_t *>(vsrc + (size_t)(kg * 8 + i) * kAttnD + dg * 8);
+#pragma unroll
+    for (int cw = 0; cw < 4; ++cw) {  // word cw holds d = 8 dg + 2 cw (low half) and + 1 (high half)
+      u32x4_t lo, hi;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        *reinterpret_cast<uint16_t *>(smem + (dc * 8 + 2 * q) * kAttnTPitch + key * 2) = (uint16_t)v[q];
-        *reinterpret_cast<uint16_t *>(smem + (dc * 8 + 2 * q + 1) * kAttnTPitch + key * 2) =
-            (uint16_t)(v[q] >> 16);
+        lo[q] = __builtin_amdgcn_perm(in[2 * q + 1][cw], in[2 * q][cw], 0x05040100u);
+        hi[q] = __builtin_amdgcn_perm(in[2 * q + 1][cw], in[2 * q][cw], 0x07060302u);
       }
+      *reinterpret_cast<u32x4_t *>(vdst + (size_t)(dg * 8 + 2 * cw) * p.S_kv + kg * 8) = lo;
+      *reinterpret_cast<u32x4_t *>(vdst + (size_t)(dg * 8 + 2 * cw + 1) * p.S_kv + kg * 8) = hi;
     }
-    __syncthreads();
-    // write: one 16-byte piece (8 keys) of a V^T row per item
-    for (int i = tid; i < kAttnD * (kAttnKT / 8); i += kAttnThreads) {
-      const int d = i >> 3, kc = i & 7;
-      const uint32_t *l = reinterpret_cast<const uint32_t *>(smem + d * kAttnTPitch + kc * 16);
-      u32x4_t w;
-      w[0] = l[0]; w[1] = l[1]; w[2] = l[2]; w[3] = l[3];
-      *reinterpret_cast<u32x4_t *>(vdst + (size_t)d * p.S_kv + k0 + kc * 8) = w;
-    }
-    __syncthreads();
   }
   wait_stores();
   __syncthreads();
@@ -480,7 +478,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnParams p) {
     for (;;) {
       const uint32_t it = next_index(&ctrl->land_ctr, &s_word);
       if (it >= (uint32_t)p.n_items) break;
-      attn_land_item(p, (int)it, smem);
+      attn_land_item(p, (int)it);
     }
   }
   // land workgroups join once landing is done, unless the launch lands only
