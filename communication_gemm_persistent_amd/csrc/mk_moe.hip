@@ -68,7 +68,104 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 // ---------------------------------------------------------------- route
 
+// Route item `item` with two lanes per token (E = 64, top-2, 512 threads):
+// lane h of token tt reads logits 32h .. 32h+31 and keeps its top-2; the
+// pair merges the two lists (both lanes get the same result, the order of
+// (logit descending, expert ascending) being strict) and adds its softmax
+// sums; lane h then owns selection h -- its expert, gate and rank -- so
+// every routing output is one store per lane.  Half the loads, compares and
+// exponentials per lane of the one-lane-per-token form.
+__device__ __forceinline__ void moe_route_item_pairs(const MoeParams &p, int item, MoeShared &sh) {
+  const int s = item / p.items_per_src, b = item % p.items_per_src;
+  const int tt = (int)threadIdx.x >> 1, h = (int)threadIdx.x & 1;
+  const int t = b * kRouteTokens + tt;
+  const bool valid = t < p.T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr float kLog2e = 1.4426950408889634f;
+  f32x4_t l[8];
+  int i0 = -1, i1 = -1;
+  float v0 = 0.f, v1 = 0.f;
+  if (valid) {
+    const f32x4_t *lg = reinterpret_cast<const f32x4_t *>(p.logits[s] + (size_t)t * 64 + h * 32);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) l[q] = lg[q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float v = l[q][u];
+        const int e = h * 32 + q * 4 + u;
+        if (i0 < 0 || v > v0) {
+          i1 = i0; v1 = v0;
+          i0 = e; v0 = v;
+        } else if (i1 < 0 || v > v1) {
+          i1 = e; v1 = v;
+        }
+      }
+  }
+  // merge with the partner lane's list (every lane takes part in the shuffles)
+  const float pv0 = __shfl_xor(v0, 1, 64), pv1 = __shfl_xor(v1, 1, 64);
+  const int pi0 = __shfl_xor(i0, 1, 64), pi1 = __shfl_xor(i1, 1, 64);
+  auto better = [](float va, int ia, float vb, int ib) { return va > vb || (va == vb && ia < ib); };
+  int s0, s1;
+  float w0, w1;
+  if (better(v0, i0, pv0, pi0)) {
+    s0 = i0; w0 = v0;
+    if (better(v1, i1, pv0, pi0)) { s1 = i1; w1 = v1; } else { s1 = pi0; w1 = pv0; }
+  } else {
+    s0 = pi0; w0 = pv0;
+    if (better(v0, i0, pv1, pi1)) { s1 = i0; w1 = v0; } else { s1 = pi1; w1 = pv1; }
+  }
+  // softmax terms as exp2(l log2(e) - max log2(e)): one fma and one
+  // v_exp_f32 each; the pair adds its two partial sums
+  const float mxl = w0 * kLog2e;
+  float sum = 0.f;
+  if (valid) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(l[q][u], kLog2e, -mxl));
+  }
+  sum += __shfl_xor(sum, 1, 64);
+  const int my_e = h == 0 ? s0 : s1;
+  const float my_gate = __builtin_amdgcn_exp2f(__builtin_fmaf(h == 0 ? w0 : w1, kLog2e, -mxl)) / sum;
+  // per local expert: count and rank of this item's tokens (token order:
+  // lanes are token-major, and a token's two lanes never share an expert)
+  const int e_lo = p.rank * p.E_loc;
+  int my_rank = -1;
+  for (int e = 0; e < p.E_loc; ++e) {
+    const bool mine = valid && my_e == e_lo + e;
+    const uint64_t m = __ballot(mine);
+    if (mine) my_rank = __popcll(m & lanemask_lt());
+    if (lane == 0) sh.wave_cnt[wave][e] = __popcll(m);
+  }
+  __syncthreads();
+  if (my_rank >= 0) {
+    const int e = my_e - e_lo;
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += sh.wave_cnt[w][e];
+    my_rank += before;
+  }
+  // every routing output in one batch of write-through stores
+  if (valid) {
+    const size_t o = ((size_t)s * p.T + t) * 2 + h;
+    st_through(&p.topk_idx[o], (int32_t)my_e);
+    st_through(&p.topk_gate[o], my_gate);
+    st_through(&p.tok_rank[o], (int32_t)my_rank);
+  }
+  if (threadIdx.x < (unsigned)p.E_loc) {
+    int tot = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += sh.wave_cnt[w][threadIdx.x];
+    st_through(&p.item_cnt[(size_t)item * p.E_loc + threadIdx.x], (int32_t)tot);
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ void moe_route_item(const MoeParams &p, int item, MoeShared &sh) {
+  if (p.E == 64 && p.top_k == 2 && blockDim.x == 2 * kRouteTokens) {
+    moe_route_item_pairs(p, item, sh);
+    return;
+  }
   const int s = item / p.items_per_src, b = item % p.items_per_src;
   // one token per thread; threads past kRouteTokens only join the counts
   const int t = b * kRouteTokens + (int)threadIdx.x;

@@ -130,6 +130,28 @@ def test_moe_e64_routing_with_ties(handle, top_k):
     check_moe(d, out, top_k, 0, I.FLOAT)
 
 
+@pytest.mark.parametrize("variant", [I.FLOAT, I.INTEGER])
+def test_moe_e64_top2_pair_routing_with_ties(mk, monkeypatch, variant):
+    """E = 64, top-2 on the 256-row kernel (MK_TILE=256 forces it at this
+    size) routes each token with two lanes whose top-2 lists merge; forced
+    ties at the top, across the two lanes' halves of the logits (experts 31
+    and 32) and among all 64 experts keep the lower expert id first."""
+    S, T, H, N, E, E_loc, top_k = 2, 700, 64, 64, 64, 8, 2
+    print(f"moe pair routing with ties, variant={variant}", flush=True)
+    d = I.gen_moe(S, T, H, N, E, E_loc, variant, config=445)
+    for s in range(S):
+        lg = d["logits"][s]
+        top = lg.max(axis=1)
+        lg[::3, 5] = lg[::3, 6] = top[::3] + 1.0      # tie at the top, one lane
+        lg[1::4, 31] = lg[1::4, 32] = top[1::4] + 2.0  # tie across the lanes' halves
+        lg[2::5, 40] = lg[2::5, 3] = top[2::5] + 1.5   # tie, higher id in the other lane
+        lg[3::7, :] = 0.25                              # all equal
+    monkeypatch.setenv("MK_TILE", "256")
+    with mk.Handle(0, spin_timeout_ms=10000) as h:
+        out = run_moe(h, d, E, top_k, rank=0)
+    check_moe(d, out, top_k, 0, variant)
+
+
 @pytest.mark.parametrize("roles,static", [((1, -1), False), ((1, 3), False), ((4, 60), False),
                                           ((4, 60), True), ((1, 3), True)])
 def test_moe_role_splits_bit_identical(handle, mk, roles, static):
