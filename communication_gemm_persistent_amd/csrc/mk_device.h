@@ -722,9 +722,10 @@ __device__ __forceinline__ void interleave_reads_and_mfmas() {
 }
 
 // Run the K loop of one tile with every wave doing both jobs (tiles of
-// four waves, one per SIMD).  va covers rows [m0, m0 + valid_m) of A with
-// row pitch lda_bytes; vb rows [n0, n0 + valid_n) of Bt.  smem holds two
-// stages.  On return the accumulators hold the tile and smem is free.
+// four waves, one per SIMD).  va covers rows [m0, m0 + valid_m) of A, vb
+// rows [n0, n0 + valid_n) of Bt; both hold K-contiguous rows of pitch
+// ld_bytes.  smem holds two stages.  On return the accumulators hold the
+// tile and smem is free.
 //
 // Pipeline (per 64-wide K stage kb, 4 substeps of 16):
 //   substeps 0..2: read the next substep's fragments, MFMAs of this one
@@ -736,7 +737,7 @@ __device__ __forceinline__ void interleave_reads_and_mfmas() {
 // to land.
 template <int BM, int BN>
 __device__ __forceinline__ void gemm_tile_interleaved(
-    char *smem, i32x4_t va, int lda_bytes, i32x4_t vb, int ldb_bytes, int K, AccTile<BM, BN> &acc) {
+    char *smem, i32x4_t va, i32x4_t vb, int ld_bytes, int K, AccTile<BM, BN> &acc) {
   using C = TileCfg<BM, BN>;
   static_assert(C::MFMA == 32, "substep pipeline of the 32x32 MFMA tiles");
   const int lane = threadIdx.x & 63;
@@ -749,11 +750,11 @@ __device__ __forceinline__ void gemm_tile_interleaved(
 
   const uint32_t base = lds_addr(smem);
   const int nk = (K + kBK - 1) / kBK;
-  stage_operand<BM, C::WAVES>(va, base, lda_bytes, 0, K, wave, lane);
-  stage_operand<BN, C::WAVES>(vb, base + C::A_BYTES, ldb_bytes, 0, K, wave, lane);
+  stage_operand<BM, C::WAVES>(va, base, ld_bytes, 0, K, wave, lane);
+  stage_operand<BN, C::WAVES>(vb, base + C::A_BYTES, ld_bytes, 0, K, wave, lane);
   if (nk > 1) {
-    stage_operand<BM, C::WAVES>(va, base + C::STAGE_BYTES, lda_bytes, kBK, K, wave, lane);
-    stage_operand<BN, C::WAVES>(vb, base + C::STAGE_BYTES + C::A_BYTES, ldb_bytes, kBK, K, wave, lane);
+    stage_operand<BM, C::WAVES>(va, base + C::STAGE_BYTES, ld_bytes, kBK, K, wave, lane);
+    stage_operand<BN, C::WAVES>(vb, base + C::STAGE_BYTES + C::A_BYTES, ld_bytes, kBK, K, wave, lane);
     wait_vmcnt<C::LOADS>();
   } else {
     wait_vmcnt<0>();
@@ -781,8 +782,8 @@ __device__ __forceinline__ void gemm_tile_interleaved(
     wg_barrier();
     if (kb + 2 < nk) {
       const uint32_t dst = base + (kb & 1) * C::STAGE_BYTES;
-      stage_operand<BM, C::WAVES>(va, dst, lda_bytes, (kb + 2) * kBK, K, wave, lane);
-      stage_operand<BN, C::WAVES>(vb, dst + C::A_BYTES, ldb_bytes, (kb + 2) * kBK, K, wave, lane);
+      stage_operand<BM, C::WAVES>(va, dst, ld_bytes, (kb + 2) * kBK, K, wave, lane);
+      stage_operand<BN, C::WAVES>(vb, dst + C::A_BYTES, ld_bytes, (kb + 2) * kBK, K, wave, lane);
     }
     load_frags<BM, BN>(f0, smem + ((kb + 1) & 1) * C::STAGE_BYTES, 0, wm, wn, lane);
     mma_frags<BM, BN>(f1, acc);
@@ -873,7 +874,7 @@ struct SlabGate {
 // every iteration; they are drained at the end.
 template <int BM, int BN>
 __device__ __forceinline__ void gemm_tile_pingpong(
-    char *smem, i32x4_t va, int lda_bytes, i32x4_t vb, int ldb_bytes, int K, AccTile<BM, BN> &acc,
+    char *smem, i32x4_t va, i32x4_t vb, int ld_bytes, int K, AccTile<BM, BN> &acc,
     const SlabGate &gate) {
   using C = TileCfg<BM, BN>;
   constexpr int G = 4;                                // waves per group
@@ -895,7 +896,7 @@ __device__ __forceinline__ void gemm_tile_pingpong(
 
   const uint32_t base = lds_addr(smem);
   const int nk = (K + kBK - 1) / kBK;
-  const int ld = lda_bytes;  // every caller passes equal pitches (2 K bytes)
+  const int ld = ld_bytes;
   const int rg = wave * R;   // first owned row group (= 16 group + 4 index)
   const uint32_t lane_off[2] = {(uint32_t)((lane >> 3) * ld + dma_chunk(lane, 0) * 16),
                                 (uint32_t)((lane >> 3) * ld + dma_chunk(lane, 1) * 16)};
@@ -1009,16 +1010,18 @@ __device__ __forceinline__ void gemm_tile_pingpong(
   wg_barrier();  // every wave is done reading; the caller may refill either stage
 }
 
-// A tile's K loop.  gate applies to the 8-wave tile only; a caller using
-// the 4-wave tile waits for all of its A rows before calling.
+// A tile's K loop over K-contiguous operand rows of pitch ld_bytes (A and
+// Bt both hold K bf16 values per row).  gate applies to the 8-wave tile
+// only; a caller using the 4-wave tile waits for all of its A rows before
+// calling.
 template <int BM, int BN>
-__device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, int lda_bytes, i32x4_t vb,
-                                          int ldb_bytes, int K, AccTile<BM, BN> &acc,
+__device__ __forceinline__ void gemm_tile(char *smem, i32x4_t va, i32x4_t vb, int ld_bytes, int K,
+                                          AccTile<BM, BN> &acc,
                                           const SlabGate &gate = SlabGate{nullptr, 0u, 0}) {
   if constexpr (TileCfg<BM, BN>::WAVES == 8)
-    gemm_tile_pingpong<BM, BN>(smem, va, lda_bytes, vb, ldb_bytes, K, acc, gate);
+    gemm_tile_pingpong<BM, BN>(smem, va, vb, ld_bytes, K, acc, gate);
   else
-    gemm_tile_interleaved<BM, BN>(smem, va, lda_bytes, vb, ldb_bytes, K, acc);
+    gemm_tile_interleaved<BM, BN>(smem, va, vb, ld_bytes, K, acc);
 }
 
 // Position of accumulator group g (4 consecutive columns) of block (i, j).

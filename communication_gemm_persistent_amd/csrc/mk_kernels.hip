@@ -203,9 +203,9 @@ __device__ __forceinline__ void ag_compute(const AgParams &p, char *smem, uint32
     // two instantiations of the K loop: with a gate it is longer and holds
     // more registers, so tiles that need no in-loop check run the plain one
     if (gated)
-      gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc, gate);
+      gemm_tile<BM, BN>(smem, ra, rb, ldb, p.k, acc, gate);
     else
-      gemm_tile<BM, BN>(smem, ra, ldb, rb, ldb, p.k, acc);
+      gemm_tile<BM, BN>(smem, ra, rb, ldb, p.k, acc);
     staged_epilogue<BM, BN>(acc, smem, [&](int r, int cc, const f32x4_t &v) {
       const int row = m0 + r, col = n0 + cc;
       if (row < m1 && col < p.n) store_nt(p.c + (size_t)row * p.n + col, pack_bf16x4(v[0], v[1], v[2], v[3]));
@@ -500,7 +500,6 @@ __device__ __forceinline__ void rs_reduce_item(const RsParams &p, const PtrTable
 template <int BM, int BN>
 __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &tab, char *smem,
                                            uint32_t *s_word) {
-  using C = TileCfg<BM, BN>;
   const int xcd = xcd_id();
   const int lda = p.k * 2;
   // what the epilogues add to the own slice: the peers' partials, or their
@@ -519,7 +518,7 @@ __device__ __forceinline__ void rs_compute(const RsParams &p, const PtrTable &ta
     const i32x4_t ra = make_vdesc(p.a + (size_t)m0 * p.k, (uint32_t)((m1 - m0) * lda));
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * lda));
     AccTile<BM, BN> acc;
-    gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
+    gemm_tile<BM, BN>(smem, ra, rb, lda, p.k, acc);
     // the reduce item of this tile's own-slice rows (worked out after the K
     // loop: values held across it cost registers the loop needs)
     if (red && m0 < hi && m1 > lo &&
@@ -634,7 +633,6 @@ __device__ __forceinline__ void ar_reduce_item(const ArParams &p, const PtrTable
 template <int BM, int BN>
 __device__ __forceinline__ void ar_compute(const ArParams &p, const PtrTable &tab, char *smem,
                                            uint32_t *s_word) {
-  using C = TileCfg<BM, BN>;
   const int xcd = xcd_id();
   const int lda = p.k * 2;
   const bool red = p.red.n_items > 0;
@@ -649,7 +647,7 @@ __device__ __forceinline__ void ar_compute(const ArParams &p, const PtrTable &ta
     const i32x4_t ra = make_vdesc(p.a + (size_t)m0 * p.k, (uint32_t)((m1 - m0) * lda));
     const i32x4_t rb = make_vdesc(p.bt + (size_t)n0 * p.k, (uint32_t)(valid_n * lda));
     AccTile<BM, BN> acc;
-    gemm_tile<BM, BN>(smem, ra, lda, rb, lda, p.k, acc);
+    gemm_tile<BM, BN>(smem, ra, rb, lda, p.k, acc);
     if (red && !red_wait(p.sync, (uint32_t)((m0 / BM) * p.tiles_n + n0 / BN), p.red.light_acquire != 0, s_word))
       break;
     const int cols = min(BN, p.n - n0);

@@ -550,7 +550,6 @@ __device__ __forceinline__ int moe_next_tile(const MoeParams &p, const MoeShared
 
 template <int BM, int BN>
 __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeShared &sh) {
-  using C = TileCfg<BM, BN>;
   if (threadIdx.x < (unsigned)MK_MAX_WORLD) sh.ret_ptr[threadIdx.x] = p.ret[threadIdx.x];
   __syncthreads();
   const int n_row_tiles = (int)uniform((uint32_t)sh.tile_base[p.E_loc]);
@@ -600,7 +599,7 @@ __device__ __forceinline__ void moe_compute(const MoeParams &p, char *smem, MoeS
       sh.tile_ret_row[threadIdx.x] = rrow;
     }
     AccTile<BM, BN> acc;
-    gemm_tile<BM, BN>(smem, ra, ld, rb, ld, p.H, acc);
+    gemm_tile<BM, BN>(smem, ra, rb, ld, p.H, acc);
     // y = bf16(gate * acc) row by row through LDS (whole-row stores); a row
     // of a remote token is also stored to its source's return buffer
     const int rows = slot1 - slot0;
