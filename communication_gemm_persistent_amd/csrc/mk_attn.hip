@@ -181,44 +181,65 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
   // this wave's DMAs of a tile: K half (wave >> 1), row groups 4 (wave & 1) ..
   // +3; V^T row groups 4 wave .. +3.  K and V^T of tile t go to the K and V
   // parts of stage t & 1, K one tile ahead of V (see the loop below).
-  auto block_of = [&](int j) {
-    const int src = (p.rank - j / tpb + p.world) % p.world;
-    return (size_t)src * p.BH + bh;
+  // Ring position of a tile, advanced tile by tile so the loop divides
+  // nothing: tile j is key tile kt = j % tpb of ring step j / tpb, whose
+  // source rank is (rank - step) mod W; landing chunk c = kt / tpc holds it
+  // (tile kc = kt % tpc of the chunk)
+  const int tpc = p.chunk_keys / kAttnKT;
+  struct Pos {
+    int kt, c, kc;
+    int src;
   };
-  auto stage_k = [&](int j, int buf) {
-    const int kt = j % tpb;
-    const i32x4_t vk = make_vdesc(p.k_recv + block_of(j) * p.S_kv * kAttnD, (uint32_t)(p.S_kv * ldk));
+  auto pos_of = [&](int j) {
+    Pos q;
+    const int step = j / tpb;
+    q.kt = j - step * tpb;
+    q.c = q.kt / tpc;
+    q.kc = q.kt - q.c * tpc;
+    q.src = p.rank - step < 0 ? p.rank - step + p.world : p.rank - step;
+    return q;
+  };
+  auto advance = [&](Pos &q) {
+    ++q.kt;
+    if (++q.kc == tpc) {
+      q.kc = 0;
+      ++q.c;
+    }
+    if (q.kt == tpb) {  // next ring step: the previous rank's block
+      q.kt = q.c = q.kc = 0;
+      q.src = q.src == 0 ? p.world - 1 : q.src - 1;
+    }
+  };
+  const size_t blk_k = (size_t)p.S_kv * kAttnD;  // elements of one (rank, bh) block
+  auto stage_k = [&](const Pos &q, int buf) {
+    const i32x4_t vk = make_vdesc(p.k_recv + ((size_t)q.src * p.BH + bh) * blk_k, (uint32_t)(p.S_kv * ldk));
     const uint32_t st = base + buf * kAttnStage;
     const int half = wave >> 1;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int gl = 4 * (wave & 1) + d;  // row group within the tile
-      const uint32_t uni = (uint32_t)__builtin_amdgcn_readfirstlane((kt * kAttnKT + kperm(gl)) * ldk + half * 128);
+      const uint32_t uni = (uint32_t)__builtin_amdgcn_readfirstlane((q.kt * kAttnKT + kperm(gl)) * ldk + half * 128);
       dma16(vk, __builtin_amdgcn_readfirstlane(st + half * kAttnKHalf + gl * 1024), lane_off_k[gl & 1] + uni);
     }
   };
-  auto stage_v = [&](int j, int buf) {
-    const int kt = j % tpb;
-    const i32x4_t vv = make_vdesc(p.vt_recv + block_of(j) * kAttnD * p.S_kv, (uint32_t)(kAttnD * ldv));
+  auto stage_v = [&](const Pos &q, int buf) {
+    const i32x4_t vv = make_vdesc(p.vt_recv + ((size_t)q.src * p.BH + bh) * blk_k, (uint32_t)(kAttnD * ldv));
     const uint32_t st = base + buf * kAttnStage;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int gl = 4 * wave + d;
       dma_row_group(vv, st + kAttnVOff + gl * 1024, lane_off_v[gl & 1], lane_c8[gl & 1], ldv,
-                    kt * kAttnKT, p.S_kv, gl);
+                    q.kt * kAttnKT, p.S_kv, gl);
     }
   };
-  // wait for the chunk holding tile j (once per chunk)
+  // wait for the chunk holding a tile (once per chunk)
   int have = -1;
-  auto acquire = [&](int j) -> bool {
-    const int step = j / tpb, kt = j % tpb;
-    const int src = (p.rank - step + p.world) % p.world;
-    const int c = kt * kAttnKT / p.chunk_keys;
-    const int id = src * p.chunks + c;
+  auto acquire = [&](const Pos &q) -> bool {
+    const int id = q.src * p.chunks + q.c;
     if (id == have || p.prelanded) return true;
     have = id;
     bool ok0 = true;
-    const uint32_t f = attn_flag(p, src, bh, c);
+    const uint32_t f = attn_flag(p, q.src, bh, q.c);
     if (threadIdx.x == 0) ok0 = spin_until_eq(p.sync, flag_ptr(p.sync, f), p.sync.epoch, f);
     return wg_sync_ok(ok0, s_word, !p.light_acquire);
   };
@@ -265,11 +286,15 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
   // max of tile j + 1.  LDS holds K(j+1) and V(j) during iteration j, while
   // K(j+2) and V(j+1) land.  The acquires come before any DMA of the
   // iteration is issued, so a failed wait returns with nothing in flight.
-  if (!acquire(j0)) return false;
-  if (j0 + 1 < j1 && !acquire(j0 + 1)) return false;
-  stage_k(j0, j0 & 1);
-  stage_v(j0, j0 & 1);
-  if (j0 + 1 < j1) stage_k(j0 + 1, (j0 + 1) & 1);
+  Pos p1 = pos_of(j0), p2 = p1;
+  advance(p2);
+  if (!acquire(p1)) return false;
+  if (j0 + 1 < j1 && !acquire(p2)) return false;
+  stage_k(p1, j0 & 1);
+  stage_v(p1, j0 & 1);
+  if (j0 + 1 < j1) stage_k(p2, (j0 + 1) & 1);
+  advance(p1);  // from here on, in iteration j: p1 is tile j + 1, p2 tile j + 2
+  advance(p2);
   wait_vmcnt<0>();
   wg_barrier();
   f32x4_t sacc[2][4];
@@ -281,10 +306,12 @@ __device__ __forceinline__ bool attn_task(const AttnParams &p, int bh, int qt, i
     // DMAs of K(j+1) and V(j) have landed (waited for below, or in the prologue)
     wg_barrier();
     if (j + 2 < j1) {
-      if (!acquire(j + 2)) return false;
-      stage_k(j + 2, j & 1);
+      if (!acquire(p2)) return false;
+      stage_k(p2, j & 1);
     }
-    if (j + 1 < j1) stage_v(j + 1, (j + 1) & 1);
+    if (j + 1 < j1) stage_v(p1, (j + 1) & 1);
+    advance(p1);
+    advance(p2);
     // the running max; when no row's max grows, alpha is exactly 1 for every
     // row of the wave and the rescale of O is skipped (the same bits)
     float mnew[2];
