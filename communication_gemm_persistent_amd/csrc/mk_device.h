@@ -533,18 +533,20 @@ __device__ __attribute__((noinline)) void wg_copy2d_call(void *dst, const void *
 
 template <int BM, int BN>
 struct TileCfg {
-  // 256x256 tiles run 8 waves (2 per SIMD, a 2 x 4 grid of 128x64 blocks of
-  // 32x32x16 MFMAs); smaller tiles run 4 waves in a 2 x 2 grid.  256x224
-  // tiles (an N of 7 x 512 splits into 2^k x 224 columns) run 8 waves in a
-  // 4 x 2 grid of 64x112 blocks of 16x16x32 MFMAs; their B stage keeps 256
-  // rows of LDS, the last 32 filled with zeros.
+  // 256-row tiles run 8 waves (2 per SIMD) in a 4 x 2 grid of 16x16x32
+  // MFMA blocks: 64x64 per wave for 256x256 tiles, 64x112 for 256x224 (an N
+  // of 7 x 512 splits into 2^k x 224 columns), whose B stage keeps 256 rows
+  // of LDS, the last 32 filled with zeros.  (32x32x16 MFMAs in a 2 x 4 grid
+  // of 128x64 blocks measured 5-8% slower for the 256x256 tiles.)  Smaller
+  // tiles run 4 waves in a 2 x 2 grid of 32x32x16 MFMA blocks.
   static constexpr bool N224 = (BM == 256 && BN == 224);
-  static constexpr int MFMA = N224 ? 16 : 32;                 // MFMA output edge
-  static constexpr int SUBSTEPS = N224 ? 2 : 4;               // MFMA K steps per 64-wide stage
-  static constexpr int GROUPS = N224 ? 1 : 4;                 // 4-column groups per accumulator
-  using Acc = std::conditional_t<N224, f32x4_t, f32x16_t>;
-  static constexpr int WAVES_M = N224 ? 4 : 2;
-  static constexpr int WAVES_N = N224 ? 2 : ((BM >= 256 && BN >= 256) ? 4 : 2);
+  static constexpr bool M16 = (BM == 256);  // 16x16x32 MFMAs
+  static constexpr int MFMA = M16 ? 16 : 32;                 // MFMA output edge
+  static constexpr int SUBSTEPS = M16 ? 2 : 4;               // MFMA K steps per 64-wide stage
+  static constexpr int GROUPS = M16 ? 1 : 4;                 // 4-column groups per accumulator
+  using Acc = std::conditional_t<M16, f32x4_t, f32x16_t>;
+  static constexpr int WAVES_M = M16 ? 4 : 2;
+  static constexpr int WAVES_N = 2;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
