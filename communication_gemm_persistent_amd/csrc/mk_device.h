@@ -512,12 +512,13 @@ __device__ __attribute__((noinline)) void wg_copy2d_call(void *dst, const void *
 // ---------------------------------------------------------------- GEMM tile engine
 //
 // C_tile[BM x BN] = A[m0:m0+BM, :] @ Bt[n0:n0+BN, :]^T with fp32 accumulation.
-// 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BN/2) block built from
-// 32x32x16 bf16 MFMAs.  The MFMA is issued with the B^T fragment as its first
-// operand and the A fragment as its second, so the accumulator holds C^T
-// blocks: lane l holds row (l % 32) of its 32x32 block and, for v = 0..15,
-// column 8*(v/4) + 4*(l/32) + v%4 -- four consecutive columns per group,
-// which the epilogues store as 8-byte bf16 / 16-byte fp32 vectors.
+// Each wave owns a block of the tile built from E x E bf16 MFMA blocks
+// (TileCfg: E = 16, 16x16x32 MFMAs, for the 8-wave 256-row tiles; E = 32,
+// 32x32x16 MFMAs, for the 4-wave 128-row tiles).  The MFMA is issued with
+// the B^T fragment as its first operand and the A fragment as its second, so
+// the accumulator holds C^T blocks: lane l holds row (l % E) of its block and
+// groups of four consecutive columns (acc_pos), which the epilogues store as
+// 8-byte bf16 / 16-byte fp32 vectors.
 //
 // LDS layout of one operand stage: row r occupies 128 bytes (64 bf16 of K);
 // its eight 16-byte chunks are stored at position p = c ^ ((r >> 1) & 7) for
